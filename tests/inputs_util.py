@@ -1,0 +1,52 @@
+"""Test-side input conditioning: the routing predicates use the fp64 oracle.
+
+Argmax and the gate-descending order are integer decisions taken from
+floating-point values.  The HIP router evaluates them in fp32, the oracle in
+fp64.  The inputs are conditioned so that the decision is the same in either
+precision:
+
+* top-2 logit margin >= 1e-3 on every row (the fp32 accumulation error of a
+  logit is ~1e-5 at d = 768 and ~1e-4 at d = 5120);
+* for gate-descending runs: among each expert's C_max + 1 highest-gate tokens,
+  adjacent gates differ by a relative 1e-4 (the fp32 gate error is ~1e-5).
+
+Rows that fail are redrawn by the input generator.
+"""
+import numpy as np
+
+import oracle
+import workloads
+
+MARGIN = 1e-3
+GATE_GAP = 1e-4
+
+
+def stored_router(inp):
+    dt = inp.wl.dtype
+    return oracle.route(oracle.widen(inp.x, dt), oracle.widen(inp.w_gate, dt), inp.bias)
+
+
+def margin_bad_rows(inp):
+    l, _, _, _ = stored_router(inp)
+    top2 = np.partition(l, -2, axis=1)[:, -2:]
+    return np.nonzero(top2[:, 1] - top2[:, 0] < MARGIN)[0]
+
+
+def gate_gap_bad_rows(c_max):
+    def bad(inp):
+        rows = list(margin_bad_rows(inp))
+        l, p, e, g = stored_router(inp)
+        for i in np.unique(e):
+            toks = np.nonzero(e == i)[0]
+            order = toks[np.lexsort((toks, -g[toks]))][: c_max + 1]
+            gg = g[order]
+            close = (gg[:-1] - gg[1:]) < GATE_GAP * gg[:-1]
+            rows.extend(order[1:][close].tolist())
+        return np.array(sorted(set(rows)), dtype=np.int64)
+    return bad
+
+
+def conditioned_inputs(wl, *, weights=True, gate_order_cmax=None, threads=8):
+    """Inputs with the margin rule (and the gate-gap rule if gate_order_cmax is set)."""
+    pred = margin_bad_rows if gate_order_cmax is None else gate_gap_bad_rows(gate_order_cmax)
+    return workloads.make_inputs(wl, weights=weights, bad_rows=pred, threads=threads)
