@@ -1,0 +1,223 @@
+/*
+ * switch_moe.h -- C ABI of a Switch top-1 mixture-of-experts layer forward
+ * for AMD Instinct MI355X (gfx950), one GPU, every expert resident.
+ *
+ * Sources for the operations (page title, then section):
+ *   [TOP1] "Top-1 Routing" concept page (compassingai.com): Core mechanism,
+ *          Load balancing, Token Dropping, Key parameters and compute.
+ *   [SWT]  Switch Transformers summary page (personwebsite.pages.dev,
+ *          moe-switch): Switch-layer passage (k = 1, gate value as the
+ *          multiplier), expert-capacity passage, Eq. 4 auxiliary loss
+ *          passage, selective-precision passage.
+ *   [CAP]  "MoE expert capacity factor and token dropping" (wiblog.cn):
+ *          Where capacity comes from, After overflow, training-step
+ *          flowchart.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor pointers are DEVICE pointers; the descriptor structs and scalar
+ *     arguments live on the host.  `stream` is a hipStream_t passed as void*
+ *     (NULL = the default stream).  Every call only enqueues work on
+ *     `stream` and returns; nothing is synchronised and nothing is copied to
+ *     the host.
+ *   - The caller owns every buffer (inputs, outputs and workspace).  The
+ *     library never allocates or frees memory and keeps no state between
+ *     calls.  Inputs are read only.  Workspace contents are undefined on
+ *     entry and on return.
+ *   - Layouts are row-major: x [T, d_model]; w_gate [N, d_model];
+ *     w1 [N, d_model, d_ff]; w2 [N, d_ff, d_model]; expert buffers
+ *     [N, C, d_model]; y [T, d_model]; shared ws1 [d_model, d_ff_s],
+ *     ws2 [d_ff_s, d_model].
+ *   - dtype: SWITCH_F32 (float) or SWITCH_BF16 (bfloat16 storage with fp32
+ *     arithmetic inside every kernel).  The router always computes in fp32
+ *     and returns fp32 gates ([SWT] selective precision).
+ *   - Errors: validation runs before any launch, so an error return other
+ *     than SWITCH_E_HIP enqueues no work.  SWITCH_E_HIP means a launch
+ *     failed; outputs are then undefined.  switch_last_error() returns a
+ *     thread-local message describing the last failure.  No C++ exception
+ *     crosses the ABI.
+ *   - Shape rules: T >= 1; 1 <= N <= 1024; 1 <= C <= T; pointers 16-byte
+ *     aligned.  bf16: d_model and d_ff multiples of 128.  f32: d_model a
+ *     multiple of 4.
+ *   - Determinism: identical inputs give bitwise identical outputs (no
+ *     floating-point atomics; every reduction has a fixed order).
+ */
+#ifndef SWITCH_MOE_H
+#define SWITCH_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum switch_status {
+  SWITCH_OK = 0,
+  SWITCH_E_NULL = 1,        /* a required pointer is NULL */
+  SWITCH_E_SHAPE = 2,       /* a size violates the shape rules */
+  SWITCH_E_UNSUPPORTED = 3, /* dtype / priority / flag value not supported */
+  SWITCH_E_WORKSPACE = 4,   /* workspace smaller than the *_workspace_bytes figure */
+  SWITCH_E_HIP = 5,         /* a HIP launch failed */
+  SWITCH_E_ALIGN = 6        /* a pointer is not 16-byte aligned */
+} switch_status;
+
+typedef enum switch_dtype { SWITCH_F32 = 0, SWITCH_BF16 = 1 } switch_dtype;
+
+/* Overflow priority inside one expert ([CAP] After overflow and flowchart;
+ * token order is the plain reading of "the excess tokens" in [TOP1]
+ * Token Dropping). */
+typedef enum switch_priority {
+  SWITCH_TOKEN_ORDER = 0, /* earlier tokens first */
+  SWITCH_GATE_DESC = 1    /* higher gate first; equal gates: earlier token first */
+} switch_priority;
+
+/* Combine flags.  SWITCH_GATE_SCALE: y = gate * E(x) ([SWT] Switch-layer
+ * passage); without it y = E(x) ([TOP1] Core mechanism).  The pages
+ * disagree, so this is a flag.  SWITCH_RESIDUAL_ALL: kept tokens also get
+ * + x (the Transformer residual around the layer, [TOP1] MoE layer figure).
+ * Dropped tokens always get y = x. */
+#define SWITCH_GATE_SCALE 1u
+#define SWITCH_RESIDUAL_ALL 2u
+
+/* ------------------------------------------------------------------------
+ * Capacity ([TOP1] Token Dropping; [SWT] expert capacity; [CAP] Where
+ * capacity comes from): C = max(1, ceil(capacity_factor * T / N)).
+ * Host-only.  Returns -1 if T < 1, N < 1 or capacity_factor <= 0.
+ * ---------------------------------------------------------------------- */
+int32_t switch_capacity(int64_t T, int32_t N, double capacity_factor);
+
+/* ------------------------------------------------------------------------
+ * Router ([TOP1] Core mechanism and Load balancing; [SWT] Switch layer,
+ * Eq. 4 passage, selective precision).
+ *   logits l[t,i] = sum_k w_gate[i,k] x[t,k] + bias[i]   (fp32)
+ *   p = softmax_i(l);  expert_id[t] = argmax_i l[t,i] (lowest index on ties);
+ *   gate[t] = p[t, expert_id[t]]
+ *   routed_count[i] = #{t : expert_id[t] = i};  f[i] = routed_count[i] / T
+ *   P[i] = (1/T) sum_t p[t,i];  l_aux[0] = N * sum_i f[i] P[i]
+ * x, w_gate: dtype; bias: fp32 [N] or NULL; outputs: expert_id int32 [T],
+ * gate fp32 [T], routed_count int32 [N], f fp32 [N], P fp32 [N], l_aux fp32
+ * [1].  f counts argmax decisions before any capacity cut; l_aux excludes
+ * the training coefficient alpha.
+ * ---------------------------------------------------------------------- */
+size_t switch_route_workspace_bytes(int64_t T, int32_t d_model, int32_t N, int32_t dtype);
+switch_status switch_route(const void* x, const void* w_gate, const float* bias, int64_t T, int32_t d_model,
+                           int32_t N, int32_t dtype, int32_t* expert_id, float* gate, int32_t* routed_count,
+                           float* f, float* P, float* l_aux, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Capacity / slot assignment ([CAP] After overflow and flowchart steps
+ * C-F; [TOP1] Token Dropping).  Each token's rank among the tokens routed
+ * to its expert under `priority`; kept iff rank < C.
+ *   slot[t] = rank if kept else -1                       int32 [T]
+ *   token_of_slot[e*C + s] = token in slot s, -1 if empty int32 [N*C]
+ *   kept_count[e] = min(routed_count[e], C)              int32 [N]
+ *   n_dropped[0] = T - sum_e kept_count[e]               int32 [1]
+ *   active[0..n_active) = experts with kept_count > 0, ascending; rest
+ *   undefined                                            int32 [N]
+ *   n_active[0]                                          int32 [1]
+ * gate (fp32 [T]) is read only for SWITCH_GATE_DESC (may be NULL for
+ * token order).  Integer results are exact.
+ * ---------------------------------------------------------------------- */
+size_t switch_assign_workspace_bytes(int64_t T, int32_t N, int32_t C, int32_t priority);
+switch_status switch_assign_capacity(const int32_t* expert_id, const float* gate, int64_t T, int32_t N, int32_t C,
+                                     int32_t priority, int32_t* slot, int32_t* token_of_slot, int32_t* kept_count,
+                                     int32_t* n_dropped, int32_t* active, int32_t* n_active, void* ws,
+                                     size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Dispatch into fixed per-expert buffers ([CAP] Where capacity comes from:
+ * fixed slots turn dynamic routing into static shapes).
+ *   expert_in[e, s, :] = x[token_of_slot[e*C+s], :]  for s < kept_count[e]
+ * Rows s >= kept_count[e] are not written.  Bit copy.
+ * ---------------------------------------------------------------------- */
+switch_status switch_dispatch(const void* x, int32_t dtype, int64_t T, int32_t d_model, const int32_t* token_of_slot,
+                              const int32_t* kept_count, int32_t N, int32_t C, void* expert_in, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Expert FFN ([TOP1] Key parameters and compute: two-layer FFN, biases
+ * ignored; ReLU activation).
+ *   expert_out[e, s, :] = ReLU(expert_in[e, s, :] . w1[e]) . w2[e]
+ * for e in active[0..n_active) and s < kept_count[e].  Empty slots and
+ * inactive experts are never read (their weights are not touched); rows
+ * s >= kept_count[e] of expert_out are not written.  bf16: the hidden
+ * activation is rounded to bf16 between the two GEMMs, both accumulate in
+ * fp32, the output is rounded once to bf16.
+ * A dense FFN over M rows is the case N = 1, C = M, kept_count = {M},
+ * active = {0}, n_active = {1}.
+ * ---------------------------------------------------------------------- */
+size_t switch_expert_ffn_workspace_bytes(int32_t N, int32_t C, int32_t d_model, int32_t d_ff, int32_t dtype);
+switch_status switch_expert_ffn(const void* expert_in, const void* w1, const void* w2, int32_t dtype, int32_t N,
+                                int32_t C, int32_t d_model, int32_t d_ff, const int32_t* kept_count,
+                                const int32_t* active, const int32_t* n_active, void* expert_out, void* ws,
+                                size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Combine ([TOP1] Core mechanism; [SWT] Switch-layer passage; dropped
+ * tokens: [TOP1] Token Dropping, [SWT] expert capacity, [CAP] After
+ * overflow, residual bypass).
+ *   kept t (slot[t] >= 0): y[t] = (flags & GATE_SCALE ? gate[t] : 1) *
+ *        expert_out[expert_id[t], slot[t]] (+ x[t] if RESIDUAL_ALL)
+ *   dropped t:             y[t] = x[t]
+ *   and + shared_out[t] for every t when shared_out != NULL.
+ * Arithmetic in fp32, rounded once to dtype; a dropped row without a
+ * shared term is a bit copy.
+ * ---------------------------------------------------------------------- */
+switch_status switch_combine(const void* expert_out, const void* x, const void* shared_out, int32_t dtype, int64_t T,
+                             int32_t d_model, const int32_t* expert_id, const int32_t* slot, const float* gate,
+                             int32_t N, int32_t C, uint32_t flags, void* y, void* stream);
+
+/* ------------------------------------------------------------------------
+ * The whole layer: route -> capacity/slots -> dispatch -> expert FFN ->
+ * (shared FFN) -> combine, enqueued on one stream.
+ * ---------------------------------------------------------------------- */
+typedef struct switch_moe_desc {
+  int64_t T;
+  int32_t d_model;
+  int32_t d_ff;
+  int32_t N;
+  int32_t C;                /* 0: derive from capacity_factor */
+  double capacity_factor;
+  int32_t dtype;            /* switch_dtype */
+  int32_t priority;         /* switch_priority */
+  uint32_t flags;           /* SWITCH_GATE_SCALE | SWITCH_RESIDUAL_ALL */
+  int32_t d_ff_shared;      /* 0: no shared expert; else one always-on dense
+                               FFN added to every token ([TOP1] History,
+                               shared experts) */
+} switch_moe_desc;
+
+typedef struct switch_moe_inputs {
+  const void* x;
+  const void* w_gate;
+  const float* bias; /* NULL: no router bias */
+  const void* w1;
+  const void* w2;
+  const void* ws1;   /* shared expert, only if d_ff_shared > 0 */
+  const void* ws2;
+} switch_moe_inputs;
+
+typedef struct switch_moe_outputs {
+  void* y;               /* [T, d_model] dtype (required) */
+  int32_t* expert_id;    /* [T] (required) */
+  float* gate;           /* [T] (required) */
+  int32_t* slot;         /* [T] (required) */
+  int32_t* routed_count; /* [N] (required) */
+  int32_t* kept_count;   /* [N] (required) */
+  int32_t* n_dropped;    /* [1] (required) */
+  float* f;              /* [N] (required) */
+  float* P;              /* [N] (required) */
+  float* l_aux;          /* [1] (required) */
+} switch_moe_outputs;
+
+size_t switch_moe_workspace_bytes(const switch_moe_desc* desc);
+switch_status switch_moe_forward(const switch_moe_desc* desc, const switch_moe_inputs* in,
+                                 const switch_moe_outputs* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* switch_status_str(switch_status s);
+/* Thread-local message of the last error on this thread ("" if none). */
+const char* switch_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SWITCH_MOE_H */

@@ -1,0 +1,430 @@
+// C ABI of the Switch top-1 MoE layer: argument validation, workspace layout
+// and the launch sequence.  Validation happens before any launch, so an error
+// return (other than SWITCH_E_HIP) enqueues nothing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "kernels.hpp"
+#include "switch_moe.h"
+
+using namespace swm;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+switch_status fail(switch_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+switch_status ok() {
+  g_err[0] = '\0';
+  return SWITCH_OK;
+}
+
+switch_status hip_fail(hipError_t e, const char* where) {
+  return fail(SWITCH_E_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr int kMaxExperts = 1024;
+constexpr int64_t kMaxTokens = (int64_t)1 << 30;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+#define REQUIRE_PTR(p)                                               \
+  do {                                                               \
+    if ((p) == nullptr) return fail(SWITCH_E_NULL, "%s is NULL", #p); \
+  } while (0)
+
+#define REQUIRE_ALIGN(p, a)                                                                       \
+  do {                                                                                            \
+    if (!aligned((p), (a))) return fail(SWITCH_E_ALIGN, "%s is not %d-byte aligned", #p, (int)(a)); \
+  } while (0)
+
+switch_status check_dtype(int32_t dtype) {
+  if (dtype != SWITCH_F32 && dtype != SWITCH_BF16) return fail(SWITCH_E_UNSUPPORTED, "dtype %d is not supported", dtype);
+  return SWITCH_OK;
+}
+
+switch_status check_tn(int64_t T, int32_t N) {
+  if (T < 1 || T > kMaxTokens) return fail(SWITCH_E_SHAPE, "T=%lld outside [1, 2^30]", (long long)T);
+  if (N < 1 || N > kMaxExperts) return fail(SWITCH_E_SHAPE, "N=%d outside [1, %d]", N, kMaxExperts);
+  return SWITCH_OK;
+}
+
+switch_status check_rows(int32_t d, int32_t dtype, const char* name) {
+  if (d < 1) return fail(SWITCH_E_SHAPE, "%s=%d must be >= 1", name, d);
+  if (dtype == SWITCH_BF16 && d % 128 != 0) return fail(SWITCH_E_SHAPE, "%s=%d must be a multiple of 128 for bf16", name, d);
+  if (dtype == SWITCH_F32 && d % 4 != 0) return fail(SWITCH_E_SHAPE, "%s=%d must be a multiple of 4 for f32", name, d);
+  return SWITCH_OK;
+}
+
+switch_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
+  if (need > 0 && ws == nullptr) return fail(SWITCH_E_NULL, "workspace is NULL (%zu bytes needed)", need);
+  if (ws_bytes < need) return fail(SWITCH_E_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+  if (need > 0 && !aligned(ws, 256)) return fail(SWITCH_E_ALIGN, "workspace is not 256-byte aligned");
+  return SWITCH_OK;
+}
+
+#define TRY(expr)                        \
+  do {                                   \
+    switch_status _s = (expr);           \
+    if (_s != SWITCH_OK) return _s;      \
+  } while (0)
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+switch_status validate_route(const void* x, const void* w_gate, const float* bias, int64_t T, int32_t d, int32_t N,
+                             int32_t dtype, const void* expert_id, const void* gate, const void* routed_count,
+                             const void* f, const void* P, const void* l_aux) {
+  TRY(check_dtype(dtype));
+  TRY(check_tn(T, N));
+  if (d < 1) return fail(SWITCH_E_SHAPE, "d_model=%d must be >= 1", d);
+  if (dtype == SWITCH_BF16 && d % 32 != 0) return fail(SWITCH_E_SHAPE, "d_model=%d must be a multiple of 32 for bf16 routing", d);
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(w_gate);
+  REQUIRE_PTR(expert_id);
+  REQUIRE_PTR(gate);
+  REQUIRE_PTR(routed_count);
+  REQUIRE_PTR(f);
+  REQUIRE_PTR(P);
+  REQUIRE_PTR(l_aux);
+  REQUIRE_ALIGN(x, 16);
+  REQUIRE_ALIGN(w_gate, 16);
+  if (bias) REQUIRE_ALIGN(bias, 4);
+  REQUIRE_ALIGN(expert_id, 4);
+  REQUIRE_ALIGN(gate, 4);
+  REQUIRE_ALIGN(routed_count, 4);
+  REQUIRE_ALIGN(f, 4);
+  REQUIRE_ALIGN(P, 4);
+  REQUIRE_ALIGN(l_aux, 4);
+  return SWITCH_OK;
+}
+
+switch_status validate_assign(const void* expert_id, const void* gate, int64_t T, int32_t N, int32_t C,
+                              int32_t priority, const void* slot, const void* token_of_slot, const void* kept_count,
+                              const void* n_dropped, const void* active, const void* n_active) {
+  TRY(check_tn(T, N));
+  if (C < 1 || C > T) return fail(SWITCH_E_SHAPE, "C=%d outside [1, T=%lld]", C, (long long)T);
+  if ((int64_t)N * C > ((int64_t)1 << 31) - 1) return fail(SWITCH_E_SHAPE, "N*C exceeds 2^31-1");
+  if (priority != SWITCH_TOKEN_ORDER && priority != SWITCH_GATE_DESC)
+    return fail(SWITCH_E_UNSUPPORTED, "priority %d is not supported", priority);
+  REQUIRE_PTR(expert_id);
+  if (priority == SWITCH_GATE_DESC) REQUIRE_PTR(gate);
+  REQUIRE_PTR(slot);
+  REQUIRE_PTR(token_of_slot);
+  REQUIRE_PTR(kept_count);
+  REQUIRE_PTR(n_dropped);
+  REQUIRE_PTR(active);
+  REQUIRE_PTR(n_active);
+  return SWITCH_OK;
+}
+
+switch_status validate_dispatch(const void* x, int32_t dtype, int64_t T, int32_t d, const void* token_of_slot,
+                                const void* kept_count, int32_t N, int32_t C, const void* expert_in) {
+  TRY(check_dtype(dtype));
+  TRY(check_tn(T, N));
+  if (C < 1 || C > T) return fail(SWITCH_E_SHAPE, "C=%d outside [1, T=%lld]", C, (long long)T);
+  if (d < 1 || (d * (dtype == SWITCH_BF16 ? 2 : 4)) % 16 != 0)
+    return fail(SWITCH_E_SHAPE, "d_model=%d: rows must be a multiple of 16 bytes", d);
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(token_of_slot);
+  REQUIRE_PTR(kept_count);
+  REQUIRE_PTR(expert_in);
+  REQUIRE_ALIGN(x, 16);
+  REQUIRE_ALIGN(expert_in, 16);
+  return SWITCH_OK;
+}
+
+switch_status validate_ffn(const void* expert_in, const void* w1, const void* w2, int32_t dtype, int32_t N, int32_t C,
+                           int32_t d, int32_t dff, const void* kept_count, const void* active, const void* n_active,
+                           const void* expert_out) {
+  TRY(check_dtype(dtype));
+  if (N < 1 || N > kMaxExperts) return fail(SWITCH_E_SHAPE, "N=%d outside [1, %d]", N, kMaxExperts);
+  if (C < 1 || C > kMaxTokens) return fail(SWITCH_E_SHAPE, "C=%d must be >= 1", C);
+  TRY(check_rows(d, dtype, "d_model"));
+  TRY(check_rows(dff, dtype, "d_ff"));
+  REQUIRE_PTR(expert_in);
+  REQUIRE_PTR(w1);
+  REQUIRE_PTR(w2);
+  REQUIRE_PTR(kept_count);
+  REQUIRE_PTR(active);
+  REQUIRE_PTR(n_active);
+  REQUIRE_PTR(expert_out);
+  REQUIRE_ALIGN(expert_in, 16);
+  REQUIRE_ALIGN(w1, 16);
+  REQUIRE_ALIGN(w2, 16);
+  REQUIRE_ALIGN(expert_out, 16);
+  return SWITCH_OK;
+}
+
+switch_status validate_combine(const void* expert_out, const void* x, const void* shared_out, int32_t dtype, int64_t T,
+                               int32_t d, const void* expert_id, const void* slot, const void* gate, int32_t N,
+                               int32_t C, uint32_t flags, const void* y) {
+  TRY(check_dtype(dtype));
+  TRY(check_tn(T, N));
+  if (C < 1) return fail(SWITCH_E_SHAPE, "C=%d must be >= 1", C);
+  if (d < 1 || (d * (dtype == SWITCH_BF16 ? 2 : 4)) % 16 != 0)
+    return fail(SWITCH_E_SHAPE, "d_model=%d: rows must be a multiple of 16 bytes", d);
+  if (flags & ~(SWITCH_GATE_SCALE | SWITCH_RESIDUAL_ALL)) return fail(SWITCH_E_UNSUPPORTED, "unknown flag bits 0x%x", flags);
+  REQUIRE_PTR(expert_out);
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(expert_id);
+  REQUIRE_PTR(slot);
+  if (flags & SWITCH_GATE_SCALE) REQUIRE_PTR(gate);
+  REQUIRE_PTR(y);
+  REQUIRE_ALIGN(expert_out, 16);
+  REQUIRE_ALIGN(x, 16);
+  if (shared_out) REQUIRE_ALIGN(shared_out, 16);
+  REQUIRE_ALIGN(y, 16);
+  return SWITCH_OK;
+}
+
+// ---------------------------------------------------------------------------
+// whole-layer workspace layout
+// ---------------------------------------------------------------------------
+struct FwdLayout {
+  int32_t C;
+  RoutePlan route;
+  AssignPlan assign;
+  FfnPlan ffn, sffn;
+  size_t off_route, off_assign, off_tos, off_active, off_nact, off_xin, off_xout, off_ffn;
+  size_t off_dense, off_sffn, off_sout, bytes;
+};
+
+FwdLayout fwd_layout(const switch_moe_desc& d, int32_t C) {
+  FwdLayout L{};
+  L.C = C;
+  const size_t esz = d.dtype == SWITCH_BF16 ? 2 : 4;
+  L.route = route_plan(d.T, d.d_model, d.N, d.dtype);
+  L.assign = assign_plan(d.T, d.N, C, d.priority);
+  L.ffn = ffn_plan(d.N, C, d.d_model, d.d_ff, d.dtype);
+  size_t off = 0;
+  L.off_route = off;
+  off = align_up(off + L.route.bytes);
+  L.off_assign = off;
+  off = align_up(off + L.assign.bytes);
+  L.off_tos = off;
+  off = align_up(off + (size_t)d.N * C * 4);
+  L.off_active = off;
+  off = align_up(off + (size_t)d.N * 4);
+  L.off_nact = off;
+  off = align_up(off + 4);
+  L.off_xin = off;
+  off = align_up(off + (size_t)d.N * C * d.d_model * esz);
+  L.off_xout = off;
+  off = align_up(off + (size_t)d.N * C * d.d_model * esz);
+  L.off_ffn = off;
+  off = align_up(off + L.ffn.bytes);
+  if (d.d_ff_shared > 0) {
+    L.sffn = ffn_plan(1, (int)d.T, d.d_model, d.d_ff_shared, d.dtype);
+    L.off_dense = off;
+    off = align_up(off + 3 * 4);
+    L.off_sffn = off;
+    off = align_up(off + L.sffn.bytes);
+    L.off_sout = off;
+    off = align_up(off + (size_t)d.T * d.d_model * esz);
+  }
+  L.bytes = off;
+  return L;
+}
+
+switch_status validate_desc(const switch_moe_desc* d, int32_t* C) {
+  if (d == nullptr) return fail(SWITCH_E_NULL, "desc is NULL");
+  TRY(check_dtype(d->dtype));
+  TRY(check_tn(d->T, d->N));
+  TRY(check_rows(d->d_model, d->dtype, "d_model"));
+  TRY(check_rows(d->d_ff, d->dtype, "d_ff"));
+  if (d->d_ff_shared < 0) return fail(SWITCH_E_SHAPE, "d_ff_shared=%d must be >= 0", d->d_ff_shared);
+  if (d->d_ff_shared > 0) TRY(check_rows(d->d_ff_shared, d->dtype, "d_ff_shared"));
+  if (d->priority != SWITCH_TOKEN_ORDER && d->priority != SWITCH_GATE_DESC)
+    return fail(SWITCH_E_UNSUPPORTED, "priority %d is not supported", d->priority);
+  if (d->flags & ~(SWITCH_GATE_SCALE | SWITCH_RESIDUAL_ALL))
+    return fail(SWITCH_E_UNSUPPORTED, "unknown flag bits 0x%x", d->flags);
+  int32_t c = d->C;
+  if (c == 0) {
+    c = switch_capacity(d->T, d->N, d->capacity_factor);
+    if (c < 1) return fail(SWITCH_E_SHAPE, "capacity_factor=%g gives no capacity", d->capacity_factor);
+  }
+  if (c < 1 || c > d->T) return fail(SWITCH_E_SHAPE, "C=%d outside [1, T=%lld]", c, (long long)d->T);
+  if ((int64_t)d->N * c > ((int64_t)1 << 31) - 1) return fail(SWITCH_E_SHAPE, "N*C exceeds 2^31-1");
+  *C = c;
+  return SWITCH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t switch_capacity(int64_t T, int32_t N, double capacity_factor) {
+  if (T < 1 || N < 1 || !(capacity_factor > 0.0)) return -1;
+  const double v = std::ceil(capacity_factor * (double)T / (double)N);
+  if (v > (double)T) return (int32_t)(T < INT32_MAX ? T : INT32_MAX);
+  const int32_t c = (int32_t)v;
+  return c < 1 ? 1 : c;
+}
+
+size_t switch_route_workspace_bytes(int64_t T, int32_t d_model, int32_t N, int32_t dtype) {
+  if (T < 1 || N < 1 || d_model < 1) return 0;
+  return route_plan(T, d_model, N, dtype).bytes;
+}
+
+switch_status switch_route(const void* x, const void* w_gate, const float* bias, int64_t T, int32_t d_model,
+                           int32_t N, int32_t dtype, int32_t* expert_id, float* gate, int32_t* routed_count,
+                           float* f, float* P, float* l_aux, void* ws, size_t ws_bytes, void* stream) {
+  TRY(validate_route(x, w_gate, bias, T, d_model, N, dtype, expert_id, gate, routed_count, f, P, l_aux));
+  const RoutePlan pl = route_plan(T, d_model, N, dtype);
+  TRY(check_ws(ws, ws_bytes, pl.bytes));
+  hipError_t e = launch_route(pl, x, w_gate, bias, T, d_model, N, dtype, expert_id, gate, routed_count, f, P, l_aux,
+                              static_cast<char*>(ws), as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "switch_route");
+  return ok();
+}
+
+size_t switch_assign_workspace_bytes(int64_t T, int32_t N, int32_t C, int32_t priority) {
+  if (T < 1 || N < 1) return 0;
+  return assign_plan(T, N, C, priority).bytes;
+}
+
+switch_status switch_assign_capacity(const int32_t* expert_id, const float* gate, int64_t T, int32_t N, int32_t C,
+                                     int32_t priority, int32_t* slot, int32_t* token_of_slot, int32_t* kept_count,
+                                     int32_t* n_dropped, int32_t* active, int32_t* n_active, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  TRY(validate_assign(expert_id, gate, T, N, C, priority, slot, token_of_slot, kept_count, n_dropped, active,
+                      n_active));
+  const AssignPlan pl = assign_plan(T, N, C, priority);
+  TRY(check_ws(ws, ws_bytes, pl.bytes));
+  hipError_t e = launch_assign(pl, expert_id, gate, T, N, C, priority, slot, token_of_slot, kept_count, n_dropped,
+                               active, n_active, static_cast<char*>(ws), as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "switch_assign_capacity");
+  return ok();
+}
+
+switch_status switch_dispatch(const void* x, int32_t dtype, int64_t T, int32_t d_model, const int32_t* token_of_slot,
+                              const int32_t* kept_count, int32_t N, int32_t C, void* expert_in, void* stream) {
+  TRY(validate_dispatch(x, dtype, T, d_model, token_of_slot, kept_count, N, C, expert_in));
+  hipError_t e = launch_dispatch(x, dtype, T, d_model, token_of_slot, kept_count, N, C, expert_in,
+                                 as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "switch_dispatch");
+  return ok();
+}
+
+size_t switch_expert_ffn_workspace_bytes(int32_t N, int32_t C, int32_t d_model, int32_t d_ff, int32_t dtype) {
+  if (N < 1 || C < 1 || d_model < 1 || d_ff < 1) return 0;
+  return ffn_plan(N, C, d_model, d_ff, dtype).bytes;
+}
+
+switch_status switch_expert_ffn(const void* expert_in, const void* w1, const void* w2, int32_t dtype, int32_t N,
+                                int32_t C, int32_t d_model, int32_t d_ff, const int32_t* kept_count,
+                                const int32_t* active, const int32_t* n_active, void* expert_out, void* ws,
+                                size_t ws_bytes, void* stream) {
+  TRY(validate_ffn(expert_in, w1, w2, dtype, N, C, d_model, d_ff, kept_count, active, n_active, expert_out));
+  const FfnPlan pl = ffn_plan(N, C, d_model, d_ff, dtype);
+  TRY(check_ws(ws, ws_bytes, pl.bytes));
+  hipError_t e = launch_ffn(pl, expert_in, w1, w2, dtype, N, C, d_model, d_ff, kept_count, active, n_active,
+                            expert_out, static_cast<char*>(ws), as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "switch_expert_ffn");
+  return ok();
+}
+
+switch_status switch_combine(const void* expert_out, const void* x, const void* shared_out, int32_t dtype, int64_t T,
+                             int32_t d_model, const int32_t* expert_id, const int32_t* slot, const float* gate,
+                             int32_t N, int32_t C, uint32_t flags, void* y, void* stream) {
+  TRY(validate_combine(expert_out, x, shared_out, dtype, T, d_model, expert_id, slot, gate, N, C, flags, y));
+  hipError_t e = launch_combine(expert_out, x, shared_out, dtype, T, d_model, expert_id, slot, gate, N, C, flags, y,
+                                as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "switch_combine");
+  return ok();
+}
+
+size_t switch_moe_workspace_bytes(const switch_moe_desc* desc) {
+  int32_t C = 0;
+  if (validate_desc(desc, &C) != SWITCH_OK) return 0;
+  return fwd_layout(*desc, C).bytes;
+}
+
+switch_status switch_moe_forward(const switch_moe_desc* desc, const switch_moe_inputs* in,
+                                 const switch_moe_outputs* out, void* ws, size_t ws_bytes, void* stream) {
+  int32_t C = 0;
+  TRY(validate_desc(desc, &C));
+  if (in == nullptr) return fail(SWITCH_E_NULL, "inputs is NULL");
+  if (out == nullptr) return fail(SWITCH_E_NULL, "outputs is NULL");
+  const switch_moe_desc& d = *desc;
+  TRY(validate_route(in->x, in->w_gate, in->bias, d.T, d.d_model, d.N, d.dtype, out->expert_id, out->gate,
+                     out->routed_count, out->f, out->P, out->l_aux));
+  REQUIRE_PTR(in->w1);
+  REQUIRE_PTR(in->w2);
+  REQUIRE_ALIGN(in->w1, 16);
+  REQUIRE_ALIGN(in->w2, 16);
+  REQUIRE_PTR(out->y);
+  REQUIRE_ALIGN(out->y, 16);
+  REQUIRE_PTR(out->slot);
+  REQUIRE_PTR(out->kept_count);
+  REQUIRE_PTR(out->n_dropped);
+  if (d.d_ff_shared > 0) {
+    REQUIRE_PTR(in->ws1);
+    REQUIRE_PTR(in->ws2);
+    REQUIRE_ALIGN(in->ws1, 16);
+    REQUIRE_ALIGN(in->ws2, 16);
+  }
+  const FwdLayout L = fwd_layout(d, C);
+  TRY(check_ws(ws, ws_bytes, L.bytes));
+  char* w = static_cast<char*>(ws);
+  hipStream_t st = as_stream(stream);
+  int32_t* tos = reinterpret_cast<int32_t*>(w + L.off_tos);
+  int32_t* active = reinterpret_cast<int32_t*>(w + L.off_active);
+  int32_t* nact = reinterpret_cast<int32_t*>(w + L.off_nact);
+  void* xin = w + L.off_xin;
+  void* xout = w + L.off_xout;
+
+  hipError_t e = launch_route(L.route, in->x, in->w_gate, in->bias, d.T, d.d_model, d.N, d.dtype, out->expert_id,
+                              out->gate, out->routed_count, out->f, out->P, out->l_aux, w + L.off_route, st);
+  if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/route");
+  e = launch_assign(L.assign, out->expert_id, out->gate, d.T, d.N, C, d.priority, out->slot, tos, out->kept_count,
+                    out->n_dropped, active, nact, w + L.off_assign, st);
+  if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/assign");
+  e = launch_dispatch(in->x, d.dtype, d.T, d.d_model, tos, out->kept_count, d.N, C, xin, st);
+  if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/dispatch");
+  e = launch_ffn(L.ffn, xin, in->w1, in->w2, d.dtype, d.N, C, d.d_model, d.d_ff, out->kept_count, active, nact, xout,
+                 w + L.off_ffn, st);
+  if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/expert_ffn");
+  void* sout = nullptr;
+  if (d.d_ff_shared > 0) {
+    int32_t* dk = reinterpret_cast<int32_t*>(w + L.off_dense);
+    e = launch_dense_plan(dk, dk + 1, dk + 2, (int32_t)d.T, st);
+    if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/shared_plan");
+    sout = w + L.off_sout;
+    e = launch_ffn(L.sffn, in->x, in->ws1, in->ws2, d.dtype, 1, (int)d.T, d.d_model, d.d_ff_shared, dk, dk + 1,
+                   dk + 2, sout, w + L.off_sffn, st);
+    if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/shared_ffn");
+  }
+  e = launch_combine(xout, in->x, sout, d.dtype, d.T, d.d_model, out->expert_id, out->slot, out->gate, d.N, C,
+                     d.flags, out->y, st);
+  if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/combine");
+  return ok();
+}
+
+const char* switch_status_str(switch_status s) {
+  switch (s) {
+    case SWITCH_OK: return "ok";
+    case SWITCH_E_NULL: return "null pointer";
+    case SWITCH_E_SHAPE: return "invalid shape";
+    case SWITCH_E_UNSUPPORTED: return "unsupported value";
+    case SWITCH_E_WORKSPACE: return "workspace too small";
+    case SWITCH_E_HIP: return "HIP launch failure";
+    case SWITCH_E_ALIGN: return "misaligned pointer";
+  }
+  return "unknown status";
+}
+
+const char* switch_last_error(void) { return g_err; }
+
+}  // extern "C"

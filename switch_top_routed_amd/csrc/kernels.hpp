@@ -1,0 +1,62 @@
+// Internal launch interface between the C ABI (api.cpp) and the HIP kernels.
+// Every launcher enqueues on `stream` and returns the launch status.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "switch_moe.h"
+
+namespace swm {
+
+// ---------------- router ----------------
+struct RoutePlan {
+  int split;        // 0: fused kernel; >0: number of k-chunks of the split path
+  int tm;           // 16-token tiles per workgroup (fused path)
+  int64_t nblk;     // number of per-workgroup partial rows
+  size_t off_part_p, off_part_cnt, off_logits, bytes;
+};
+RoutePlan route_plan(int64_t T, int d, int N, int dtype);
+hipError_t launch_route(const RoutePlan& pl, const void* x, const void* wg, const float* bias, int64_t T, int d, int N,
+                        int dtype, int32_t* expert_id, float* gate, int32_t* routed_count, float* f, float* P,
+                        float* l_aux, char* ws, hipStream_t st);
+
+// ---------------- capacity / slots ----------------
+struct AssignPlan {
+  int64_t nblk;  // 256-token blocks
+  size_t off_blockcount, off_blockoff, off_local_rank, off_total, off_seg_start, off_perm, off_keys, bytes;
+};
+AssignPlan assign_plan(int64_t T, int N, int C, int priority);
+hipError_t launch_assign(const AssignPlan& pl, const int32_t* expert_id, const float* gate, int64_t T, int N, int C,
+                         int priority, int32_t* slot, int32_t* token_of_slot, int32_t* kept_count,
+                         int32_t* n_dropped, int32_t* active, int32_t* n_active, char* ws, hipStream_t st);
+
+// ---------------- dispatch / combine ----------------
+hipError_t launch_dispatch(const void* x, int dtype, int64_t T, int d, const int32_t* token_of_slot,
+                           const int32_t* kept_count, int N, int C, void* expert_in, hipStream_t st);
+hipError_t launch_combine(const void* expert_out, const void* x, const void* shared_out, int dtype, int64_t T, int d,
+                          const int32_t* expert_id, const int32_t* slot, const float* gate, int N, int C,
+                          uint32_t flags, void* y, hipStream_t st);
+
+// ---------------- expert FFN ----------------
+struct FfnPlan {
+  int mt;           // 16-row tiles per item (bf16 path)
+  int mch;          // m-chunks per expert
+  int grid;         // persistent workgroups
+  int target;       // item count the split factor aims at
+  int smax;         // largest split factor
+  int64_t part_tiles;   // capacity of the partial buffer, in tiles
+  int64_t n_counters;   // phase-2 tile counters
+  size_t off_h, off_part, off_part2, off_cnt2, bytes;
+};
+FfnPlan ffn_plan(int N, int C, int d, int dff, int dtype);
+// two launches of one kernel (phase 1: H = ReLU(X W1), phase 2: Y = H W2)
+hipError_t launch_ffn(const FfnPlan& pl, const void* xin, const void* w1, const void* w2, int dtype, int N, int C, int d,
+                      int dff, const int32_t* kept_count, const int32_t* active, const int32_t* n_active, void* xout,
+                      char* ws, hipStream_t st);
+// writes {M}, {0}, {1} for the dense (shared-expert) FFN
+hipError_t launch_dense_plan(int32_t* kept, int32_t* active, int32_t* n_active, int32_t M, hipStream_t st);
+
+inline size_t align_up(size_t v, size_t a = 256) { return (v + a - 1) / a * a; }
+
+}  // namespace swm

@@ -1,0 +1,420 @@
+// Router: logits W_g.x (+b), softmax, top-1 argmax, gate value, and the
+// per-expert load statistics f_i, P_i and L_aux = N * sum_i f_i P_i.
+//
+// Sources: "Top-1 Routing" concept page, Core mechanism (gate, softmax,
+// argmax, gate value) and Load balancing (f_i, P_i, L_aux); Switch
+// Transformers summary page, Eq. 4 passage (the same loss, alpha left to the
+// caller) and selective-precision passage (router computed in fp32).
+//
+// bf16 operands meet on MFMA v_mfma_f32_16x16x32_bf16: a bf16 x bf16 product is
+// exact in fp32 and accumulation is fp32, so this is the fp32 router of the
+// selective-precision passage evaluated on bf16-stored inputs.
+//
+// Two shapes:
+//  * fused (T >= 2048 tokens): one workgroup owns TM x 16 tokens and all N
+//    experts; the 4 waves split the expert tiles, logits meet in LDS, then each
+//    wave takes whole tokens for the softmax/argmax (wave reductions) and
+//    accumulates sum_t p[t, i] and the per-expert counts in registers; the 4
+//    waves' partials are summed in LDS in a fixed order and written once per
+//    workgroup.
+//  * split (few tokens, e.g. a 128-token decode batch): the token tiles alone
+//    cannot fill 256 CUs, so the K dimension is cut into chunks, partial logits
+//    go to the workspace, and a second kernel sums them in chunk order and runs
+//    the same epilogue.
+// A final single-workgroup kernel reduces the per-workgroup partials in a
+// fixed order (fp64) into routed_count, f, P and L_aux.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace swm {
+
+constexpr int kRouteThreads = 256;
+
+// logits for `rows` tokens live in LDS lg[m * ldl + n] (no bias yet)
+// lg must hold >= 8 * N floats; it is reused for the cross-wave partial sums.
+// J = experts per lane (N <= 64 * J).
+template <int J>
+__device__ void route_epilogue(float* lg, int ldl, int rows, int64_t t0, int64_t T, int N,
+                               const float* __restrict__ bias, int32_t* __restrict__ expert_id,
+                               float* __restrict__ gate, float* __restrict__ part_p, int32_t* __restrict__ part_cnt,
+                               int64_t blk) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  float bs[J], ps[J];
+  int cn[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int n = lane + 64 * j;
+    bs[j] = (bias != nullptr && n < N) ? bias[n] : 0.f;
+    ps[j] = 0.f;
+    cn[j] = 0;
+  }
+  for (int m = w; m < rows; m += 4) {
+    const int64_t t = t0 + m;
+    if (t >= T) break;
+    float v[J];
+    float best = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int n = lane + 64 * j;
+      v[j] = (n < N) ? lg[m * ldl + n] + bs[j] : -INFINITY;
+      if (n < N && v[j] > best) {  // ascending n: keeps the lowest index on ties
+        best = v[j];
+        bi = n;
+      }
+    }
+    wave_argmax(best, bi);
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int n = lane + 64 * j;
+      v[j] = (n < N) ? __expf(v[j] - best) : 0.f;
+      s += v[j];
+    }
+    s = wave_sum(s);
+    const float inv = 1.0f / s;  // p at the argmax: exp(0) / s
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int n = lane + 64 * j;
+      ps[j] += v[j] * inv;
+      cn[j] += (n == bi) ? 1 : 0;
+    }
+    if (lane == 0) {
+      expert_id[t] = bi;
+      gate[t] = inv;
+    }
+  }
+  __syncthreads();  // every wave is done reading the logits
+  float* red_p = lg;
+  int* red_c = reinterpret_cast<int*>(lg + 4 * N);
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int n = lane + 64 * j;
+    if (n < N) {
+      red_p[w * N + n] = ps[j];
+      red_c[w * N + n] = cn[j];
+    }
+  }
+  __syncthreads();
+  for (int n = threadIdx.x; n < N; n += kRouteThreads) {
+    part_p[blk * N + n] = ((red_p[n] + red_p[N + n]) + red_p[2 * N + n]) + red_p[3 * N + n];
+    part_cnt[blk * N + n] = red_c[n] + red_c[N + n] + red_c[2 * N + n] + red_c[3 * N + n];
+  }
+}
+
+// ----------------------------------------------------------------------------
+// fused bf16 router.  lane l: c = l & 15 selects the A row / B column, kg = l >> 4
+// selects 8 consecutive k.  A = x rows (k contiguous), B = W_g^T, whose
+// fragment is 8 consecutive k of one W_g row (also contiguous).
+// ----------------------------------------------------------------------------
+template <int TM, int NG, int J>
+__global__ __launch_bounds__(kRouteThreads) void route_fused_bf16(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg, const float* __restrict__ bias, int64_t T, int d,
+    int N, int32_t* __restrict__ expert_id, float* __restrict__ gate, float* __restrict__ part_p,
+    int32_t* __restrict__ part_cnt) {
+  extern __shared__ float smem[];
+  const int NT = (N + 15) >> 4;
+  const int ldl = NT * 16;
+  float* lg = smem;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = lane & 15, kg = lane >> 4;
+  const int64_t t0 = (int64_t)blockIdx.x * TM * 16;
+  const int ksteps = d >> 5;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+
+  for (int ntb = w * NG; ntb < NT; ntb += 4 * NG) {
+    f32x4 acc[TM][NG];
+#pragma unroll
+    for (int mt = 0; mt < TM; ++mt)
+#pragma unroll
+      for (int g = 0; g < NG; ++g) acc[mt][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint16_t* bp[NG];
+    bool bvalid[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const int n = (ntb + g) * 16 + c;
+      bvalid[g] = (ntb + g) < NT && n < N;
+      bp[g] = wg + (int64_t)(bvalid[g] ? n : 0) * d + kg * 8;
+    }
+    const uint16_t* ap[TM];
+    bool avalid[TM];
+#pragma unroll
+    for (int mt = 0; mt < TM; ++mt) {
+      const int64_t row = t0 + mt * 16 + c;
+      avalid[mt] = row < T;
+      ap[mt] = x + (avalid[mt] ? row : 0) * (int64_t)d + kg * 8;
+    }
+    for (int ks = 0; ks < ksteps; ++ks) {
+      u32x4 a[TM], b[NG];
+#pragma unroll
+      for (int mt = 0; mt < TM; ++mt)
+        a[mt] = avalid[mt] ? *reinterpret_cast<const u32x4*>(ap[mt] + ks * 32) : zero;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) b[g] = bvalid[g] ? *reinterpret_cast<const u32x4*>(bp[g] + ks * 32) : zero;
+#pragma unroll
+      for (int mt = 0; mt < TM; ++mt)
+#pragma unroll
+        for (int g = 0; g < NG; ++g) acc[mt][g] = mfma_bf16_16x16x32(a[mt], b[g], acc[mt][g]);
+    }
+#pragma unroll
+    for (int mt = 0; mt < TM; ++mt)
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        if (ntb + g < NT) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) lg[(mt * 16 + kg * 4 + i) * ldl + (ntb + g) * 16 + c] = acc[mt][g][i];
+        }
+      }
+  }
+  __syncthreads();
+  route_epilogue<J>(lg, ldl, TM * 16, t0, T, N, bias, expert_id, gate, part_p, part_cnt, blockIdx.x);
+}
+
+// ----------------------------------------------------------------------------
+// split path: partial logits plog[s][t][n] over k-chunk s
+// ----------------------------------------------------------------------------
+template <int NG>
+__global__ __launch_bounds__(kRouteThreads) void route_logits_split_bf16(const uint16_t* __restrict__ x,
+                                                                         const uint16_t* __restrict__ wg, int64_t T,
+                                                                         int d, int N, int S,
+                                                                         float* __restrict__ plog) {
+  const int NT = (N + 15) >> 4;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = lane & 15, kg = lane >> 4;
+  const int64_t t0 = (int64_t)blockIdx.x * 16;
+  const int s = blockIdx.y;
+  const int ksteps = d >> 5;
+  const int ks0 = (int)((int64_t)ksteps * s / S), ks1 = (int)((int64_t)ksteps * (s + 1) / S);
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  const int64_t row = t0 + c;
+  const bool avalid = row < T;
+  const uint16_t* ap = x + (avalid ? row : 0) * (int64_t)d + kg * 8;
+  for (int ntb = w * NG; ntb < NT; ntb += 4 * NG) {
+    f32x4 acc[NG];
+    const uint16_t* bp[NG];
+    bool bvalid[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int n = (ntb + g) * 16 + c;
+      bvalid[g] = (ntb + g) < NT && n < N;
+      bp[g] = wg + (int64_t)(bvalid[g] ? n : 0) * d + kg * 8;
+    }
+    for (int ks = ks0; ks < ks1; ++ks) {
+      const u32x4 a = avalid ? *reinterpret_cast<const u32x4*>(ap + ks * 32) : zero;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const u32x4 b = bvalid[g] ? *reinterpret_cast<const u32x4*>(bp[g] + ks * 32) : zero;
+        acc[g] = mfma_bf16_16x16x32(a, b, acc[g]);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const int n = (ntb + g) * 16 + c;
+      if ((ntb + g) < NT && n < N) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t t = t0 + kg * 4 + i;
+          if (t < T) plog[((int64_t)s * T + t) * N + n] = acc[g][i];
+        }
+      }
+    }
+  }
+}
+
+template <int J>
+__global__ __launch_bounds__(kRouteThreads) void route_softmax_split(const float* __restrict__ plog, int S, int64_t T,
+                                                                     int N, const float* __restrict__ bias,
+                                                                     int32_t* __restrict__ expert_id,
+                                                                     float* __restrict__ gate,
+                                                                     float* __restrict__ part_p,
+                                                                     int32_t* __restrict__ part_cnt) {
+  extern __shared__ float smem[];
+  const int ldl = N;
+  float* lg = smem;
+  const int64_t t0 = (int64_t)blockIdx.x * 16;
+  for (int idx = threadIdx.x; idx < 16 * N; idx += kRouteThreads) {
+    const int m = idx / N, n = idx - m * N;
+    const int64_t t = t0 + m;
+    float v = 0.f;
+    if (t < T)
+      for (int s = 0; s < S; ++s) v += plog[((int64_t)s * T + t) * N + n];
+    lg[m * ldl + n] = v;
+  }
+  __syncthreads();
+  route_epilogue<J>(lg, ldl, 16, t0, T, N, bias, expert_id, gate, part_p, part_cnt, blockIdx.x);
+}
+
+// ----------------------------------------------------------------------------
+// fp32 router: plain fp32 FMA dot products (sequential in k), same epilogue
+// ----------------------------------------------------------------------------
+template <int J>
+__global__ __launch_bounds__(kRouteThreads) void route_f32(const float* __restrict__ x, const float* __restrict__ wg,
+                                                           const float* __restrict__ bias, int64_t T, int d, int N,
+                                                           int32_t* __restrict__ expert_id, float* __restrict__ gate,
+                                                           float* __restrict__ part_p,
+                                                           int32_t* __restrict__ part_cnt) {
+  extern __shared__ float smem[];
+  const int ldl = N;
+  float* lg = smem;
+  const int64_t t0 = (int64_t)blockIdx.x * 16;
+  for (int idx = threadIdx.x; idx < 16 * N; idx += kRouteThreads) {
+    const int m = idx / N, n = idx - m * N;
+    const int64_t t = t0 + m;
+    float acc = 0.f;
+    if (t < T) {
+      const float* xr = x + t * d;
+      const float* wr = wg + (int64_t)n * d;
+      for (int k = 0; k < d; ++k) acc = fmaf(xr[k], wr[k], acc);
+    }
+    lg[m * ldl + n] = acc;
+  }
+  __syncthreads();
+  route_epilogue<J>(lg, ldl, 16, t0, T, N, bias, expert_id, gate, part_p, part_cnt, blockIdx.x);
+}
+
+// ----------------------------------------------------------------------------
+// fixed-order reduction of the per-workgroup partials
+// ----------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void route_finalize(const float* __restrict__ part_p,
+                                                       const int32_t* __restrict__ part_cnt, int64_t nblk, int64_t T,
+                                                       int N, int G, int32_t* __restrict__ routed_count,
+                                                       float* __restrict__ f, float* __restrict__ P,
+                                                       float* __restrict__ l_aux) {
+  __shared__ double sp[1024];
+  __shared__ long long sc[1024];
+  __shared__ double sl[1024];
+  const int tid = threadIdx.x;
+  const int n = tid / G, g = tid - (tid / G) * G;
+  double accp = 0.0;
+  long long accc = 0;
+  if (n < N)
+    for (int64_t b = g; b < nblk; b += G) {
+      accp += (double)part_p[b * N + n];
+      accc += part_cnt[b * N + n];
+    }
+  sp[tid] = accp;
+  sc[tid] = accc;
+  __syncthreads();
+  double term = 0.0;
+  if (n < N && g == 0) {
+    double s = 0.0;
+    long long cnum = 0;
+    for (int i = 0; i < G; ++i) {
+      s += sp[tid + i];
+      cnum += sc[tid + i];
+    }
+    const double fn = (double)cnum / (double)T;
+    const double pn = s / (double)T;
+    routed_count[n] = (int32_t)cnum;
+    f[n] = (float)fn;
+    P[n] = (float)pn;
+    term = fn * pn;
+  }
+  sl[tid] = term;
+  __syncthreads();
+  for (int o = 512; o > 0; o >>= 1) {
+    if (tid < o) sl[tid] += sl[tid + o];
+    __syncthreads();
+  }
+  if (tid == 0) l_aux[0] = (float)((double)N * sl[0]);
+}
+
+// ----------------------------------------------------------------------------
+// host side
+// ----------------------------------------------------------------------------
+RoutePlan route_plan(int64_t T, int d, int N, int dtype) {
+  RoutePlan pl{};
+  const int64_t tiles16 = (T + 15) / 16;
+  if (dtype == 1 && tiles16 >= 128) {
+    const int NT = (N + 15) / 16;
+    int tm = 1;
+    for (int c : {2, 4})
+      if ((T + c * 16 - 1) / (c * 16) >= 256 && (size_t)c * 16 * NT * 16 * 4 <= 64 * 1024) tm = c;
+    pl.split = 0;
+    pl.tm = tm;
+    pl.nblk = (T + tm * 16 - 1) / (tm * 16);
+  } else if (dtype == 1) {
+    const int ksteps = d / 32;
+    int64_t s = (256 + tiles16 - 1) / tiles16;
+    if (s > ksteps) s = ksteps;
+    if (s > 32) s = 32;
+    if (s < 1) s = 1;
+    pl.split = (int)s;
+    pl.tm = 1;
+    pl.nblk = tiles16;
+  } else {
+    pl.split = 0;
+    pl.tm = 1;
+    pl.nblk = tiles16;
+  }
+  size_t off = 0;
+  pl.off_part_p = off;
+  off = align_up(off + (size_t)pl.nblk * N * 4);
+  pl.off_part_cnt = off;
+  off = align_up(off + (size_t)pl.nblk * N * 4);
+  pl.off_logits = off;
+  if (pl.split > 0) off = align_up(off + (size_t)pl.split * T * N * 4);
+  pl.bytes = off;
+  return pl;
+}
+
+template <int J>
+static hipError_t launch_route_j(const RoutePlan& pl, const void* x, const void* wg, const float* bias, int64_t T,
+                                 int d, int N, int dtype, int32_t* expert_id, float* gate, float* part_p,
+                                 int32_t* part_cnt, char* ws, hipStream_t st) {
+  if (dtype == 1 && pl.split == 0) {
+    const int NT = (N + 15) / 16;
+    const size_t lds = (size_t)pl.tm * 16 * NT * 16 * 4;
+    dim3 grid((unsigned)pl.nblk);
+    auto* xb = static_cast<const uint16_t*>(x);
+    auto* wb = static_cast<const uint16_t*>(wg);
+    if (pl.tm == 4)
+      hipLaunchKernelGGL((route_fused_bf16<4, 2, J>), grid, dim3(kRouteThreads), lds, st, xb, wb, bias, T, d, N,
+                         expert_id, gate, part_p, part_cnt);
+    else if (pl.tm == 2)
+      hipLaunchKernelGGL((route_fused_bf16<2, 2, J>), grid, dim3(kRouteThreads), lds, st, xb, wb, bias, T, d, N,
+                         expert_id, gate, part_p, part_cnt);
+    else
+      hipLaunchKernelGGL((route_fused_bf16<1, 2, J>), grid, dim3(kRouteThreads), lds, st, xb, wb, bias, T, d, N,
+                         expert_id, gate, part_p, part_cnt);
+  } else if (dtype == 1) {
+    float* plog = reinterpret_cast<float*>(ws + pl.off_logits);
+    hipLaunchKernelGGL((route_logits_split_bf16<2>), dim3((unsigned)pl.nblk, (unsigned)pl.split), dim3(kRouteThreads),
+                       0, st, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wg), T, d, N, pl.split,
+                       plog);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t lds = (size_t)16 * N * 4;
+    hipLaunchKernelGGL(route_softmax_split<J>, dim3((unsigned)pl.nblk), dim3(kRouteThreads), lds, st, plog, pl.split,
+                       T, N, bias, expert_id, gate, part_p, part_cnt);
+  } else {
+    const size_t lds = (size_t)16 * N * 4;
+    hipLaunchKernelGGL(route_f32<J>, dim3((unsigned)pl.nblk), dim3(kRouteThreads), lds, st,
+                       static_cast<const float*>(x), static_cast<const float*>(wg), bias, T, d, N, expert_id, gate,
+                       part_p, part_cnt);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_route(const RoutePlan& pl, const void* x, const void* wg, const float* bias, int64_t T, int d, int N,
+                        int dtype, int32_t* expert_id, float* gate, int32_t* routed_count, float* f, float* P,
+                        float* l_aux, char* ws, hipStream_t st) {
+  float* part_p = reinterpret_cast<float*>(ws + pl.off_part_p);
+  int32_t* part_cnt = reinterpret_cast<int32_t*>(ws + pl.off_part_cnt);
+  hipError_t e;
+  if (N <= 128)
+    e = launch_route_j<2>(pl, x, wg, bias, T, d, N, dtype, expert_id, gate, part_p, part_cnt, ws, st);
+  else if (N <= 512)
+    e = launch_route_j<8>(pl, x, wg, bias, T, d, N, dtype, expert_id, gate, part_p, part_cnt, ws, st);
+  else
+    e = launch_route_j<16>(pl, x, wg, bias, T, d, N, dtype, expert_id, gate, part_p, part_cnt, ws, st);
+  if (e != hipSuccess) return e;
+  int G = 1;
+  while (G * 2 * N <= 1024) G *= 2;
+  hipLaunchKernelGGL(route_finalize, dim3(1), dim3(1024), 0, st, part_p, part_cnt, pl.nblk, T, N, G, routed_count, f,
+                     P, l_aux);
+  return hipGetLastError();
+}
+
+}  // namespace swm

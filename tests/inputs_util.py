@@ -28,11 +28,13 @@ def stored_router(inp):
 
 def margin_bad_rows(inp):
     l, _, _, _ = stored_router(inp)
+    if l.shape[1] < 2:
+        return np.zeros(0, dtype=np.int64)
     top2 = np.partition(l, -2, axis=1)[:, -2:]
     return np.nonzero(top2[:, 1] - top2[:, 0] < MARGIN)[0]
 
 
-def gate_gap_bad_rows(c_max):
+def gate_gap_bad_rows(c_max, gap=GATE_GAP):
     def bad(inp):
         rows = list(margin_bad_rows(inp))
         l, p, e, g = stored_router(inp)
@@ -40,7 +42,7 @@ def gate_gap_bad_rows(c_max):
             toks = np.nonzero(e == i)[0]
             order = toks[np.lexsort((toks, -g[toks]))][: c_max + 1]
             gg = g[order]
-            close = (gg[:-1] - gg[1:]) < GATE_GAP * gg[:-1]
+            close = (gg[:-1] - gg[1:]) < gap * gg[:-1]
             rows.extend(order[1:][close].tolist())
         return np.array(sorted(set(rows)), dtype=np.int64)
     return bad

@@ -1,0 +1,119 @@
+"""C ABI on the host (no GPU needed): the library loads, exports every function
+the header declares, and rejects bad arguments before launching anything."""
+import ctypes
+
+import pytest
+
+from switch_top_routed_amd import native
+
+E_NULL, E_SHAPE, E_UNSUP, E_WS, E_ALIGN = 1, 2, 3, 4, 6
+FAKE = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
+
+
+@pytest.fixture(scope="module")
+def L():
+    return native.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = native.header_functions()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(native._SIGS)
+
+
+def test_capacity(L):
+    assert L.switch_capacity(4096, 128, 1.25) == 40
+    assert L.switch_capacity(256, 8, 1.0) == 32
+    assert L.switch_capacity(128, 384, 2.0) == 1
+    assert L.switch_capacity(16384, 128, 1.25) == 160
+    assert L.switch_capacity(4096, 128, 0.5) == 16
+    assert L.switch_capacity(0, 8, 1.0) == -1
+    assert L.switch_capacity(10, 8, 0.0) == -1
+    assert L.switch_capacity(10, 1, 5.0) == 10  # clamped to T
+
+
+def test_status_strings(L):
+    for s in range(7):
+        assert L.switch_status_str(s)
+    assert L.switch_status_str(99) == b"unknown status"
+
+
+def _route(L, x=FAKE, wg=FAKE, T=64, d=128, N=8, dtype=1, outs=FAKE, ws=FAKE, wsb=1 << 30):
+    return L.switch_route(x, wg, None, T, d, N, dtype, outs, outs, outs, outs, outs, outs, ws, wsb, None)
+
+
+def test_route_validation(L):
+    assert _route(L, x=None) == E_NULL
+    assert b"x is NULL" in L.switch_last_error()
+    assert _route(L, wg=None) == E_NULL
+    assert _route(L, outs=None) == E_NULL
+    assert _route(L, T=0) == E_SHAPE
+    assert _route(L, N=0) == E_SHAPE
+    assert _route(L, N=1025) == E_SHAPE
+    assert _route(L, d=100) == E_SHAPE  # bf16 needs d % 32 == 0
+    assert _route(L, dtype=7) == E_UNSUP
+    assert _route(L, x=ctypes.c_void_p((1 << 20) + 2)) == E_ALIGN
+    assert _route(L, wsb=0) == E_WS
+    assert _route(L, ws=None) == E_NULL
+
+
+def test_workspace_sizes(L):
+    assert L.switch_route_workspace_bytes(4096, 768, 128, 1) > 0
+    assert L.switch_assign_workspace_bytes(4096, 128, 40, 1) > L.switch_assign_workspace_bytes(4096, 128, 40, 0)
+    assert L.switch_expert_ffn_workspace_bytes(128, 40, 768, 3072, 1) >= 128 * 40 * 3072 * 2
+    d = native.SwitchMoeDesc(T=4096, d_model=768, d_ff=3072, N=128, C=0, capacity_factor=1.25, dtype=1,
+                             priority=0, flags=1, d_ff_shared=0)
+    assert L.switch_moe_workspace_bytes(ctypes.byref(d)) > 0
+    d.d_model = 100
+    assert L.switch_moe_workspace_bytes(ctypes.byref(d)) == 0
+
+
+def test_assign_validation(L):
+    f = L.switch_assign_capacity
+    args = lambda **k: dict(dict(eid=FAKE, gate=FAKE, T=64, N=8, C=8, pr=0), **k)
+
+    def call(**k):
+        a = args(**k)
+        return f(a["eid"], a["gate"], a["T"], a["N"], a["C"], a["pr"], FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                 1 << 30, None)
+    assert call(C=0) == E_SHAPE
+    assert call(C=65) == E_SHAPE
+    assert call(pr=2) == E_UNSUP
+    assert call(eid=None) == E_NULL
+    assert call(gate=None, pr=1) == E_NULL
+
+
+def test_ffn_and_combine_validation(L):
+    ffn = L.switch_expert_ffn
+    assert ffn(FAKE, FAKE, FAKE, 1, 8, 8, 100, 256, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == E_SHAPE
+    assert ffn(FAKE, FAKE, FAKE, 1, 8, 8, 128, 200, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == E_SHAPE
+    assert ffn(None, FAKE, FAKE, 1, 8, 8, 128, 256, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == E_NULL
+    assert ffn(FAKE, FAKE, FAKE, 1, 8, 8, 128, 256, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == E_WS
+    comb = L.switch_combine
+    assert comb(FAKE, FAKE, None, 1, 64, 128, FAKE, FAKE, FAKE, 8, 8, 4, FAKE, None) == E_UNSUP
+    assert comb(FAKE, FAKE, None, 1, 64, 128, FAKE, FAKE, None, 8, 8, 1, FAKE, None) == E_NULL
+    assert comb(FAKE, FAKE, None, 1, 64, 12, FAKE, FAKE, FAKE, 8, 8, 1, FAKE, None) == E_SHAPE
+    disp = L.switch_dispatch
+    assert disp(FAKE, 1, 64, 12, FAKE, FAKE, 8, 8, FAKE, None) == E_SHAPE
+    assert disp(FAKE, 1, 64, 128, FAKE, FAKE, 8, 65, FAKE, None) == E_SHAPE
+
+
+def test_forward_validation(L):
+    d = native.SwitchMoeDesc(T=64, d_model=128, d_ff=128, N=8, C=0, capacity_factor=1.0, dtype=1, priority=0,
+                             flags=1, d_ff_shared=0)
+    ins = native.SwitchMoeInputs(1 << 20, 1 << 20, None, 1 << 20, 1 << 20, None, None)
+    outs = native.SwitchMoeOutputs(*([1 << 20] * 10))
+    fwd = L.switch_moe_forward
+    assert fwd(None, ctypes.byref(ins), ctypes.byref(outs), FAKE, 1 << 30, None) == E_NULL
+    assert fwd(ctypes.byref(d), None, ctypes.byref(outs), FAKE, 1 << 30, None) == E_NULL
+    assert fwd(ctypes.byref(d), ctypes.byref(ins), ctypes.byref(outs), FAKE, 16, None) == E_WS
+    d.flags = 8
+    assert fwd(ctypes.byref(d), ctypes.byref(ins), ctypes.byref(outs), FAKE, 1 << 30, None) == E_UNSUP
+    d.flags = 1
+    d.d_ff_shared = 128
+    assert fwd(ctypes.byref(d), ctypes.byref(ins), ctypes.byref(outs), FAKE, 1 << 30, None) == E_NULL  # ws1 missing
+    d.d_ff_shared = 0
+    d.capacity_factor = 0.0
+    assert fwd(ctypes.byref(d), ctypes.byref(ins), ctypes.byref(outs), FAKE, 1 << 30, None) == E_SHAPE
