@@ -92,5 +92,6 @@ def check_output(y_dev: torch.Tensor, ref: dict, x_stored: np.ndarray, dtype: st
             assert r.max() <= tol, f"dropped rows: max rel err {r.max():.3g}"
         else:
             yb = host_bits(y_dev)[drop]
-            np.testing.assert_array_equal(yb, x_stored[drop])
+            xs = x_stored.view(np.uint32) if x_stored.dtype == np.float32 else x_stored
+            np.testing.assert_array_equal(yb, xs[drop])
     return y
