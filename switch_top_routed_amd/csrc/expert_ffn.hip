@@ -12,33 +12,31 @@
 // every weight byte once for a few dozen FLOPs, so they are bound by HBM on the
 // weights; the kernel is built to stream them:
 //  * W is row-major [K][Ncols] (Ncols contiguous), but an MFMA operand wants
-//    8 consecutive k per lane.  Lane l (c = l & 15, kg = l >> 4) loads the 16
-//    bytes at columns 8c..8c+7 of the 8 rows 8kg..8kg+7 of a 32 x 128 weight
-//    block (8 fully used 256-byte row segments per instruction across the
-//    wave), then transposes that 8 x 8 bf16 tile in registers.  Column j of
-//    the tile becomes the B operand of MFMA j, whose 16 output columns are the
-//    physical columns 8c + j: the weights never touch LDS, and the 8
-//    accumulators of a lane hold 8 consecutive output columns of one row, so
-//    the results leave as 16-byte stores.
+//    8 consecutive k per lane.  Lane l (c = l & 15, kg = l >> 4) loads the 8
+//    bytes at columns 4c..4c+3 of the 8 rows 8kg..8kg+7 of a 32 x 64 weight
+//    block (full 128-byte row segments across the wave), then transposes that
+//    8 x 4 bf16 tile in registers.  Column j of the tile becomes the B operand
+//    of MFMA j, whose 16 output columns are the physical columns 4c + j: the
+//    weights never touch LDS, and the 4 accumulators of a lane hold 4
+//    consecutive output columns of one row, so results leave as 8-byte stores.
 //  * A = token rows (k contiguous), 16 rows per MFMA tile, up to MT tiles per
-//    item.  Rows at or beyond kept_count are neither loaded nor stored, and
-//    tiles beyond kept_count are skipped, so empty capacity slots cost nothing.
-//  * Work item = (active expert, m-chunk of MT*16 rows, 128-column block,
-//    k-split).  The 4 waves of a workgroup take every 4th 32-deep k-step of
-//    the item and meet in LDS (fixed-order sum).  Workgroups are persistent and
-//    walk the item list.  When few experts are active (skewed routing, decode
-//    batches) the items are also split along K so that ~1k items exist; each
-//    split writes an fp32 partial tile and the last workgroup to finish a tile
-//    (agent-scope counter) sums the partials in split order and applies the
-//    epilogue.  The split factor is derived on the device from n_active, so
-//    nothing is synchronised with the host.
+//    item.  Rows at or beyond kept_count are neither loaded (they read as zero
+//    through the buffer descriptor) nor stored, and items beyond kept_count are
+//    skipped, so empty capacity slots cost nothing.
+//  * Work item = (active expert, 64-column block, m-chunk of MT*16 rows).  The
+//    KW waves that share an item (1, 2 or 4, chosen on the device from n_active
+//    so that every wave slot of the persistent grid is busy) take every KW-th
+//    32-deep k-step and meet in LDS (fixed-order sum); with KW == 1 a wave owns
+//    its item.  Each wave keeps STAGES weight blocks in flight in a register
+//    ring and loads its A fragments one step ahead; the k-loop is branch-free
+//    so that the compiler's wait counts keep the ring full.
+// No reduction ever crosses workgroups, so no agent-scope fences (which write
+// back and invalidate whole L2 caches on this multi-XCD part) are needed.
 // fp32 kernel: plain fp32 FMA, one workgroup per (slot row, expert).
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace swm {
-
-constexpr int kFfnThreads = 256;
 
 // in[r] = 8 bf16 of row r (two per dword); out[j] = the 8 rows of column j
 __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
@@ -53,9 +51,56 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[
   }
 }
 
-__device__ __forceinline__ void load_wblock(u32x4 (&br)[8], const uint16_t* p, int64_t ld) {
+// in[r] = 4 bf16 of row r (two per dword); out[j] = the 8 rows of column j
+__device__ __forceinline__ void transpose8x4(const u32x2 (&in)[8], u32x4 (&out)[4]) {
 #pragma unroll
-  for (int r = 0; r < 8; ++r) br[r] = *reinterpret_cast<const u32x4*>(p + r * ld);
+  for (int p = 0; p < 2; ++p) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t a = in[2 * q][p], b = in[2 * q + 1][p];
+      out[2 * p][q] = (a & 0xffffu) | (b << 16);
+      out[2 * p + 1][q] = (a >> 16) | (b & 0xffff0000u);
+    }
+  }
+}
+
+constexpr int kOutOfRange = 0x7ffffff0;  // buffer lane offset that reads as zero
+
+// raw buffer resource over `bytes` bytes from p (dword 3 is the gfx9 raw-buffer format)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+#ifndef SWM_W_CPOL
+#define SWM_W_CPOL 0
+#endif
+
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// weight stream: read once, so it may carry a streaming cache policy
+__device__ __forceinline__ u32x4 buffer_load16_w(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, SWM_W_CPOL));
+}
+
+__device__ __forceinline__ u32x2 buffer_load8(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, SWM_W_CPOL));
+}
+
+
+__device__ __forceinline__ u32x2 pack4(const float (&v)[4], bool relu) {
+  u32x2 o;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    float lo = v[2 * q], hi = v[2 * q + 1];
+    if (relu) {
+      lo = fmaxf(lo, 0.f);
+      hi = fmaxf(hi, 0.f);
+    }
+    o[q] = pack_bf2(lo, hi);
+  }
+  return o;
 }
 
 __device__ __forceinline__ u32x4 pack8(const float (&v)[8], bool relu) {
@@ -72,185 +117,220 @@ __device__ __forceinline__ u32x4 pack8(const float (&v)[8], bool relu) {
   return o;
 }
 
-// split factor along K, identical in every workgroup of a launch
-__device__ __forceinline__ int split_factor(int64_t base, int target, int smax, int ksteps, int64_t part_tiles) {
-  if (base <= 0 || base >= target) return 1;
-  int64_t s = (target + base - 1) / base;
-  if (s > smax) s = smax;
-  if (s > ksteps / 4) s = ksteps / 4;
-  if (s > part_tiles / base) s = part_tiles / base;
-  return s < 1 ? 1 : (int)s;
+#ifndef SWM_FFN_MINB
+#define SWM_FFN_MINB 2
+#endif
+
+
+// Waves of one workgroup that share a work item along K (1, 2 or 4), the same
+// in every workgroup of a launch.  Work is dealt out in rounds of one wave task
+// per wave slot, so the choice maximises the busy fraction of the slots
+// base * KW / (rounds * slots); ties go to the smaller KW (fewer LDS
+// reductions).  Every wave keeps at least 4 k-steps.
+__device__ __forceinline__ int waves_per_item(int64_t base, int64_t wave_slots, int waves, int ksteps) {
+  int best = 1;
+  double best_util = 0.0;
+  for (int kw = 1; kw <= waves; kw *= 2) {
+    if (kw > 1 && ksteps < kw * 4) break;
+    const int64_t tasks = base * kw;
+    const int64_t rounds = (tasks + wave_slots - 1) / wave_slots;
+    const double util = (double)tasks / (double)(rounds * wave_slots);
+    if (util > best_util + 0.02) {
+      best_util = util;
+      best = kw;
+    }
+  }
+  return best;
 }
 
-// phase 1: H = ReLU(X . W1) (K = d_model, Ncols = d_ff)
-// phase 2: Y = H . W2      (K = d_ff,    Ncols = d_model)
-// Phase 1 with a K split leaves fp32 partial tiles in part1 and no bf16 H; phase
-// 2 then sums those partials (split order), applies ReLU and rounds to bf16 as
-// it loads its A operand.  Phase 1 also clears the phase-2 tile counters.
-template <int MT>
-__global__ __launch_bounds__(kFfnThreads, MT <= 2 ? 2 : 1) void ffn_gemm_bf16(
+// One launch computes out = act(A . W) over the filled slots of the active
+// experts: phase 1 (K = d_model, Ncols = d_ff, ReLU) or phase 2 (K = d_ff,
+// Ncols = d_model).  A work item is (active expert, 64-column block, m-chunk of
+// MT*16 rows); the KW waves that share an item take every KW-th 32-deep k-step
+// and meet in LDS; with KW == 1 a wave owns its item and stores directly.  Each
+// wave keeps STAGES weight blocks in flight (register ring) and its A fragments
+// one step ahead.
+// J = columns per lane (4: 64-column waves with 8-byte loads; 8: 128-column
+// waves with 16-byte loads)
+template <int J>
+struct WRow;
+template <>
+struct WRow<4> {
+  typedef u32x2 type;
+  static __device__ __forceinline__ type load(__amdgpu_buffer_rsrc_t r, int v, int s) { return buffer_load8(r, v, s); }
+  static __device__ __forceinline__ void transpose(const type (&in)[8], u32x4 (&out)[4]) { transpose8x4(in, out); }
+};
+template <>
+struct WRow<8> {
+  typedef u32x4 type;
+  static __device__ __forceinline__ type load(__amdgpu_buffer_rsrc_t r, int v, int s) { return buffer_load16_w(r, v, s); }
+  static __device__ __forceinline__ void transpose(const type (&in)[8], u32x4 (&out)[8]) { transpose8x8(in, out); }
+};
+
+template <int J>
+__device__ __forceinline__ void store_row(uint16_t* p, const float (&v)[J], bool relu);
+template <>
+__device__ __forceinline__ void store_row<4>(uint16_t* p, const float (&v)[4], bool relu) {
+  *reinterpret_cast<u32x2*>(p) = pack4(v, relu);
+}
+template <>
+__device__ __forceinline__ void store_row<8>(uint16_t* p, const float (&v)[8], bool relu) {
+  *reinterpret_cast<u32x4*>(p) = pack8(v, relu);
+}
+
+template <int MT, int WAVES, int STAGES, int J>
+__global__ __launch_bounds__(WAVES * 64, SWM_FFN_MINB) void ffn_gemm_bf16(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, uint16_t* __restrict__ out,
-    float* __restrict__ part1, float* __restrict__ part2, int32_t* __restrict__ cnt2, int64_t n_cnt2,
     const int32_t* __restrict__ kept_count, const int32_t* __restrict__ active, const int32_t* __restrict__ n_active,
-    int N, int C, int K, int Ncols, int phase, int mch, int target, int smax, int64_t part_tiles) {
-  __shared__ float red[4 * 4 * 8 * 64];
-  __shared__ int s_last;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, c = lane & 15, kg = lane >> 4;
-  if (phase == 1)
-    for (int64_t i = (int64_t)blockIdx.x * kFfnThreads + tid; i < n_cnt2; i += (int64_t)gridDim.x * kFfnThreads)
-      cnt2[i] = 0;
-  const int NCB = Ncols >> 7;
+    int N, int C, int K, int Ncols, int relu, int mch) {
+  __shared__ float red[WAVES * 4 * J * 64];
+  constexpr int COLS = 16 * J;  // output columns per item
+  const int tid = threadIdx.x, lane = tid & 63, c = lane & 15, kg = lane >> 4;
+  // wave index as a wave-uniform (scalar) value: everything derived from it -- item,
+  // expert, buffer descriptors, row offsets -- then lives in SGPRs
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int NCB = Ncols / COLS;
   int n_act = n_active[0];
   if (n_act > N) n_act = N;
   const int ksteps = K >> 5;
   const int64_t base = (int64_t)n_act * NCB * mch;
   if (base <= 0) return;
-  const int S = split_factor(base, target, smax, ksteps, part_tiles);
-  // phase 2: how phase 1 was split (its K = Ncols here, its Ncols = K here)
-  const int S1 = phase == 2 ? split_factor((int64_t)n_act * (K >> 7) * mch, target, smax, Ncols >> 5, part_tiles) : 1;
-  const bool relu_out = phase == 1;
-  const int64_t items = base * S;
-  constexpr int kTile = MT * 16 * 128;
+  const int KW = waves_per_item(base, (int64_t)gridDim.x * WAVES, WAVES, ksteps);
+  const int groups = WAVES / KW;
+  const int g = w / KW, kw = w - g * KW;
+  const int64_t total_groups = (int64_t)gridDim.x * groups;
+  const int64_t rounds = (base + total_groups - 1) / total_groups;
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  float* part = phase == 1 ? part1 : part2;
+  const int nk = (ksteps - kw + KW - 1) / KW;  // my k-steps: kw, kw + KW, ...
 
-  for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
-    const int mc = (int)(item % mch);
-    int64_t r = item / mch;
-    const int s = (int)(r % S);
-    r /= S;
-    const int cb = (int)(r % NCB);
-    const int a = (int)(r / NCB);
-    const int64_t tile = ((int64_t)a * NCB + cb) * mch + mc;
-    const int e = active[a];
-    if (e < 0 || e >= N) continue;
-    const int m0 = mc * MT * 16;
-    int kept = kept_count[e];
-    if (kept > C) kept = C;
-    int rows = kept - m0;
-    if (rows > MT * 16) rows = MT * 16;
-    if (rows <= 0) continue;
-    const int mtc = (rows + 15) >> 4;
-    const int ks0 = (int)((int64_t)ksteps * s / S), ks1 = (int)((int64_t)ksteps * (s + 1) / S);
+  for (int64_t round = 0; round < rounds; ++round) {
+    const int64_t item = round * total_groups + (int64_t)blockIdx.x * groups + g;
+    int rows = 0, e = 0, cb = 0, m0 = 0;
+    if (item < base) {
+      const int mc = (int)(item % mch);
+      const int64_t r = item / mch;
+      cb = (int)(r % NCB);
+      const int a = (int)(r / NCB);
+      e = __builtin_amdgcn_readfirstlane(active[a]);
+      if (e >= 0 && e < N) {
+        m0 = mc * MT * 16;
+        int kept = __builtin_amdgcn_readfirstlane(kept_count[e]);
+        if (kept > C) kept = C;
+        rows = kept - m0;
+        if (rows > MT * 16) rows = MT * 16;
+      }
+    }
+    const int mtc = rows > 0 ? (rows + 15) >> 4 : 0;  // uniform across the wave
 
-    f32x4 acc[MT][8];
+    f32x4 acc[MT][J];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < J; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const uint16_t* arow[MT];
-    bool aval[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int rr = mt * 16 + c;
-      aval[mt] = rr < rows;
-      arow[mt] = A + ((int64_t)e * C + m0 + (aval[mt] ? rr : 0)) * K + kg * 8;
-    }
-    // phase-1 partial tiles of this expert / m-chunk: tile1 = (a * (K/128) + ks/4) * mch + mc
-    const float* p1 = part1 + (((int64_t)a * (K >> 7)) * mch + mc) * S1 * kTile;
-    const uint16_t* wb = W + (int64_t)e * K * Ncols + (int64_t)(kg * 8) * Ncols + cb * 128 + c * 8;
-
-    int ks = ks0 + w;
-    u32x4 br[8];
-    if (ks < ks1) load_wblock(br, wb + (int64_t)ks * 32 * Ncols, Ncols);
-    for (; ks < ks1; ks += 4) {
-      u32x4 av[MT];
-      if (S1 == 1) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          av[mt] = (mt < mtc && aval[mt]) ? *reinterpret_cast<const u32x4*>(arow[mt] + ks * 32) : zero;
-      } else {
-        const float* pk = p1 + (int64_t)(ks >> 2) * mch * S1 * kTile + (ks & 3) * 32 + kg * 8;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          av[mt] = zero;
-          if (mt < mtc && aval[mt]) {
-            float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            const float* pr = pk + (mt * 16 + c) * 128;
-            for (int s1 = 0; s1 < S1; ++s1) {
-              const f32x4 q0 = *reinterpret_cast<const f32x4*>(pr + (int64_t)s1 * kTile);
-              const f32x4 q1 = *reinterpret_cast<const f32x4*>(pr + (int64_t)s1 * kTile + 4);
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                v[q] += q0[q];
-                v[4 + q] += q1[q];
-              }
-            }
-            av[mt] = pack8(v, true);
-          }
-        }
-      }
-      u32x4 bn[8];
-      if (ks + 4 < ks1) load_wblock(bn, wb + (int64_t)(ks + 4) * 32 * Ncols, Ncols);
-      u32x4 bt[8];
-      transpose8x8(br, bt);
+    if (mtc > 0) {
+      // Buffer loads: one 32-bit lane offset per operand, the per-row and per-step
+      // offsets are wave-uniform SGPR values.  A rows at or beyond `rows` get a lane
+      // offset past the descriptor's extent, so they read as zeros.
+      const __amdgpu_buffer_rsrc_t wres = make_rsrc(W + (int64_t)e * K * Ncols, (int64_t)K * Ncols * 2);
+      const __amdgpu_buffer_rsrc_t ares = make_rsrc(A + ((int64_t)e * C + m0) * K, (int64_t)rows * K * 2);
+      const int w_voff = ((kw * 32 + kg * 8) * Ncols + cb * COLS + c * J) * 2;
+      const int w_row = Ncols * 2;
+      const int w_step = KW * 32 * Ncols * 2;
+      int a_voff[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        if (mt < mtc) {
+        const int rr = mt * 16 + c;
+        a_voff[mt] = rr < rows ? (rr * K + kw * 32 + kg * 8) * 2 : kOutOfRange;
+      }
+      const int a_step = KW * 32 * 2;
+
+      // The k-loop has no data-dependent branches (the waitcnt pass would drain
+      // every load at each join).  The step count is padded to a multiple of
+      // STAGES; prefetches past the last step re-read the last weight block (an L2
+      // hit) and padding steps multiply a zero A fragment.
+      auto load_a = [&](u32x4 (&dst)[MT], int step) {
+        const int so = (step < nk ? step : nk - 1) * a_step;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) acc[mt][j] = mfma_bf16_16x16x32(av[mt], bt[j], acc[mt][j]);
+        for (int mt = 0; mt < MT; ++mt) {
+          const u32x4 v = buffer_load16(ares, a_voff[mt], so);
+          dst[mt] = step < nk ? v : zero;
+        }
+      };
+      typedef typename WRow<J>::type wrow_t;
+      auto load_w = [&](wrow_t (&dst)[8], int step) {
+        const int so = (step < nk ? step : nk - 1) * w_step;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) dst[r] = WRow<J>::load(wres, w_voff, so + r * w_row);
+      };
+      u32x4 acur[MT];
+      load_a(acur, 0);  // oldest load: waiting for it never waits for the weights behind it
+      wrow_t buf[STAGES][8];
+#pragma unroll
+      for (int s = 0; s < STAGES - 1; ++s) load_w(buf[s], s);
+
+      const int nk_pad = (nk + STAGES - 1) / STAGES * STAGES;
+      for (int it = 0; it < nk_pad; it += STAGES) {
+#pragma unroll
+        for (int u = 0; u < STAGES; ++u) {
+          const int cur = it + u;
+          u32x4 anext[MT];
+          load_a(anext, cur + 1);
+          load_w(buf[(u + STAGES - 1) % STAGES], cur + STAGES - 1);
+          u32x4 bt[J];
+          WRow<J>::transpose(buf[u], bt);
+#pragma unroll
+          for (int j = 0; j < J; ++j)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[mt][j] = mfma_bf16_16x16x32(acur[mt], bt[j], acc[mt][j]);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acur[mt] = anext[mt];
         }
       }
-#pragma unroll
-      for (int q = 0; q < 8; ++q) br[q] = bn[q];
     }
 
-    // cross-wave sum in LDS, one 16-row tile at a time; wave w finishes row 4*kg + w
-    const int rl_base = kg * 4 + w;
+    if (KW == 1) {
+      // this wave owns the item: lane holds rows 4*kg + i, columns J*c .. J*c + J-1
+      if (mtc > 0) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      if (mt < mtc) {
+        for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+          for (int i = 0; i < 4; ++i) {
+            const int rl = mt * 16 + kg * 4 + i;
+            if (mt < mtc && rl < rows) {
+              float v[J];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) red[((w * 4 + i) * 8 + j) * 64 + lane] = acc[mt][j][i];
-        __syncthreads();
-        float v[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          v[j] = ((red[((0 * 4 + w) * 8 + j) * 64 + lane] + red[((1 * 4 + w) * 8 + j) * 64 + lane]) +
-                  red[((2 * 4 + w) * 8 + j) * 64 + lane]) +
-                 red[((3 * 4 + w) * 8 + j) * 64 + lane];
-        __syncthreads();
-        const int rl = mt * 16 + rl_base;
-        if (rl < rows) {
-          if (S == 1) {
-            *reinterpret_cast<u32x4*>(out + ((int64_t)e * C + m0 + rl) * Ncols + cb * 128 + c * 8) =
-                pack8(v, relu_out);
-          } else {
-            float* pp = part + (tile * S + s) * kTile + rl * 128 + c * 8;
-            *reinterpret_cast<f32x4*>(pp) = f32x4{v[0], v[1], v[2], v[3]};
-            *reinterpret_cast<f32x4*>(pp + 4) = f32x4{v[4], v[5], v[6], v[7]};
-          }
-        }
-      }
-    }
-    if (S > 1 && phase == 2) {
-      // the last of the S workgroups of this tile sums the partials in split order
-      __threadfence();
-      __syncthreads();
-      if (tid == 0) s_last = (atomicAdd(&cnt2[tile], 1) == S - 1) ? 1 : 0;
-      __syncthreads();
-      if (s_last) {
-        __threadfence();
-        for (int idx = tid; idx < rows * 16; idx += kFfnThreads) {
-          const int rl = idx >> 4, cc = (idx & 15) * 8;
-          float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-          for (int s2 = 0; s2 < S; ++s2) {
-            const float* pp = part + (tile * S + s2) * kTile + rl * 128 + cc;
-            const f32x4 q0 = *reinterpret_cast<const f32x4*>(pp);
-            const f32x4 q1 = *reinterpret_cast<const f32x4*>(pp + 4);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              v[q] += q0[q];
-              v[4 + q] += q1[q];
+              for (int j = 0; j < J; ++j) v[j] = acc[mt][j][i];
+              store_row<J>(out + ((int64_t)e * C + m0 + rl) * Ncols + cb * COLS + c * J, v, relu);
             }
           }
-          *reinterpret_cast<u32x4*>(out + ((int64_t)e * C + m0 + rl) * Ncols + cb * 128 + cc) = pack8(v, false);
         }
       }
-      __syncthreads();
+    } else {
+      // the KW waves of a group sum their partials in LDS (fixed order); wave kw
+      // of the group finishes rows 4*kg + i for i = kw, kw + KW, ...
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) red[((w * 4 + i) * J + j) * 64 + lane] = acc[mt][j][i];
+        __syncthreads();
+        if (mt < mtc) {
+          for (int i = kw; i < 4; i += KW) {
+            float v[J];
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+              float sum = 0.f;
+              for (int q = 0; q < KW; ++q) sum += red[(((g * KW + q) * 4 + i) * J + j) * 64 + lane];
+              v[j] = sum;
+            }
+            const int rl = mt * 16 + kg * 4 + i;
+            if (rl < rows) store_row<J>(out + ((int64_t)e * C + m0 + rl) * Ncols + cb * COLS + c * J, v, relu);
+          }
+        }
+        __syncthreads();
+      }
     }
   }
 }
@@ -285,6 +365,13 @@ __global__ void dense_plan(int32_t* kept, int32_t* active, int32_t* n_active, in
 }
 
 // ----------------------------------------------------------------------------
+#ifndef SWM_FFN_STAGES
+#define SWM_FFN_STAGES 2
+#endif
+#ifndef SWM_FFN_WAVES
+#define SWM_FFN_WAVES 4
+#endif
+
 FfnPlan ffn_plan(int N, int C, int d, int dff, int dtype) {
   FfnPlan pl{};
   size_t off = 0;
@@ -294,19 +381,7 @@ FfnPlan ffn_plan(int N, int C, int d, int dff, int dtype) {
   if (dtype == 1) {
     pl.mt = C <= 16 ? 1 : C <= 32 ? 2 : C <= 48 ? 3 : 4;
     pl.mch = (C + pl.mt * 16 - 1) / (pl.mt * 16);
-    pl.grid = 1024;
-    pl.target = 1024;
-    pl.smax = 16;
-    // a split only happens when base < target, so base * S < 2 * target tiles
-    pl.part_tiles = 2 * (int64_t)pl.target;
-    pl.n_counters = (int64_t)N * (d / 128) * pl.mch;
-    const size_t part_bytes = (size_t)pl.part_tiles * pl.mt * 16 * 128 * 4;
-    pl.off_part = off;
-    off = align_up(off + part_bytes);
-    pl.off_part2 = off;
-    off = align_up(off + part_bytes);
-    pl.off_cnt2 = off;
-    off = align_up(off + (size_t)pl.n_counters * 4);
+    pl.grid = 0;  // persistent grid: resident workgroups per CU x CUs, resolved at launch
   }
   pl.bytes = off;
   return pl;
@@ -317,26 +392,59 @@ hipError_t launch_dense_plan(int32_t* kept, int32_t* active, int32_t* n_active, 
   return hipGetLastError();
 }
 
-template <int MT>
-static hipError_t launch_gemm(const FfnPlan& pl, const void* A, const void* W, void* out, char* ws,
-                              const int32_t* kept, const int32_t* active, const int32_t* n_active, int N, int C, int K,
-                              int Ncols, int phase, hipStream_t st) {
-  hipLaunchKernelGGL((ffn_gemm_bf16<MT>), dim3(pl.grid), dim3(kFfnThreads), 0, st, static_cast<const uint16_t*>(A),
-                     static_cast<const uint16_t*>(W), static_cast<uint16_t*>(out),
-                     reinterpret_cast<float*>(ws + pl.off_part), reinterpret_cast<float*>(ws + pl.off_part2),
-                     reinterpret_cast<int32_t*>(ws + pl.off_cnt2), pl.n_counters, kept, active, n_active, N, C, K,
-                     Ncols, phase, pl.mch, pl.target, pl.smax, pl.part_tiles);
+// resident workgroups of `kernel` on the whole device (occupancy x CUs), cached
+// per (kernel, device)
+static int persistent_grid(const void* kernel, int threads) {
+  struct Entry {
+    const void* kernel;
+    int device, grid;
+  };
+  static thread_local Entry cache[16];
+  static thread_local int used = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  for (int i = 0; i < used; ++i)
+    if (cache[i].kernel == kernel && cache[i].device == dev) return cache[i].grid;
+  int per_cu = 1, cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu < 1) per_cu = 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+  const int grid = per_cu * cus;
+  if (used < 16) cache[used++] = Entry{kernel, dev, grid};
+  return grid;
+}
+
+template <int MT, int J>
+static hipError_t launch_gemm(const void* A, const void* W, void* out, const int32_t* kept, const int32_t* active,
+                              const int32_t* n_active, int N, int C, int K, int Ncols, int relu, int mch,
+                              hipStream_t st) {
+  constexpr int kWaves = SWM_FFN_WAVES;
+  auto kern = ffn_gemm_bf16<MT, kWaves, SWM_FFN_STAGES, J>;
+  const int grid = persistent_grid(reinterpret_cast<const void*>(kern), kWaves * 64);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kWaves * 64), 0, st, static_cast<const uint16_t*>(A),
+                     static_cast<const uint16_t*>(W), static_cast<uint16_t*>(out), kept, active, n_active, N, C, K,
+                     Ncols, relu, mch);
   return hipGetLastError();
 }
 
-static hipError_t gemm_bf16(const FfnPlan& pl, const void* A, const void* W, void* out, char* ws, const int32_t* kept,
-                            const int32_t* active, const int32_t* n_active, int N, int C, int K, int Ncols, int phase,
+// 128-column waves (16-byte weight loads) for wide outputs; 64-column waves when
+// the output is narrow, which doubles the work items of few-expert launches
+template <int MT>
+static hipError_t launch_gemm_cols(const void* A, const void* W, void* out, const int32_t* kept,
+                                   const int32_t* active, const int32_t* n_active, int N, int C, int K, int Ncols,
+                                   int relu, int mch, hipStream_t st) {
+  if (Ncols >= 2048 && Ncols % 128 == 0)
+    return launch_gemm<MT, 8>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, mch, st);
+  return launch_gemm<MT, 4>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, mch, st);
+}
+
+static hipError_t gemm_bf16(const FfnPlan& pl, const void* A, const void* W, void* out, const int32_t* kept,
+                            const int32_t* active, const int32_t* n_active, int N, int C, int K, int Ncols, int relu,
                             hipStream_t st) {
   switch (pl.mt) {
-    case 1: return launch_gemm<1>(pl, A, W, out, ws, kept, active, n_active, N, C, K, Ncols, phase, st);
-    case 2: return launch_gemm<2>(pl, A, W, out, ws, kept, active, n_active, N, C, K, Ncols, phase, st);
-    case 3: return launch_gemm<3>(pl, A, W, out, ws, kept, active, n_active, N, C, K, Ncols, phase, st);
-    default: return launch_gemm<4>(pl, A, W, out, ws, kept, active, n_active, N, C, K, Ncols, phase, st);
+    case 1: return launch_gemm_cols<1>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, pl.mch, st);
+    case 2: return launch_gemm_cols<2>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, pl.mch, st);
+    case 3: return launch_gemm_cols<3>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, pl.mch, st);
+    default: return launch_gemm_cols<4>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, pl.mch, st);
   }
 }
 
@@ -355,9 +463,9 @@ hipError_t launch_ffn(const FfnPlan& pl, const void* xin, const void* w1, const 
                        dff, d, 0);
     return hipGetLastError();
   }
-  hipError_t e = gemm_bf16(pl, xin, w1, h, ws, kept_count, active, n_active, N, C, d, dff, 1, st);
+  hipError_t e = gemm_bf16(pl, xin, w1, h, kept_count, active, n_active, N, C, d, dff, 1, st);
   if (e != hipSuccess) return e;
-  return gemm_bf16(pl, h, w2, xout, ws, kept_count, active, n_active, N, C, dff, d, 2, st);
+  return gemm_bf16(pl, h, w2, xout, kept_count, active, n_active, N, C, dff, d, 0, st);
 }
 
 }  // namespace swm

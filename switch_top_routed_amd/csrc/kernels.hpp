@@ -40,14 +40,10 @@ hipError_t launch_combine(const void* expert_out, const void* x, const void* sha
 
 // ---------------- expert FFN ----------------
 struct FfnPlan {
-  int mt;           // 16-row tiles per item (bf16 path)
-  int mch;          // m-chunks per expert
-  int grid;         // persistent workgroups
-  int target;       // item count the split factor aims at
-  int smax;         // largest split factor
-  int64_t part_tiles;   // capacity of the partial buffer, in tiles
-  int64_t n_counters;   // phase-2 tile counters
-  size_t off_h, off_part, off_part2, off_cnt2, bytes;
+  int mt;    // 16-row tiles per work item (bf16 path)
+  int mch;   // m-chunks per expert
+  int grid;  // persistent workgroups
+  size_t off_h, bytes;
 };
 FfnPlan ffn_plan(int N, int C, int d, int dff, int dtype);
 // two launches of one kernel (phase 1: H = ReLU(X W1), phase 2: Y = H W2)
