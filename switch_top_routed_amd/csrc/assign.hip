@@ -73,7 +73,18 @@ __global__ __launch_bounds__(1024) void assign_scan(const int32_t* __restrict__ 
   const int n = threadIdx.x;
   int run = 0, kept = 0;
   if (n < N) {
-    for (int64_t b = 0; b < nblk; ++b) {
+    int64_t b = 0;
+    for (; b + 8 <= nblk; b += 8) {  // 8 loads in flight, then the running sum
+      int cv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) cv[u] = blockcount[(b + u) * N + n];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        blockoff[(b + u) * N + n] = run;
+        run += cv[u];
+      }
+    }
+    for (; b < nblk; ++b) {
       const int c = blockcount[b * N + n];
       blockoff[b * N + n] = run;
       run += c;

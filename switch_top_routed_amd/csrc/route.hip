@@ -276,39 +276,60 @@ __global__ __launch_bounds__(kRouteThreads) void route_f32(const float* __restri
 // ----------------------------------------------------------------------------
 // fixed-order reduction of the per-workgroup partials
 // ----------------------------------------------------------------------------
+// thread tid: expert n = tid % NP (consecutive lanes read consecutive experts, so
+// every load is coalesced), block group g = tid / NP takes blocks g, g + G, ...
+// (NP = N rounded up to 64, G = 1024 / NP); the G partial sums are combined in g
+// order, the N products in a fixed tree order.
 __global__ __launch_bounds__(1024) void route_finalize(const float* __restrict__ part_p,
                                                        const int32_t* __restrict__ part_cnt, int64_t nblk, int64_t T,
-                                                       int N, int G, int32_t* __restrict__ routed_count,
+                                                       int N, int NP, int32_t* __restrict__ routed_count,
                                                        float* __restrict__ f, float* __restrict__ P,
                                                        float* __restrict__ l_aux) {
   __shared__ double sp[1024];
   __shared__ long long sc[1024];
   __shared__ double sl[1024];
   const int tid = threadIdx.x;
-  const int n = tid / G, g = tid - (tid / G) * G;
+  const int G = 1024 / NP;
+  const int n = tid % NP, g = tid / NP;
   double accp = 0.0;
   long long accc = 0;
-  if (n < N)
-    for (int64_t b = g; b < nblk; b += G) {
+  if (n < N && g < G) {
+    int64_t b = g;
+    for (; b + 7 * (int64_t)G < nblk; b += 8 * (int64_t)G) {  // 8 coalesced loads in flight
+      float pv[8];
+      int cv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        pv[u] = part_p[(b + u * (int64_t)G) * N + n];
+        cv[u] = part_cnt[(b + u * (int64_t)G) * N + n];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        accp += (double)pv[u];
+        accc += cv[u];
+      }
+    }
+    for (; b < nblk; b += G) {
       accp += (double)part_p[b * N + n];
       accc += part_cnt[b * N + n];
     }
+  }
   sp[tid] = accp;
   sc[tid] = accc;
   __syncthreads();
   double term = 0.0;
-  if (n < N && g == 0) {
+  if (tid < N) {
     double s = 0.0;
     long long cnum = 0;
     for (int i = 0; i < G; ++i) {
-      s += sp[tid + i];
-      cnum += sc[tid + i];
+      s += sp[i * NP + tid];
+      cnum += sc[i * NP + tid];
     }
     const double fn = (double)cnum / (double)T;
     const double pn = s / (double)T;
-    routed_count[n] = (int32_t)cnum;
-    f[n] = (float)fn;
-    P[n] = (float)pn;
+    routed_count[tid] = (int32_t)cnum;
+    f[tid] = (float)fn;
+    P[tid] = (float)pn;
     term = fn * pn;
   }
   sl[tid] = term;
@@ -410,9 +431,8 @@ hipError_t launch_route(const RoutePlan& pl, const void* x, const void* wg, cons
   else
     e = launch_route_j<16>(pl, x, wg, bias, T, d, N, dtype, expert_id, gate, part_p, part_cnt, ws, st);
   if (e != hipSuccess) return e;
-  int G = 1;
-  while (G * 2 * N <= 1024) G *= 2;
-  hipLaunchKernelGGL(route_finalize, dim3(1), dim3(1024), 0, st, part_p, part_cnt, pl.nblk, T, N, G, routed_count, f,
+  const int NP = (N + 63) / 64 * 64;
+  hipLaunchKernelGGL(route_finalize, dim3(1), dim3(1024), 0, st, part_p, part_cnt, pl.nblk, T, N, NP, routed_count, f,
                      P, l_aux);
   return hipGetLastError();
 }
