@@ -56,7 +56,9 @@ def main():
 
     wl = workloads.WORKLOADS[args.workload]
     dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
-    inp = workloads.make_inputs(wl)
+    weight_bytes = 2 * wl.N * wl.d_model * wl.d_ff * (2 if wl.dtype == "bf16" else 4)
+    on_device = weight_bytes > (4 << 30)  # draw very large weight sets on the GPU
+    inp = workloads.make_inputs(wl, weights=not on_device)
 
     def dev(a):
         if a is None:
@@ -65,8 +67,12 @@ def main():
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
         return torch.from_numpy(a).cuda()
 
-    x, wg, w1, w2 = dev(inp.x), dev(inp.w_gate), dev(inp.w1), dev(inp.w2)
-    ws1, ws2 = dev(inp.ws1), dev(inp.ws2)
+    x, wg = dev(inp.x), dev(inp.w_gate)
+    if on_device:
+        W = workloads.make_device_weights(wl)
+        w1, w2, ws1, ws2 = W["w1"], W["w2"], W.get("ws1"), W.get("ws2")
+    else:
+        w1, w2, ws1, ws2 = dev(inp.w1), dev(inp.w2), dev(inp.ws1), dev(inp.ws2)
     bias = None if inp.bias is None else torch.from_numpy(inp.bias).cuda()
     layer = sw.SwitchMoE(wl.T, wl.d_model, wl.d_ff, wl.N, dtype=dt, capacity_factor=wl.capacity_factor,
                          priority=wl.priority, gate_scale=wl.gate_scale, residual_all=wl.residual_all,
@@ -155,7 +161,7 @@ def main():
                 "traffic": None, "bytes_per_launch": ffn_launch_bytes, "launch_us": launch_s * 1e6}
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not on_device:
         cpu = cpu_baseline(inp)
 
     line = {

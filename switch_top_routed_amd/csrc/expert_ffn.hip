@@ -432,7 +432,7 @@ template <int MT>
 static hipError_t launch_gemm_cols(const void* A, const void* W, void* out, const int32_t* kept,
                                    const int32_t* active, const int32_t* n_active, int N, int C, int K, int Ncols,
                                    int relu, int mch, hipStream_t st) {
-  if (Ncols >= 2048 && Ncols % 128 == 0)
+  if (MT <= 3 && Ncols >= 2048 && Ncols % 128 == 0)  // 4 tiles x 128 columns would spill
     return launch_gemm<MT, 8>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, mch, st);
   return launch_gemm<MT, 4>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, mch, st);
 }
