@@ -37,6 +37,9 @@ def parse():
     ap.add_argument("--workload", default="switch-base-uniform")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stage-iters", type=int, default=50)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a device-to-device copy of BYTES bytes (5 times): the reference kernel whose "
+                         "FETCH_SIZE / WRITE_SIZE counters scale the measured HBM traffic")
     return ap.parse_args()
 
 
@@ -50,6 +53,15 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.calibrate_copy:
+        src = torch.ones(args.calibrate_copy, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": args.calibrate_copy}), flush=True)
+        return
 
     import switch_top_routed_amd as sw
     import workloads

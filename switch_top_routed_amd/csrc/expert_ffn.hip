@@ -65,6 +65,7 @@ __device__ __forceinline__ void transpose8x4(const u32x2 (&in)[8], u32x4 (&out)[
 }
 
 constexpr int kOutOfRange = 0x7ffffff0;  // buffer lane offset that reads as zero
+constexpr int kXcds = 8;                  // accelerator complex dies of an MI355X
 
 // raw buffer resource over `bytes` bytes from p (dword 3 is the gfx9 raw-buffer format)
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes) {
@@ -198,15 +199,22 @@ __global__ __launch_bounds__(WAVES * 64, SWM_FFN_MINB) void ffn_gemm_bf16(
   const int KW = waves_per_item(base, (int64_t)gridDim.x * WAVES, WAVES, ksteps);
   const int groups = WAVES / KW;
   const int g = w / KW, kw = w - g * KW;
-  const int64_t total_groups = (int64_t)gridDim.x * groups;
-  const int64_t rounds = (base + total_groups - 1) / total_groups;
+  // Workgroups are dealt to the 8 XCDs round-robin (blockIdx % 8).  Each XCD
+  // takes one contiguous range of the expert-major item list, so the column
+  // blocks of an expert -- which all read its activation rows -- share one L2.
+  const int nx = (gridDim.x % kXcds == 0) ? kXcds : 1;
+  const int xcd = blockIdx.x % nx;
+  const int64_t slots_x = (int64_t)(gridDim.x / nx) * groups;
+  const int64_t per_x = (base + nx - 1) / nx;
+  const int64_t rounds = (per_x + slots_x - 1) / slots_x;
   const u32x4 zero = {0u, 0u, 0u, 0u};
   const int nk = (ksteps - kw + KW - 1) / KW;  // my k-steps: kw, kw + KW, ...
 
   for (int64_t round = 0; round < rounds; ++round) {
-    const int64_t item = round * total_groups + (int64_t)blockIdx.x * groups + g;
+    const int64_t local = round * slots_x + (int64_t)(blockIdx.x / nx) * groups + g;
+    const int64_t item = xcd * per_x + local;
     int rows = 0, e = 0, cb = 0, m0 = 0;
-    if (item < base) {
+    if (local < per_x && item < base) {
       const int mc = (int)(item % mch);
       const int64_t r = item / mch;
       cb = (int)(r % NCB);
@@ -277,6 +285,9 @@ __global__ __launch_bounds__(WAVES * 64, SWM_FFN_MINB) void ffn_gemm_bf16(
           u32x4 anext[MT];
           load_a(anext, cur + 1);
           load_w(buf[(u + STAGES - 1) % STAGES], cur + STAGES - 1);
+          // keep the prefetches ahead of this step's math: the scheduler would sink
+          // them below the MFMAs, and the next step would then wait for them
+          __builtin_amdgcn_sched_barrier(0);
           u32x4 bt[J];
           WRow<J>::transpose(buf[u], bt);
 #pragma unroll
@@ -371,6 +382,10 @@ __global__ void dense_plan(int32_t* kept, int32_t* active, int32_t* n_active, in
 #ifndef SWM_FFN_WAVES
 #define SWM_FFN_WAVES 4
 #endif
+#ifndef SWM_FFN_ALLOW128
+#define SWM_FFN_ALLOW128 1
+#endif
+constexpr bool kAllow128 = SWM_FFN_ALLOW128;
 
 FfnPlan ffn_plan(int N, int C, int d, int dff, int dtype) {
   FfnPlan pl{};
@@ -432,7 +447,7 @@ template <int MT>
 static hipError_t launch_gemm_cols(const void* A, const void* W, void* out, const int32_t* kept,
                                    const int32_t* active, const int32_t* n_active, int N, int C, int K, int Ncols,
                                    int relu, int mch, hipStream_t st) {
-  if (MT <= 3 && Ncols >= 2048 && Ncols % 128 == 0)  // 4 tiles x 128 columns would spill
+  if (kAllow128 && MT <= 3 && Ncols >= 2048 && Ncols % 128 == 0)  // 4 tiles x 128 columns would spill
     return launch_gemm<MT, 8>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, mch, st);
   return launch_gemm<MT, 4>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, mch, st);
 }
