@@ -80,4 +80,31 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total
   return base + incl - v;
 }
 
+// Register transposes of bf16 tiles (for B operands stored [K][N]).
+// in[r] = 8 bf16 of row r (two per dword); out[j] = the 8 rows of column j
+__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t a = in[2 * q][p], b = in[2 * q + 1][p];
+      out[2 * p][q] = (a & 0xffffu) | (b << 16);
+      out[2 * p + 1][q] = (a >> 16) | (b & 0xffff0000u);
+    }
+  }
+}
+
+// in[r] = 4 bf16 of row r (two per dword); out[j] = the 8 rows of column j
+__device__ __forceinline__ void transpose8x4(const u32x2 (&in)[8], u32x4 (&out)[4]) {
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t a = in[2 * q][p], b = in[2 * q + 1][p];
+      out[2 * p][q] = (a & 0xffffu) | (b << 16);
+      out[2 * p + 1][q] = (a >> 16) | (b & 0xffff0000u);
+    }
+  }
+}
+
 }  // namespace swm

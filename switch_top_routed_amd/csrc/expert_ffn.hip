@@ -38,32 +38,6 @@
 
 namespace swm {
 
-// in[r] = 8 bf16 of row r (two per dword); out[j] = the 8 rows of column j
-__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t a = in[2 * q][p], b = in[2 * q + 1][p];
-      out[2 * p][q] = (a & 0xffffu) | (b << 16);
-      out[2 * p + 1][q] = (a >> 16) | (b & 0xffff0000u);
-    }
-  }
-}
-
-// in[r] = 4 bf16 of row r (two per dword); out[j] = the 8 rows of column j
-__device__ __forceinline__ void transpose8x4(const u32x2 (&in)[8], u32x4 (&out)[4]) {
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t a = in[2 * q][p], b = in[2 * q + 1][p];
-      out[2 * p][q] = (a & 0xffffu) | (b << 16);
-      out[2 * p + 1][q] = (a >> 16) | (b & 0xffff0000u);
-    }
-  }
-}
-
 constexpr int kOutOfRange = 0x7ffffff0;  // buffer lane offset that reads as zero
 constexpr int kXcds = 8;                  // accelerator complex dies of an MI355X
 
@@ -477,6 +451,11 @@ hipError_t launch_ffn(const FfnPlan& pl, const void* xin, const void* w1, const 
                        static_cast<const float*>(w2), static_cast<float*>(xout), kept_count, active, n_active, N, C,
                        dff, d, 0);
     return hipGetLastError();
+  }
+  if (tiled_ffn_applies(C, d, dff)) {
+    hipError_t e = launch_tiled_gemm(xin, w1, h, kept_count, active, n_active, N, C, d, dff, 1, st);
+    if (e != hipSuccess) return e;
+    return launch_tiled_gemm(h, w2, xout, kept_count, active, n_active, N, C, dff, d, 0, st);
   }
   hipError_t e = gemm_bf16(pl, xin, w1, h, kept_count, active, n_active, N, C, d, dff, 1, st);
   if (e != hipSuccess) return e;

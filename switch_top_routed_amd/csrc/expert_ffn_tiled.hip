@@ -1,0 +1,229 @@
+// Expert FFN for large per-expert row counts: an LDS-tiled MFMA GEMM.
+//
+// Same operation as the weight-streaming kernel (out = act(A . W) over the
+// filled slots of the active experts; "Top-1 Routing" page, Key parameters and
+// compute), used when an expert holds more than 64 rows (capacity C > 64) and
+// for the always-on shared dense expert (N = 1, C = T rows).  There the work per
+// weight byte is high enough that MFMA throughput and panel reuse matter:
+//  * a workgroup (4 waves, 2 x 2) owns a BM x 256 output tile, BM = 32 * MTW
+//    (128, 192 or 256 rows), and walks K in 32-deep steps;
+//  * per step the A rows (k contiguous) go to LDS as they are; the W block
+//    (32 k-rows x 256 columns, columns contiguous) is loaded 8 bytes per lane
+//    per row, transposed 8 x 4 in registers and written to LDS k-contiguous, so
+//    every MFMA fragment is one ds_read_b128.  Both LDS tiles store 16-byte
+//    chunks XOR-swizzled by row, which keeps the reads free of bank conflicts;
+//  * the W columns are permuted in LDS so that MFMA j of a wave reads 16
+//    consecutive LDS rows yet produces the physical columns 8c + j: a lane's 8
+//    accumulators then hold 8 consecutive output columns (16-byte stores);
+//  * global loads run two steps ahead of the MFMAs (register ring) and LDS is
+//    double-buffered, one barrier per step;
+//  * tiles are dealt to the 8 XCDs in contiguous ranges and, inside an expert,
+//    grouped 8 m-chunks at a time per column block, so that the workgroups
+//    running together on one XCD share A and W panels in its L2.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace swm {
+
+namespace {
+
+constexpr int kTileN = 256;
+constexpr int kTiledXcds = 8;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 tload16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+__device__ __forceinline__ u32x2 tload8(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+
+// byte offset of 16-byte chunk q (0..3) of LDS row r (64 bytes per row)
+__device__ __forceinline__ int lds_off(int r, int q) { return r * 64 + ((q ^ ((r >> 1) & 3)) << 4); }
+
+// LDS row of tile column col (0..255): wave half wn = col / 128, lane c = (col % 128) / 8,
+// MFMA j = col % 8  ->  row wn * 128 + 16 j + c
+__device__ __forceinline__ int col_row(int col) {
+  const int cc = col & 127;
+  return (col & 128) + ((cc & 7) << 4) + (cc >> 3);
+}
+
+__device__ __forceinline__ u32x4 pack8t(const f32x4 (&acc)[8], int i, bool relu) {
+  u32x4 o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float lo = acc[2 * q][i], hi = acc[2 * q + 1][i];
+    if (relu) {
+      lo = fmaxf(lo, 0.f);
+      hi = fmaxf(hi, 0.f);
+    }
+    o[q] = pack_bf2(lo, hi);
+  }
+  return o;
+}
+
+}  // namespace
+
+template <int MTW>
+__global__ __launch_bounds__(256, 1) void ffn_tile_bf16(const uint16_t* __restrict__ A,
+                                                        const uint16_t* __restrict__ W, uint16_t* __restrict__ out,
+                                                        const int32_t* __restrict__ kept_count,
+                                                        const int32_t* __restrict__ active,
+                                                        const int32_t* __restrict__ n_active, int N, int C, int K,
+                                                        int Ncols, int relu, int mch) {
+  constexpr int BM = 32 * MTW;          // tile rows (2 waves x MTW x 16)
+  constexpr int ACH = BM * 4 / 256;     // 16-byte A chunks per thread per step
+  constexpr int BUF = (BM + kTileN) * 64;  // bytes per LDS buffer
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * BUF];
+
+  const int tid = threadIdx.x, lane = tid & 63, c = lane & 15, kg = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w >> 1, wn = w & 1;
+  const int NT = Ncols / kTileN;
+  int n_act = n_active[0];
+  if (n_act > N) n_act = N;
+  const int64_t tiles = (int64_t)n_act * mch * NT;
+  const int nx = (gridDim.x % kTiledXcds == 0) ? kTiledXcds : 1;
+  const int64_t per_x = (tiles + nx - 1) / nx;
+  const int64_t local = blockIdx.x / nx;
+  const int64_t tile = (int64_t)(blockIdx.x % nx) * per_x + local;
+  if (local >= per_x || tile >= tiles) return;
+
+  // tile -> (active expert a, m-chunk mc, column block nt); inside an expert,
+  // groups of up to 8 m-chunks walk the column blocks together
+  const int64_t per_e = (int64_t)mch * NT;
+  const int a = (int)(tile / per_e);
+  const int rr = (int)(tile - (int64_t)a * per_e);
+  const int GM = mch < 8 ? mch : 8;
+  const int grp = rr / (GM * NT);
+  const int gm_here = (mch - grp * GM) < GM ? (mch - grp * GM) : GM;
+  const int in_g = rr - grp * GM * NT;
+  const int mc = grp * GM + in_g % gm_here;
+  const int nt = in_g / gm_here;
+
+  const int e = __builtin_amdgcn_readfirstlane(active[a]);
+  if (e < 0 || e >= N) return;
+  int kept = __builtin_amdgcn_readfirstlane(kept_count[e]);
+  if (kept > C) kept = C;
+  const int m0 = mc * BM;
+  int rows = kept - m0;
+  if (rows <= 0) return;
+  if (rows > BM) rows = BM;
+  const int n0 = nt * kTileN;
+  const int ksteps = K >> 5;
+
+  const __amdgpu_buffer_rsrc_t ares = tile_rsrc(A + ((int64_t)e * C + m0) * K, (int64_t)rows * K * 2);
+  const __amdgpu_buffer_rsrc_t wres = tile_rsrc(W + (int64_t)e * K * Ncols, (int64_t)K * Ncols * 2);
+
+  // per-thread load coordinates
+  int a_voff[ACH], a_lds[ACH];
+#pragma unroll
+  for (int i = 0; i < ACH; ++i) {
+    const int ch = tid + i * 256, r = ch >> 2, q = ch & 3;
+    a_voff[i] = r < rows ? (r * K + q * 8) * 2 : 0x7ffffff0;  // rows past `rows` read zero
+    a_lds[i] = lds_off(r, q);
+  }
+  const int w_voff = ((kg * 8) * Ncols + n0 + w * 64 + c * 4) * 2;
+  int b_lds[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) b_lds[j] = BM * 64 + lds_off(col_row(w * 64 + c * 4 + j), kg);
+
+  u32x4 ra[2][ACH];
+  u32x2 rw[2][8];
+  auto load_step = [&](int slot, int s) {
+    const int sc = s < ksteps ? s : ksteps - 1;  // past the end: re-read the last step (cache hit)
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) ra[slot][i] = tload16(ares, a_voff[i], sc * 64);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) rw[slot][r] = tload8(wres, w_voff, (sc * 32 + r) * Ncols * 2);
+  };
+  auto store_step = [&](int slot, int buf) {
+    unsigned char* base = lds + buf * BUF;
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) *reinterpret_cast<u32x4*>(base + a_lds[i]) = ra[slot][i];
+    u32x4 bt[4];
+    transpose8x4(rw[slot], bt);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(base + b_lds[j]) = bt[j];
+  };
+
+  f32x4 acc[MTW][8];
+#pragma unroll
+  for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  int a_rd[MTW], b_rd[8];
+#pragma unroll
+  for (int mt = 0; mt < MTW; ++mt) a_rd[mt] = lds_off(wm * (BM / 2) + mt * 16 + c, kg);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) b_rd[j] = BM * 64 + lds_off(wn * 128 + 16 * j + c, kg);
+
+  load_step(0, 0);
+  load_step(1, 1);
+  store_step(0, 0);
+  __syncthreads();
+  const int kpad = (ksteps + 1) & ~1;
+  for (int it = 0; it < kpad; it += 2) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int s = it + u;
+      load_step(u, s + 2);  // slot u held step s, already in LDS
+      __builtin_amdgcn_sched_barrier(0);
+      const unsigned char* base = lds + u * BUF;
+      const bool live = s < ksteps;
+      u32x4 bf[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) bf[j] = *reinterpret_cast<const u32x4*>(base + b_rd[j]);
+#pragma unroll
+      for (int mt = 0; mt < MTW; ++mt) {
+        u32x4 af = *reinterpret_cast<const u32x4*>(base + a_rd[mt]);
+        if (!live) af = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[mt][j] = mfma_bf16_16x16x32(af, bf[j], acc[mt][j]);
+      }
+      store_step(u ^ 1, u ^ 1);  // step s + 1 (loaded one iteration ago) into the other buffer
+      __syncthreads();
+    }
+  }
+
+  // lane holds rows 4*kg + i of each 16-row tile, columns 8c..8c+7 of its half
+#pragma unroll
+  for (int mt = 0; mt < MTW; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rl = wm * (BM / 2) + mt * 16 + kg * 4 + i;
+      if (rl < rows)
+        *reinterpret_cast<u32x4*>(out + ((int64_t)e * C + m0 + rl) * Ncols + n0 + wn * 128 + c * 8) =
+            pack8t(acc[mt], i, relu != 0);
+    }
+  }
+}
+
+template <int MTW>
+static hipError_t launch_tiled(const void* A, const void* W, void* out, const int32_t* kept, const int32_t* active,
+                               const int32_t* n_active, int N, int C, int K, int Ncols, int relu, hipStream_t st) {
+  constexpr int BM = 32 * MTW;
+  const int mch = (C + BM - 1) / BM;
+  int64_t grid = (int64_t)N * mch * (Ncols / kTileN);
+  grid = (grid + kTiledXcds - 1) / kTiledXcds * kTiledXcds;
+  hipLaunchKernelGGL((ffn_tile_bf16<MTW>), dim3((unsigned)grid), dim3(256), 0, st, static_cast<const uint16_t*>(A),
+                     static_cast<const uint16_t*>(W), static_cast<uint16_t*>(out), kept, active, n_active, N, C, K,
+                     Ncols, relu, mch);
+  return hipGetLastError();
+}
+
+bool tiled_ffn_applies(int C, int d, int dff) { return C > 64 && d % kTileN == 0 && dff % kTileN == 0; }
+
+hipError_t launch_tiled_gemm(const void* A, const void* W, void* out, const int32_t* kept, const int32_t* active,
+                             const int32_t* n_active, int N, int C, int K, int Ncols, int relu, hipStream_t st) {
+  if (C <= 128) return launch_tiled<4>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st);
+  if (C <= 192) return launch_tiled<6>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st);
+  return launch_tiled<8>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st);
+}
+
+}  // namespace swm
