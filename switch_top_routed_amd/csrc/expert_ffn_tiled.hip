@@ -15,7 +15,7 @@
 //  * the W columns are permuted in LDS so that MFMA j of a wave reads 16
 //    consecutive LDS rows yet produces the physical columns 8c + j: a lane's 8
 //    accumulators then hold 8 consecutive output columns (16-byte stores);
-//  * global loads run two steps ahead of the MFMAs (register ring) and LDS is
+//  * global loads run P steps ahead of the MFMAs (register ring) and LDS is
 //    double-buffered, one barrier per step;
 //  * tiles are dealt to the 8 XCDs in contiguous ranges and, inside an expert,
 //    grouped 8 m-chunks at a time per column block, so that the workgroups
@@ -68,7 +68,7 @@ __device__ __forceinline__ u32x4 pack8t(const f32x4 (&acc)[8], int i, bool relu)
 
 }  // namespace
 
-template <int MTW>
+template <int MTW, int P>
 __global__ __launch_bounds__(256, 1) void ffn_tile_bf16(const uint16_t* __restrict__ A,
                                                         const uint16_t* __restrict__ W, uint16_t* __restrict__ out,
                                                         const int32_t* __restrict__ kept_count,
@@ -132,8 +132,8 @@ __global__ __launch_bounds__(256, 1) void ffn_tile_bf16(const uint16_t* __restri
 #pragma unroll
   for (int j = 0; j < 4; ++j) b_lds[j] = BM * 64 + lds_off(col_row(w * 64 + c * 4 + j), kg);
 
-  u32x4 ra[2][ACH];
-  u32x2 rw[2][8];
+  u32x4 ra[P][ACH];
+  u32x2 rw[P][8];
   auto load_step = [&](int slot, int s) {
     const int sc = s < ksteps ? s : ksteps - 1;  // past the end: re-read the last step (cache hit)
 #pragma unroll
@@ -163,18 +163,21 @@ __global__ __launch_bounds__(256, 1) void ffn_tile_bf16(const uint16_t* __restri
 #pragma unroll
   for (int j = 0; j < 8; ++j) b_rd[j] = BM * 64 + lds_off(wn * 128 + 16 * j + c, kg);
 
-  load_step(0, 0);
-  load_step(1, 1);
+  // register ring: slot s % P holds step s from its load (issued P iterations
+  // earlier) until it is written to LDS buffer s % 2 one iteration before its MFMAs
+#pragma unroll
+  for (int s0 = 0; s0 < P; ++s0) load_step(s0, s0);
   store_step(0, 0);
   __syncthreads();
-  const int kpad = (ksteps + 1) & ~1;
-  for (int it = 0; it < kpad; it += 2) {
+  const int kpad = (ksteps + P - 1) / P * P;
+  for (int it = 0; it < kpad; it += P) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < P; ++u) {
       const int s = it + u;
-      load_step(u, s + 2);  // slot u held step s, already in LDS
+      // slot u held step s (in LDS since the last iteration): reload it with step s + P
+      load_step(u, s + P);
       __builtin_amdgcn_sched_barrier(0);
-      const unsigned char* base = lds + u * BUF;
+      const unsigned char* base = lds + (s & 1) * BUF;
       const bool live = s < ksteps;
       u32x4 bf[8];
 #pragma unroll
@@ -186,7 +189,7 @@ __global__ __launch_bounds__(256, 1) void ffn_tile_bf16(const uint16_t* __restri
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[mt][j] = mfma_bf16_16x16x32(af, bf[j], acc[mt][j]);
       }
-      store_step(u ^ 1, u ^ 1);  // step s + 1 (loaded one iteration ago) into the other buffer
+      store_step((u + 1) % P, (s + 1) & 1);  // step s + 1 into the other buffer
       __syncthreads();
     }
   }
@@ -204,6 +207,13 @@ __global__ __launch_bounds__(256, 1) void ffn_tile_bf16(const uint16_t* __restri
   }
 }
 
+#ifndef SWM_TILE_P
+#define SWM_TILE_P 4
+#endif
+#ifndef SWM_DENSE_MTW
+#define SWM_DENSE_MTW 8
+#endif
+
 template <int MTW>
 static hipError_t launch_tiled(const void* A, const void* W, void* out, const int32_t* kept, const int32_t* active,
                                const int32_t* n_active, int N, int C, int K, int Ncols, int relu, hipStream_t st) {
@@ -211,7 +221,7 @@ static hipError_t launch_tiled(const void* A, const void* W, void* out, const in
   const int mch = (C + BM - 1) / BM;
   int64_t grid = (int64_t)N * mch * (Ncols / kTileN);
   grid = (grid + kTiledXcds - 1) / kTiledXcds * kTiledXcds;
-  hipLaunchKernelGGL((ffn_tile_bf16<MTW>), dim3((unsigned)grid), dim3(256), 0, st, static_cast<const uint16_t*>(A),
+  hipLaunchKernelGGL((ffn_tile_bf16<MTW, (MTW >= 8 ? 2 : SWM_TILE_P)>), dim3((unsigned)grid), dim3(256), 0, st, static_cast<const uint16_t*>(A),
                      static_cast<const uint16_t*>(W), static_cast<uint16_t*>(out), kept, active, n_active, N, C, K,
                      Ncols, relu, mch);
   return hipGetLastError();
@@ -223,7 +233,7 @@ hipError_t launch_tiled_gemm(const void* A, const void* W, void* out, const int3
                              const int32_t* n_active, int N, int C, int K, int Ncols, int relu, hipStream_t st) {
   if (C <= 128) return launch_tiled<4>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st);
   if (C <= 192) return launch_tiled<6>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st);
-  return launch_tiled<8>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st);
+  return launch_tiled<SWM_DENSE_MTW>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st);
 }
 
 }  // namespace swm
