@@ -6,17 +6,23 @@
 // for the always-on shared dense expert (N = 1, C = T rows).  There the work per
 // weight byte is high enough that MFMA throughput and panel reuse matter:
 //  * a workgroup (4 waves, 2 x 2) owns a BM x 256 output tile, BM = 32 * MTW
-//    (128, 192 or 256 rows), and walks K in 32-deep steps;
+//    (128 or 192 rows), and walks K in 32-deep steps;
 //  * per step the A rows (k contiguous) go to LDS as they are; the W block
 //    (32 k-rows x 256 columns, columns contiguous) is loaded 8 bytes per lane
 //    per row, transposed 8 x 4 in registers and written to LDS k-contiguous, so
 //    every MFMA fragment is one ds_read_b128.  Both LDS tiles store 16-byte
-//    chunks XOR-swizzled by row, which keeps the reads free of bank conflicts;
+//    chunks XOR-swizzled by row; the swizzle keeps the fragment reads, the A
+//    stores and the transposed W stores free of bank conflicts whether the LDS
+//    serves 8 lanes x 16 bytes or 16 lanes x 16 bytes per clock;
 //  * the W columns are permuted in LDS so that MFMA j of a wave reads 16
 //    consecutive LDS rows yet produces the physical columns 8c + j: a lane's 8
 //    accumulators then hold 8 consecutive output columns (16-byte stores);
 //  * global loads run P steps ahead of the MFMAs (register ring) and LDS is
 //    double-buffered, one barrier per step;
+//  * 128-row tiles fit in half the register file, so two workgroups share a
+//    CU (two waves per SIMD): one wave's MFMAs then overlap the other's loads,
+//    LDS traffic and barrier.  That beats a single 256-row workgroup per CU,
+//    whose lone wave per SIMD runs its memory work and its MFMAs in series;
 //  * tiles are dealt to the 8 XCDs in contiguous ranges and, inside an expert,
 //    grouped 8 m-chunks at a time per column block, so that the workgroups
 //    running together on one XCD share A and W panels in its L2.
@@ -42,8 +48,15 @@ __device__ __forceinline__ u32x2 tload8(__amdgpu_buffer_rsrc_t r, int voff, int 
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
 }
 
-// byte offset of 16-byte chunk q (0..3) of LDS row r (64 bytes per row)
-__device__ __forceinline__ int lds_off(int r, int q) { return r * 64 + ((q ^ ((r >> 1) & 3)) << 4); }
+// byte offset of 16-byte chunk q (0..3) of LDS row r (64 bytes per row).  The
+// chunk is XORed with two parity bits of the row: bit 0 = r1 ^ r2, bit 1 =
+// r1 ^ r3 ^ r6 (r_i = bit i of r), chosen by exhaustive search over linear
+// swizzles so that 8 (and 16) consecutive lanes of every b128 access in this
+// kernel cover distinct banks.
+__device__ __forceinline__ int lds_swz(int r) {
+  return (((r >> 1) ^ (r >> 2)) & 1) | ((((r >> 1) ^ (r >> 3) ^ (r >> 6)) & 1) << 1);
+}
+__device__ __forceinline__ int lds_off(int r, int q) { return r * 64 + ((q ^ lds_swz(r)) << 4); }
 
 // LDS row of tile column col (0..255): wave half wn = col / 128, lane c = (col % 128) / 8,
 // MFMA j = col % 8  ->  row wn * 128 + 16 j + c
@@ -69,7 +82,7 @@ __device__ __forceinline__ u32x4 pack8t(const f32x4 (&acc)[8], int i, bool relu)
 }  // namespace
 
 template <int MTW, int P>
-__global__ __launch_bounds__(256, 1) void ffn_tile_bf16(const uint16_t* __restrict__ A,
+__global__ __launch_bounds__(256, (MTW <= 4 ? 2 : 1)) void ffn_tile_bf16(const uint16_t* __restrict__ A,
                                                         const uint16_t* __restrict__ W, uint16_t* __restrict__ out,
                                                         const int32_t* __restrict__ kept_count,
                                                         const int32_t* __restrict__ active,
@@ -210,9 +223,6 @@ __global__ __launch_bounds__(256, 1) void ffn_tile_bf16(const uint16_t* __restri
 #ifndef SWM_TILE_P
 #define SWM_TILE_P 4
 #endif
-#ifndef SWM_DENSE_MTW
-#define SWM_DENSE_MTW 8
-#endif
 
 template <int MTW>
 static hipError_t launch_tiled(const void* A, const void* W, void* out, const int32_t* kept, const int32_t* active,
@@ -221,7 +231,7 @@ static hipError_t launch_tiled(const void* A, const void* W, void* out, const in
   const int mch = (C + BM - 1) / BM;
   int64_t grid = (int64_t)N * mch * (Ncols / kTileN);
   grid = (grid + kTiledXcds - 1) / kTiledXcds * kTiledXcds;
-  hipLaunchKernelGGL((ffn_tile_bf16<MTW, (MTW >= 8 ? 2 : SWM_TILE_P)>), dim3((unsigned)grid), dim3(256), 0, st, static_cast<const uint16_t*>(A),
+  hipLaunchKernelGGL((ffn_tile_bf16<MTW, (MTW <= 4 ? 2 : SWM_TILE_P)>), dim3((unsigned)grid), dim3(256), 0, st, static_cast<const uint16_t*>(A),
                      static_cast<const uint16_t*>(W), static_cast<uint16_t*>(out), kept, active, n_active, N, C, K,
                      Ncols, relu, mch);
   return hipGetLastError();
@@ -231,9 +241,10 @@ bool tiled_ffn_applies(int C, int d, int dff) { return C > 64 && d % kTileN == 0
 
 hipError_t launch_tiled_gemm(const void* A, const void* W, void* out, const int32_t* kept, const int32_t* active,
                              const int32_t* n_active, int N, int C, int K, int Ncols, int relu, hipStream_t st) {
-  if (C <= 128) return launch_tiled<4>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st);
-  if (C <= 192) return launch_tiled<6>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st);
-  return launch_tiled<SWM_DENSE_MTW>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st);
+  // 192-row tiles for 128 < C <= 192 (one m-chunk per expert: each weight
+  // panel is streamed once); 128-row tiles, two workgroups per CU, otherwise
+  if (C > 128 && C <= 192) return launch_tiled<6>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st);
+  return launch_tiled<4>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st);
 }
 
 }  // namespace swm
