@@ -58,17 +58,20 @@ __device__ __forceinline__ int lds_swz(int r) {
 }
 __device__ __forceinline__ int lds_off(int r, int q) { return r * 64 + ((q ^ lds_swz(r)) << 4); }
 
-// LDS row of tile column col (0..255): wave half wn = col / 128, lane c = (col % 128) / 8,
-// MFMA j = col % 8  ->  row wn * 128 + 16 j + c
+// LDS row of tile column col (0..32 NJ - 1) for waves of 16 NJ columns: wave
+// half wn = col / (16 NJ), lane c = (col % (16 NJ)) / NJ, MFMA j = col % NJ
+//   ->  row wn * 16 NJ + 16 j + c
+template <int NJ>
 __device__ __forceinline__ int col_row(int col) {
-  const int cc = col & 127;
-  return (col & 128) + ((cc & 7) << 4) + (cc >> 3);
+  const int cc = col % (16 * NJ);
+  return (col - cc) + ((cc % NJ) << 4) + cc / NJ;
 }
 
-__device__ __forceinline__ u32x4 pack8t(const f32x4 (&acc)[8], int i, bool relu) {
-  u32x4 o;
+// row i of a lane's NJ accumulators as NJ bf16 (NJ / 2 dwords)
+template <int NJ>
+__device__ __forceinline__ void pack_row(const f32x4 (&acc)[NJ], int i, bool relu, uint32_t (&o)[NJ / 2]) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < NJ / 2; ++q) {
     float lo = acc[2 * q][i], hi = acc[2 * q + 1][i];
     if (relu) {
       lo = fmaxf(lo, 0.f);
@@ -76,27 +79,45 @@ __device__ __forceinline__ u32x4 pack8t(const f32x4 (&acc)[8], int i, bool relu)
     }
     o[q] = pack_bf2(lo, hi);
   }
-  return o;
+}
+
+// in[r] = 4 bf16 of k-row r (two per dword); out[j] = the 4 k-rows of column j
+__device__ __forceinline__ void transpose4x4(const u32x2 (&in)[4], u32x2 (&out)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int dw = j >> 1, sh = (j & 1) * 16;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t a = (in[2 * h][dw] >> sh) & 0xffffu, b = (in[2 * h + 1][dw] >> sh) & 0xffffu;
+      out[j][h] = a | (b << 16);
+    }
+  }
 }
 
 }  // namespace
 
-template <int MTW, int P>
-__global__ __launch_bounds__(256, (MTW <= 4 ? 2 : 1)) void ffn_tile_bf16(const uint16_t* __restrict__ A,
-                                                        const uint16_t* __restrict__ W, uint16_t* __restrict__ out,
-                                                        const int32_t* __restrict__ kept_count,
-                                                        const int32_t* __restrict__ active,
-                                                        const int32_t* __restrict__ n_active, int N, int C, int K,
-                                                        int Ncols, int relu, int mch) {
-  constexpr int BM = 32 * MTW;          // tile rows (2 waves x MTW x 16)
-  constexpr int ACH = BM * 4 / 256;     // 16-byte A chunks per thread per step
-  constexpr int BUF = (BM + kTileN) * 64;  // bytes per LDS buffer
+// MTW m-tiles x NJ n-tiles of 16 x 16 per wave; the tile is BM = 32 MTW rows
+// by TN = 32 NJ columns (NJ = 8: 256 columns, NJ = 4: 128 columns).  Tiles
+// whose accumulators fit in a quarter of the register file run two
+// workgroups per CU.
+template <int MTW, int NJ, int P>
+__global__ __launch_bounds__(256, (MTW * NJ <= 32 ? 2 : 1)) void ffn_tile_bf16(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, uint16_t* __restrict__ out,
+    const int32_t* __restrict__ kept_count, const int32_t* __restrict__ active, const int32_t* __restrict__ n_active,
+    int N, int C, int K, int Ncols, int relu, int mch) {
+  static_assert(NJ == 4 || NJ == 8, "tile width 128 or 256 columns");
+  static_assert(8 % P == 0, "prefetch depth divides the k-steps of a 256-multiple K");
+  constexpr int BM = 32 * MTW;                 // tile rows (2 waves x MTW x 16)
+  constexpr int TN = 32 * NJ;                  // tile columns (2 waves x 16 lanes x NJ)
+  constexpr int ACH = (BM * 4 + 255) / 256;    // 16-byte A chunks per thread per step
+  constexpr int BUF = (BM + TN) * 64;          // bytes per LDS buffer
+  constexpr int WLD = NJ == 8 ? 8 : 4;         // W loads (8 bytes) per thread per step
   __shared__ __attribute__((aligned(16))) unsigned char lds[2 * BUF];
 
   const int tid = threadIdx.x, lane = tid & 63, c = lane & 15, kg = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w >> 1, wn = w & 1;
-  const int NT = Ncols / kTileN;
+  const int NT = Ncols / TN;
   int n_act = n_active[0];
   if (n_act > N) n_act = N;
   const int64_t tiles = (int64_t)n_act * mch * NT;
@@ -126,13 +147,13 @@ __global__ __launch_bounds__(256, (MTW <= 4 ? 2 : 1)) void ffn_tile_bf16(const u
   int rows = kept - m0;
   if (rows <= 0) return;
   if (rows > BM) rows = BM;
-  const int n0 = nt * kTileN;
+  const int n0 = nt * TN;
   const int ksteps = K >> 5;
 
   const __amdgpu_buffer_rsrc_t ares = tile_rsrc(A + ((int64_t)e * C + m0) * K, (int64_t)rows * K * 2);
   const __amdgpu_buffer_rsrc_t wres = tile_rsrc(W + (int64_t)e * K * Ncols, (int64_t)K * Ncols * 2);
 
-  // per-thread load coordinates
+  // A: chunk ch = tid + 256 i is 16-byte chunk ch % 4 of tile row ch / 4
   int a_voff[ACH], a_lds[ACH];
 #pragma unroll
   for (int i = 0; i < ACH; ++i) {
@@ -140,82 +161,112 @@ __global__ __launch_bounds__(256, (MTW <= 4 ? 2 : 1)) void ffn_tile_bf16(const u
     a_voff[i] = r < rows ? (r * K + q * 8) * 2 : 0x7ffffff0;  // rows past `rows` read zero
     a_lds[i] = lds_off(r, q);
   }
-  const int w_voff = ((kg * 8) * Ncols + n0 + w * 64 + c * 4) * 2;
-  int b_lds[4];
+  // W, 256 columns: thread (w, c, kg) loads k-rows 8 kg .. 8 kg + 7 of columns
+  //   64 w + 4 c .. + 3, transposes 8 x 4 and writes four 16-byte k-chunks;
+  // W, 128 columns: thread (kq = 2 w + (lane & 1), c4 = lane / 2) loads k-rows
+  //   4 kq .. 4 kq + 3 of columns 4 c4 .. + 3, transposes 4 x 4 and writes four
+  //   8-byte half-chunks (adjacent lanes fill the two halves of one chunk)
+  int w_voff, b_lds[4];
+  if (NJ == 8) {
+    w_voff = ((kg * 8) * Ncols + n0 + w * 64 + c * 4) * 2;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) b_lds[j] = BM * 64 + lds_off(col_row(w * 64 + c * 4 + j), kg);
+    for (int j = 0; j < 4; ++j) b_lds[j] = BM * 64 + lds_off(col_row<NJ>(w * 64 + c * 4 + j), kg);
+  } else {
+    const int kq = 2 * w + (lane & 1), c4 = lane >> 1;
+    w_voff = ((kq * 4) * Ncols + n0 + c4 * 4) * 2;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b_lds[j] = BM * 64 + lds_off(col_row<NJ>(c4 * 4 + j), kq >> 1) + (kq & 1) * 8;
+  }
 
   u32x4 ra[P][ACH];
-  u32x2 rw[P][8];
+  u32x2 rw[P][WLD];
   auto load_step = [&](int slot, int s) {
     const int sc = s < ksteps ? s : ksteps - 1;  // past the end: re-read the last step (cache hit)
 #pragma unroll
     for (int i = 0; i < ACH; ++i) ra[slot][i] = tload16(ares, a_voff[i], sc * 64);
 #pragma unroll
-    for (int r = 0; r < 8; ++r) rw[slot][r] = tload8(wres, w_voff, (sc * 32 + r) * Ncols * 2);
+    for (int r = 0; r < WLD; ++r) rw[slot][r] = tload8(wres, w_voff, (sc * 32 + r) * Ncols * 2);
   };
   auto store_step = [&](int slot, int buf) {
     unsigned char* base = lds + buf * BUF;
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) *reinterpret_cast<u32x4*>(base + a_lds[i]) = ra[slot][i];
-    u32x4 bt[4];
-    transpose8x4(rw[slot], bt);
+    for (int i = 0; i < ACH; ++i)
+      if (i < ACH - 1 || BM * 4 % 256 == 0 || w < (BM * 4 % 256) / 64)  // wave-uniform tail
+        *reinterpret_cast<u32x4*>(base + a_lds[i]) = ra[slot][i];
+    if (NJ == 8) {
+      u32x2 in8[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(base + b_lds[j]) = bt[j];
+      for (int r = 0; r < 8; ++r) in8[r] = rw[slot][r % WLD];
+      u32x4 bt[4];
+      transpose8x4(in8, bt);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(base + b_lds[j]) = bt[j];
+    } else {
+      u32x2 in4[4], bt[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) in4[r] = rw[slot][r];
+      transpose4x4(in4, bt);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x2*>(base + b_lds[j]) = bt[j];
+    }
   };
 
-  f32x4 acc[MTW][8];
+  f32x4 acc[MTW][NJ];
 #pragma unroll
   for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NJ; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  int a_rd[MTW], b_rd[8];
+  int a_rd[MTW], b_rd[NJ];
 #pragma unroll
   for (int mt = 0; mt < MTW; ++mt) a_rd[mt] = lds_off(wm * (BM / 2) + mt * 16 + c, kg);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) b_rd[j] = BM * 64 + lds_off(wn * 128 + 16 * j + c, kg);
+  for (int j = 0; j < NJ; ++j) b_rd[j] = BM * 64 + lds_off(wn * 16 * NJ + 16 * j + c, kg);
 
-  // register ring: slot s % P holds step s from its load (issued P iterations
-  // earlier) until it is written to LDS buffer s % 2 one iteration before its MFMAs
+  // register ring: slot s % P holds step s from its load (issued P steps
+  // earlier) until it is written to LDS buffer s % 2 one step before its MFMAs.
+  // K is a multiple of 256, so ksteps is a multiple of 8 and of P.
 #pragma unroll
   for (int s0 = 0; s0 < P; ++s0) load_step(s0, s0);
   store_step(0, 0);
   __syncthreads();
-  const int kpad = (ksteps + P - 1) / P * P;
-  for (int it = 0; it < kpad; it += P) {
+  for (int it = 0; it < ksteps; it += P) {
 #pragma unroll
     for (int u = 0; u < P; ++u) {
       const int s = it + u;
-      // slot u held step s (in LDS since the last iteration): reload it with step s + P
+      // slot u held step s (in LDS since the last step): reload it with step s + P
       load_step(u, s + P);
       __builtin_amdgcn_sched_barrier(0);
-      const unsigned char* base = lds + (s & 1) * BUF;
-      const bool live = s < ksteps;
-      u32x4 bf[8];
+      const unsigned char* base = lds + (u & 1) * BUF;
+      u32x4 bf[NJ];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) bf[j] = *reinterpret_cast<const u32x4*>(base + b_rd[j]);
+      for (int j = 0; j < NJ; ++j) bf[j] = *reinterpret_cast<const u32x4*>(base + b_rd[j]);
 #pragma unroll
       for (int mt = 0; mt < MTW; ++mt) {
-        u32x4 af = *reinterpret_cast<const u32x4*>(base + a_rd[mt]);
-        if (!live) af = u32x4{0u, 0u, 0u, 0u};
+        const u32x4 af = *reinterpret_cast<const u32x4*>(base + a_rd[mt]);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[mt][j] = mfma_bf16_16x16x32(af, bf[j], acc[mt][j]);
+        for (int j = 0; j < NJ; ++j) acc[mt][j] = mfma_bf16_16x16x32(af, bf[j], acc[mt][j]);
       }
-      store_step((u + 1) % P, (s + 1) & 1);  // step s + 1 into the other buffer
+      store_step((u + 1) % P, (u + 1) & 1);  // step s + 1 into the other buffer
       __syncthreads();
     }
   }
 
-  // lane holds rows 4*kg + i of each 16-row tile, columns 8c..8c+7 of its half
+  // lane holds rows 4 kg + i of each 16-row tile, columns NJ c .. NJ c + NJ - 1 of its half
 #pragma unroll
   for (int mt = 0; mt < MTW; ++mt) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int rl = wm * (BM / 2) + mt * 16 + kg * 4 + i;
-      if (rl < rows)
-        *reinterpret_cast<u32x4*>(out + ((int64_t)e * C + m0 + rl) * Ncols + n0 + wn * 128 + c * 8) =
-            pack8t(acc[mt], i, relu != 0);
+      uint32_t o[NJ / 2];
+      pack_row<NJ>(acc[mt], i, relu != 0, o);
+      uint16_t* dst = out + ((int64_t)e * C + m0 + rl) * Ncols + n0 + wn * 16 * NJ + c * NJ;
+      if (rl < rows) {
+        if (NJ == 8)
+          *reinterpret_cast<u32x4*>(dst) = u32x4{o[0], o[1], o[2 % (NJ / 2)], o[3 % (NJ / 2)]};
+        else
+          *reinterpret_cast<u32x2*>(dst) = u32x2{o[0], o[1]};
+      }
     }
   }
 }
@@ -224,16 +275,16 @@ __global__ __launch_bounds__(256, (MTW <= 4 ? 2 : 1)) void ffn_tile_bf16(const u
 #define SWM_TILE_P 4
 #endif
 
-template <int MTW>
+template <int MTW, int NJ, int P>
 static hipError_t launch_tiled(const void* A, const void* W, void* out, const int32_t* kept, const int32_t* active,
                                const int32_t* n_active, int N, int C, int K, int Ncols, int relu, hipStream_t st) {
-  constexpr int BM = 32 * MTW;
+  constexpr int BM = 32 * MTW, TN = 32 * NJ;
   const int mch = (C + BM - 1) / BM;
-  int64_t grid = (int64_t)N * mch * (Ncols / kTileN);
+  int64_t grid = (int64_t)N * mch * (Ncols / TN);
   grid = (grid + kTiledXcds - 1) / kTiledXcds * kTiledXcds;
-  hipLaunchKernelGGL((ffn_tile_bf16<MTW, (MTW <= 4 ? 2 : SWM_TILE_P)>), dim3((unsigned)grid), dim3(256), 0, st, static_cast<const uint16_t*>(A),
-                     static_cast<const uint16_t*>(W), static_cast<uint16_t*>(out), kept, active, n_active, N, C, K,
-                     Ncols, relu, mch);
+  hipLaunchKernelGGL((ffn_tile_bf16<MTW, NJ, P>), dim3((unsigned)grid), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(W), static_cast<uint16_t*>(out), kept,
+                     active, n_active, N, C, K, Ncols, relu, mch);
   return hipGetLastError();
 }
 
@@ -241,10 +292,14 @@ bool tiled_ffn_applies(int C, int d, int dff) { return C > 64 && d % kTileN == 0
 
 hipError_t launch_tiled_gemm(const void* A, const void* W, void* out, const int32_t* kept, const int32_t* active,
                              const int32_t* n_active, int N, int C, int K, int Ncols, int relu, hipStream_t st) {
-  // 192-row tiles for 128 < C <= 192 (one m-chunk per expert: each weight
-  // panel is streamed once); 128-row tiles, two workgroups per CU, otherwise
-  if (C > 128 && C <= 192) return launch_tiled<6>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st);
-  return launch_tiled<4>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st);
+  // One m-chunk per expert where C allows (each weight panel is then streamed
+  // once): 160 x 128 tiles (two workgroups per CU) for 128 < C <= 160, 192 x 256
+  // tiles for 160 < C <= 192; 128 x 256 tiles, two workgroups per CU, otherwise.
+  if (C > 128 && C <= 160)
+    return launch_tiled<5, 4, SWM_TILE_P>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st);
+  if (C > 160 && C <= 192)
+    return launch_tiled<6, 8, SWM_TILE_P>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st);
+  return launch_tiled<4, 8, 2>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st);
 }
 
 }  // namespace swm
