@@ -4,21 +4,30 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 One step = one whole-layer forward (route -> capacity/slots -> dispatch ->
-expert FFN -> combine) over one batch of synthetic tokens already resident in
-HBM.  Prints one JSON line with:
+expert FFN -> combine, plus the shared dense expert where the workload has
+one) over one batch of synthetic tokens already resident in HBM.  Prints one
+JSON line with:
   value          tokens/s of the whole layer (T * K / wall time of K steps)
-  roofline       the expert-FFN GEMM kernel (2 launches per step, HBM-bound on
-                 the expert weights it touches): algorithmic bytes per launch /
-                 average launch time from HIP events on the launch stream
-  stages         per-stage time, HBM GB/s and % of peak (route, assign,
-                 dispatch, expert FFN, combine) and MFMA % for the expert FFN
-  cpu_baseline   the fp64 CPU oracle timed on the host on the same workload
+  roofline       the routed expert-FFN GEMM (2 launches per step, bound by the
+                 HBM bytes of the expert weights it touches): algorithmic bytes
+                 per launch / average launch time, the latter from HIP events
+                 that the library records around the routed FFN inside every
+                 timed step (switch_moe_forward_timed, on the launch stream);
+                 `traffic` = HBM bytes per launch from rocprofv3 FETCH_SIZE /
+                 WRITE_SIZE counters, kept below together with a fingerprint of
+                 the kernel sources they were taken on (null when the sources
+                 have changed since)
+  stages         per-stage time from the same stage events over extra steps:
+                 HBM GB/s and % of peak for route, dispatch, combine; TFLOP/s
+                 and % of the bf16 MFMA peak for the expert GEMMs
+  cpu_baseline   the fp64 CPU oracle timed on the host on the same batch
 Inputs are the seeded synthetic workload (x ~ N(0,1), Gaussian weights), no
 dataset.  Only one GPU is supported.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -27,6 +36,28 @@ import time
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA
 METRIC = "MoE-layer tokens/sec at 1 MI355X; expert-GEMM MFMA % and route/dispatch HBM % of peak"
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+# Sources of the expert-FFN GEMM kernels.  HBM traffic measured with rocprofv3
+# counters is reported only while these files are byte-identical to the ones
+# the counters were taken on.
+FFN_SOURCES = ("switch_top_routed_amd/csrc/expert_ffn.hip", "switch_top_routed_amd/csrc/expert_ffn_tiled.hip",
+               "switch_top_routed_amd/csrc/common.hpp", "switch_top_routed_amd/csrc/kernels.hpp")
+# FETCH_SIZE / WRITE_SIZE (KiB per dispatch, as rocprofv3 prints them) of the two
+# routed-FFN launches of one step, and the scale factors that a plain 1 GiB
+# device copy gives those counters (bytes moved / bytes counted).  Source:
+# profiles/*_hbm_traffic.md.
+TRAFFIC = {
+    "switch-base-uniform": {
+        "sources_sha256": "676637ce338e1f42dbbf52c8a15f68b9d96daf2f225772b5c0b3c071fbbf3b19",
+        "fetch_kib": [300203.0, 309293.0], "write_kib": [24108.0, 6027.0], "fetch_scale": 2.0, "write_scale": 1.0,
+    },
+    "switch-large-shared": {
+        "sources_sha256": "676637ce338e1f42dbbf52c8a15f68b9d96daf2f225772b5c0b3c071fbbf3b19",
+        "fetch_kib": [5720066.0, 6110001.0], "write_kib": [262144.0, 163840.0], "fetch_scale": 2.0,
+        "write_scale": 1.0,
+    },
+}
 
 
 def parse():
@@ -36,15 +67,29 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="switch-base-uniform")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--stage-iters", type=int, default=50)
+    ap.add_argument("--stage-steps", type=int, default=20, help="extra steps with every stage boundary timed")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="repeat oracle layer passes until this much CPU time has elapsed (at most 30 passes)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a device-to-device copy of BYTES bytes (5 times): the reference kernel whose "
                          "FETCH_SIZE / WRITE_SIZE counters scale the measured HBM traffic")
+    ap.add_argument("--sources-sha", action="store_true", help="print the fingerprint of the FFN kernel sources")
     return ap.parse_args()
+
+
+def sources_sha256():
+    h = hashlib.sha256()
+    for rel in FFN_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def main():
     args = parse()
+    if args.sources_sha:
+        print(sources_sha256())
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this layer is built and measured on one GPU; --gpus must be 1",
@@ -68,7 +113,8 @@ def main():
 
     wl = workloads.WORKLOADS[args.workload]
     dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
-    weight_bytes = 2 * wl.N * wl.d_model * wl.d_ff * (2 if wl.dtype == "bf16" else 4)
+    esz = 2 if wl.dtype == "bf16" else 4
+    weight_bytes = 2 * wl.N * wl.d_model * wl.d_ff * esz
     on_device = weight_bytes > (4 << 30)  # draw very large weight sets on the GPU
     inp = workloads.make_inputs(wl, weights=not on_device)
 
@@ -91,64 +137,41 @@ def main():
                          d_ff_shared=wl.d_ff_shared)
     stream = torch.cuda.current_stream()
 
-    def step():
-        layer(x, wg, w1, w2, bias=bias, ws1=ws1, ws2=ws2, stream=stream)
+    def step(ev=None):
+        layer(x, wg, w1, w2, bias=bias, ws1=ws1, ws2=ws2, stream=stream, stage_events=ev)
 
     for _ in range(args.warmup):
         step()
+    # one event set per timed step; only the routed-FFN boundaries are recorded there
+    ffn_ev = [sw.StageEvents(which=(3, 4)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step(ffn_ev[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed / args.steps * 1e3
     value = wl.T * args.steps / elapsed
+    ffn_stage_ms = [e.ms(3, 4) for e in ffn_ev]
 
-    # ---- per-stage timing through the per-stage entry points (HIP events on the launch stream)
-    C = layer.C
-    esz = 2 if wl.dtype == "bf16" else 4
-    r = sw.switch_route(x, wg, bias, stream=stream)
-    a = sw.switch_assign_capacity(r["expert_id"], r["gate"], wl.N, C, wl.priority, stream=stream)
-    xin = sw.switch_dispatch(x, a["token_of_slot"], a["kept_count"], wl.N, C, stream=stream)
-    xout = sw.switch_expert_ffn(xin, w1, w2, a["kept_count"], a["active"], a["n_active"], stream=stream)
+    # every stage boundary, over extra (untimed) steps
+    full_ev = [sw.StageEvents() for _ in range(args.stage_steps)]
+    for e in full_ev:
+        step(e)
     torch.cuda.synchronize()
-    kept = int(a["kept_count"].sum().item())
-    n_active = int(a["n_active"].item())
-    flags = sw.GATE_SCALE if wl.gate_scale else 0
+    names = ["route", "assign", "dispatch", "expert_ffn", "shared_ffn", "combine"]
+    st_s = {n: float(np.mean([e.ms(i, i + 1) for e in full_ev])) * 1e-3 for i, n in enumerate(names)}
 
-    def timed(fn, iters):
-        ev0 = torch.cuda.Event(enable_timing=True)
-        ev1 = torch.cuda.Event(enable_timing=True)
-        fn()
-        ev0.record(stream)
-        for _ in range(iters):
-            fn()
-        ev1.record(stream)
-        ev1.synchronize()
-        return ev0.elapsed_time(ev1) / iters * 1e-3  # seconds per call
-
-    it = args.stage_iters
-    rws = torch.empty(max(1, sw.lib().switch_route_workspace_bytes(wl.T, wl.d_model, wl.N, 1 if esz == 2 else 0)),
-                      dtype=torch.uint8, device="cuda")
-    t_route = timed(lambda: sw.switch_route(x, wg, bias, ws=rws, stream=stream), it)
-    t_assign = timed(lambda: sw.switch_assign_capacity(r["expert_id"], r["gate"], wl.N, C, wl.priority,
-                                                       stream=stream), it)
-    t_disp = timed(lambda: sw.switch_dispatch(x, a["token_of_slot"], a["kept_count"], wl.N, C, expert_in=xin,
-                                              stream=stream), it)
-    fws = torch.empty(sw.lib().switch_expert_ffn_workspace_bytes(wl.N, C, wl.d_model, wl.d_ff, 1 if esz == 2 else 0),
-                      dtype=torch.uint8, device="cuda")
-    t_ffn = timed(lambda: sw.switch_expert_ffn(xin, w1, w2, a["kept_count"], a["active"], a["n_active"],
-                                               expert_out=xout, ws=fws, stream=stream), it)
-    yb = torch.empty_like(x)
-    t_comb = timed(lambda: sw.switch_combine(xout, x, r["expert_id"], a["slot"], r["gate"], flags, y=yb,
-                                             stream=stream), it)
-
-    T, d, F, N = wl.T, wl.d_model, wl.d_ff, wl.N
+    out = layer.out
+    kept = int(out["kept_count"].sum().item())
+    n_active = int((out["kept_count"] > 0).sum().item())
+    T, d, F, N, C = wl.T, wl.d_model, wl.d_ff, wl.N, layer.C
     dropped = T - kept
     route_bytes = T * d * esz + N * d * esz + T * 8 + N * 16
     disp_bytes = 2 * kept * d * esz + 4 * kept
-    comb_bytes = (kept + T) * d * esz + dropped * 0 + T * d * esz + T * 12
+    # combine: one row read per token (expert output if kept, x if dropped), one row written,
+    # plus the shared-expert row when there is one, and expert id, slot and gate per token
+    comb_bytes = 2 * T * d * esz + (T * d * esz if wl.d_ff_shared else 0) + T * 12
     ffn_launch_bytes = n_active * d * F * esz + kept * (d + F) * esz  # one GEMM launch
     ffn_flops = 4.0 * kept * d * F
 
@@ -156,25 +179,39 @@ def main():
         return b / t / 1e9
 
     stages = {
-        "route": {"us": t_route * 1e6, "GB_s": gbs(route_bytes, t_route), "hbm_frac": gbs(route_bytes, t_route) / HBM_PEAK_GBS},
-        "assign": {"us": t_assign * 1e6},
-        "dispatch": {"us": t_disp * 1e6, "GB_s": gbs(disp_bytes, t_disp), "hbm_frac": gbs(disp_bytes, t_disp) / HBM_PEAK_GBS},
-        "expert_ffn": {"us": t_ffn * 1e6, "launches": 2, "GB_s": gbs(2 * ffn_launch_bytes, t_ffn),
-                       "hbm_frac": gbs(2 * ffn_launch_bytes, t_ffn) / HBM_PEAK_GBS,
-                       "TFLOP_s": ffn_flops / t_ffn / 1e12,
-                       "mfma_frac": ffn_flops / t_ffn / 1e12 / MFMA_BF16_PEAK_TFLOPS},
-        "combine": {"us": t_comb * 1e6, "GB_s": gbs(comb_bytes, t_comb), "hbm_frac": gbs(comb_bytes, t_comb) / HBM_PEAK_GBS},
-        "n_active": n_active, "kept": kept, "dropped": dropped,
+        "route": {"us": st_s["route"] * 1e6, "GB_s": gbs(route_bytes, st_s["route"]),
+                  "hbm_frac": gbs(route_bytes, st_s["route"]) / HBM_PEAK_GBS},
+        "assign": {"us": st_s["assign"] * 1e6},
+        "dispatch": {"us": st_s["dispatch"] * 1e6, "GB_s": gbs(disp_bytes, st_s["dispatch"]),
+                     "hbm_frac": gbs(disp_bytes, st_s["dispatch"]) / HBM_PEAK_GBS},
+        "expert_ffn": {"us": st_s["expert_ffn"] * 1e6, "launches": 2,
+                       "GB_s": gbs(2 * ffn_launch_bytes, st_s["expert_ffn"]),
+                       "hbm_frac": gbs(2 * ffn_launch_bytes, st_s["expert_ffn"]) / HBM_PEAK_GBS,
+                       "TFLOP_s": ffn_flops / st_s["expert_ffn"] / 1e12,
+                       "mfma_frac": ffn_flops / st_s["expert_ffn"] / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+        "combine": {"us": st_s["combine"] * 1e6, "GB_s": gbs(comb_bytes, st_s["combine"]),
+                    "hbm_frac": gbs(comb_bytes, st_s["combine"]) / HBM_PEAK_GBS},
+        "n_active": n_active, "kept": kept, "dropped": dropped, "stage_steps": args.stage_steps,
     }
-    launch_s = t_ffn / 2
+    if wl.d_ff_shared:
+        Fs = wl.d_ff_shared
+        sh_flops = 4.0 * T * d * Fs
+        stages["shared_ffn"] = {"us": st_s["shared_ffn"] * 1e6, "launches": 2,
+                                "TFLOP_s": sh_flops / st_s["shared_ffn"] / 1e12,
+                                "mfma_frac": sh_flops / st_s["shared_ffn"] / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+
+    launch_s = float(np.mean(ffn_stage_ms)) * 1e-3 / 2
     achieved = gbs(ffn_launch_bytes, launch_s)
-    roofline = {"bound": "hbm", "kernel": "ffn_gemm_bf16 (expert FFN GEMM, 2 launches per step)",
-                "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                "traffic": None, "bytes_per_launch": ffn_launch_bytes, "launch_us": launch_s * 1e6}
+    kernel = "ffn_tile_bf16" if C > 64 and d % 256 == 0 and F % 256 == 0 else "ffn_gemm_bf16"
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_bytes(wl.name),
+                "kernel": f"{kernel} (routed expert FFN GEMM, 2 launches per step)",
+                "bytes_per_launch": ffn_launch_bytes, "launch_us": launch_s * 1e6,
+                "launch_timing": f"HIP events around the routed FFN in each of the {args.steps} timed steps"}
 
     cpu = None
     if not args.no_cpu_baseline and not on_device:
-        cpu = cpu_baseline(inp)
+        cpu = cpu_baseline(inp, args.cpu_seconds)
 
     line = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -188,19 +225,36 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(inp):
-    """The fp64 oracle, as it stands, on the same workload (one full layer pass)."""
+def traffic_bytes(workload):
+    """HBM bytes per routed-FFN launch from the stored counter readings, or None
+    if there are none for this workload or the kernel sources have changed."""
+    t = TRAFFIC.get(workload)
+    if t is None or t["sources_sha256"] != sources_sha256():
+        return None
+    per = [f * 1024 * t["fetch_scale"] + w * 1024 * t["write_scale"] for f, w in zip(t["fetch_kib"], t["write_kib"])]
+    return sum(per) / len(per)
+
+
+def cpu_baseline(inp, seconds):
+    """The fp64 oracle, as it stands, on the same workload: whole layer passes
+    over the batch, repeated until `seconds` have elapsed (at most 30 passes)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
+    passes = 0
     t0 = time.perf_counter()
-    oracle.moe_forward_stored(inp)
-    el = time.perf_counter() - t0
-    return {"value": inp.wl.T / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "seconds": el, "sample": f"one full fp64 layer pass over the {inp.wl.name} batch (T={inp.wl.T})"}
+    while True:
+        oracle.moe_forward_stored(inp)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or passes >= 30:
+            break
+    return {"value": inp.wl.T * passes / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "seconds": el, "sample": f"{passes} full fp64 layer passes over the {inp.wl.name} batch "
+                                     f"(T={inp.wl.T} tokens each)"}
 
 
 if __name__ == "__main__":

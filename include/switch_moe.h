@@ -212,6 +212,20 @@ size_t switch_moe_workspace_bytes(const switch_moe_desc* desc);
 switch_status switch_moe_forward(const switch_moe_desc* desc, const switch_moe_inputs* in,
                                  const switch_moe_outputs* out, void* ws, size_t ws_bytes, void* stream);
 
+/* switch_moe_forward with its stage boundaries recorded on `stream`, for
+   timing the stages of the very launches a caller measures.  stage_events
+   holds 7 hipEvent_t handles created by the caller (entries may be NULL and
+   are then skipped; the array itself may not be NULL -> SWITCH_E_NULL):
+     [0] before the route, [1] before the capacity/slot assignment,
+     [2] before the dispatch, [3] before the routed expert FFN (two GEMM
+     launches), [4] after it (before the shared dense expert, if any),
+     [5] before the combine, [6] after the combine.
+   Outputs, workspace, validation and errors are those of switch_moe_forward;
+   a failed event record returns SWITCH_E_HIP. */
+switch_status switch_moe_forward_timed(const switch_moe_desc* desc, const switch_moe_inputs* in,
+                                       const switch_moe_outputs* out, void* ws, size_t ws_bytes, void* stream,
+                                       void* const* stage_events);
+
 /* Static description of a status code. */
 const char* switch_status_str(switch_status s);
 /* Thread-local message of the last error on this thread ("" if none). */

@@ -351,8 +351,12 @@ size_t switch_moe_workspace_bytes(const switch_moe_desc* desc) {
   return fwd_layout(*desc, C).bytes;
 }
 
-switch_status switch_moe_forward(const switch_moe_desc* desc, const switch_moe_inputs* in,
-                                 const switch_moe_outputs* out, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+// The whole layer; `ev` (7 events or NULL) marks the stage boundaries on the stream.
+static switch_status moe_forward(const switch_moe_desc* desc, const switch_moe_inputs* in,
+                                 const switch_moe_outputs* out, void* ws, size_t ws_bytes, void* stream,
+                                 void* const* ev) {
   int32_t C = 0;
   TRY(validate_desc(desc, &C));
   if (in == nullptr) return fail(SWITCH_E_NULL, "inputs is NULL");
@@ -384,18 +388,27 @@ switch_status switch_moe_forward(const switch_moe_desc* desc, const switch_moe_i
   int32_t* nact = reinterpret_cast<int32_t*>(w + L.off_nact);
   void* xin = w + L.off_xin;
   void* xout = w + L.off_xout;
+  auto mark = [&](int i) -> hipError_t {
+    return (ev != nullptr && ev[i] != nullptr) ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), st) : hipSuccess;
+  };
 
-  hipError_t e = launch_route(L.route, in->x, in->w_gate, in->bias, d.T, d.d_model, d.N, d.dtype, out->expert_id,
+  hipError_t e = mark(0);
+  if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
+  e = launch_route(L.route, in->x, in->w_gate, in->bias, d.T, d.d_model, d.N, d.dtype, out->expert_id,
                               out->gate, out->routed_count, out->f, out->P, out->l_aux, w + L.off_route, st);
   if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/route");
+  if ((e = mark(1)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
   e = launch_assign(L.assign, out->expert_id, out->gate, d.T, d.N, C, d.priority, out->slot, tos, out->kept_count,
                     out->n_dropped, active, nact, w + L.off_assign, st);
   if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/assign");
+  if ((e = mark(2)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
   e = launch_dispatch(in->x, d.dtype, d.T, d.d_model, tos, out->kept_count, d.N, C, xin, st);
   if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/dispatch");
+  if ((e = mark(3)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
   e = launch_ffn(L.ffn, xin, in->w1, in->w2, d.dtype, d.N, C, d.d_model, d.d_ff, out->kept_count, active, nact, xout,
                  w + L.off_ffn, st);
   if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/expert_ffn");
+  if ((e = mark(4)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
   void* sout = nullptr;
   if (d.d_ff_shared > 0) {
     int32_t* dk = reinterpret_cast<int32_t*>(w + L.off_dense);
@@ -406,10 +419,26 @@ switch_status switch_moe_forward(const switch_moe_desc* desc, const switch_moe_i
                    dk + 2, sout, w + L.off_sffn, st);
     if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/shared_ffn");
   }
+  if ((e = mark(5)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
   e = launch_combine(xout, in->x, sout, d.dtype, d.T, d.d_model, out->expert_id, out->slot, out->gate, d.N, C,
                      d.flags, out->y, st);
   if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/combine");
+  if ((e = mark(6)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
   return ok();
+}
+
+extern "C" {
+
+switch_status switch_moe_forward(const switch_moe_desc* desc, const switch_moe_inputs* in,
+                                 const switch_moe_outputs* out, void* ws, size_t ws_bytes, void* stream) {
+  return moe_forward(desc, in, out, ws, ws_bytes, stream, nullptr);
+}
+
+switch_status switch_moe_forward_timed(const switch_moe_desc* desc, const switch_moe_inputs* in,
+                                       const switch_moe_outputs* out, void* ws, size_t ws_bytes, void* stream,
+                                       void* const* stage_events) {
+  if (stage_events == nullptr) return fail(SWITCH_E_NULL, "stage_events is NULL");
+  return moe_forward(desc, in, out, ws, ws_bytes, stream, stage_events);
 }
 
 const char* switch_status_str(switch_status s) {

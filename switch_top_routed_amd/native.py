@@ -57,6 +57,8 @@ _SIGS = {
     "switch_moe_workspace_bytes": (_sz, [ctypes.POINTER(SwitchMoeDesc)]),
     "switch_moe_forward": (_i32, [ctypes.POINTER(SwitchMoeDesc), ctypes.POINTER(SwitchMoeInputs),
                                   ctypes.POINTER(SwitchMoeOutputs), _vp, _sz, _vp]),
+    "switch_moe_forward_timed": (_i32, [ctypes.POINTER(SwitchMoeDesc), ctypes.POINTER(SwitchMoeInputs),
+                                        ctypes.POINTER(SwitchMoeOutputs), _vp, _sz, _vp, ctypes.POINTER(_vp)]),
     "switch_status_str": (ctypes.c_char_p, [_i32]),
     "switch_last_error": (ctypes.c_char_p, []),
 }
@@ -215,6 +217,60 @@ def switch_combine(expert_out, x, expert_id, slot, gate, flags=GATE_SCALE, *, sh
     return y
 
 
+_hip = None
+
+
+def _hip_runtime():
+    """The HIP runtime library (for event handles: create, elapsed time, destroy)."""
+    global _hip
+    if _hip is None:
+        _hip = ctypes.CDLL("libamdhip64.so")
+        _hip.hipEventCreate.argtypes = [ctypes.POINTER(_vp)]
+        _hip.hipEventCreate.restype = ctypes.c_int
+        _hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), _vp, _vp]
+        _hip.hipEventElapsedTime.restype = ctypes.c_int
+        _hip.hipEventSynchronize.argtypes = [_vp]
+        _hip.hipEventSynchronize.restype = ctypes.c_int
+        _hip.hipEventDestroy.argtypes = [_vp]
+        _hip.hipEventDestroy.restype = ctypes.c_int
+    return _hip
+
+
+class StageEvents:
+    """Seven HIP events for switch_moe_forward_timed: [0] before route, [1] assign, [2] dispatch,
+    [3] routed expert FFN, [4] after it, [5] combine, [6] after combine."""
+
+    N = 7
+
+    def __init__(self, which=None):
+        """which: indices of the events to create (default all); the others stay NULL and are not recorded."""
+        h = _hip_runtime()
+        self.handles = (_vp * self.N)()
+        for i in range(self.N) if which is None else which:
+            ev = _vp()
+            rc = h.hipEventCreate(ctypes.byref(ev))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed ({rc})")
+            self.handles[i] = ev
+
+    def ms(self, i, j):
+        """Milliseconds from event i to event j (both recorded and complete)."""
+        h = _hip_runtime()
+        if h.hipEventSynchronize(self.handles[j]) != 0:
+            raise RuntimeError("hipEventSynchronize failed")
+        out = ctypes.c_float()
+        rc = h.hipEventElapsedTime(ctypes.byref(out), self.handles[i], self.handles[j])
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return out.value
+
+    def __del__(self):
+        if _hip is not None:
+            for i in range(self.N):
+                if self.handles[i]:
+                    _hip.hipEventDestroy(self.handles[i])
+
+
 class SwitchMoE:
     """The whole layer with its outputs and workspace preallocated (one call = switch_moe_forward)."""
 
@@ -242,13 +298,21 @@ class SwitchMoE:
                                         ("y", "expert_id", "gate", "slot", "routed_count", "kept_count",
                                          "n_dropped", "f", "P", "l_aux")])
 
-    def __call__(self, x, w_gate, w1, w2, bias=None, ws1=None, ws2=None, stream=None):
+    def __call__(self, x, w_gate, w1, w2, bias=None, ws1=None, ws2=None, stream=None, stage_events=None):
+        """One layer forward.  stage_events: optional StageEvents (7 HIP events) recorded at the stage
+        boundaries (switch_moe_forward_timed)."""
         ins = SwitchMoeInputs(x.data_ptr(), w_gate.data_ptr(), None if bias is None else bias.data_ptr(),
                               w1.data_ptr(), w2.data_ptr(), None if ws1 is None else ws1.data_ptr(),
                               None if ws2 is None else ws2.data_ptr())
-        _check("switch_moe_forward", lib().switch_moe_forward(ctypes.byref(self.desc), ctypes.byref(ins),
-                                                              ctypes.byref(self._outs), _p(self.ws),
-                                                              self.ws.numel(), _stream(stream)))
+        if stage_events is None:
+            _check("switch_moe_forward", lib().switch_moe_forward(ctypes.byref(self.desc), ctypes.byref(ins),
+                                                                  ctypes.byref(self._outs), _p(self.ws),
+                                                                  self.ws.numel(), _stream(stream)))
+        else:
+            _check("switch_moe_forward_timed",
+                   lib().switch_moe_forward_timed(ctypes.byref(self.desc), ctypes.byref(ins), ctypes.byref(self._outs),
+                                                  _p(self.ws), self.ws.numel(), _stream(stream),
+                                                  stage_events.handles))
         return self.out
 
 

@@ -117,3 +117,13 @@ def test_forward_validation(L):
     d.d_ff_shared = 0
     d.capacity_factor = 0.0
     assert fwd(ctypes.byref(d), ctypes.byref(ins), ctypes.byref(outs), FAKE, 1 << 30, None) == E_SHAPE
+
+
+def test_timed_forward_validation(L):
+    d = native.SwitchMoeDesc(T=64, d_model=128, d_ff=256, N=8, C=0, capacity_factor=1.0, dtype=1,
+                             priority=0, flags=1, d_ff_shared=0)
+    assert L.switch_moe_forward_timed(ctypes.byref(d), None, None, FAKE, 1 << 30, None, None) == E_NULL
+    assert b"stage_events" in L.switch_last_error()
+    ev = (ctypes.c_void_p * 7)()
+    assert L.switch_moe_forward_timed(ctypes.byref(d), None, None, FAKE, 1 << 30, None, ev) == E_NULL
+    assert b"inputs is NULL" in L.switch_last_error()

@@ -206,6 +206,22 @@ def test_base_layer_deterministic_and_poison_proof(base):
         np.testing.assert_array_equal(host_bits(v), a[k], err_msg=k)
 
 
+def test_base_layer_timed_matches_untimed(base):
+    """switch_moe_forward_timed: same outputs bit for bit, stage events in order."""
+    wl, inp, d, ref = base
+    _say("base layer with stage events")
+    layer, o1 = run_layer(wl, d)
+    a = {k: host_bits(v).copy() for k, v in o1.items()}
+    ev = native.StageEvents()
+    layer(d["x"], d["w_gate"], d["w1"], d["w2"], bias=d["bias"], stage_events=ev)
+    torch.cuda.synchronize()
+    for k, v in layer.out.items():
+        np.testing.assert_array_equal(host_bits(v), a[k], err_msg=k)
+    spans = [ev.ms(i, i + 1) for i in range(ev.N - 1)]
+    assert all(s >= 0.0 for s in spans), spans
+    assert ev.ms(3, 4) > 0.0  # the routed expert FFN takes time
+
+
 # ---------------------------------------------------------------------------
 # skewed routing: capacity factor x priority x gate scaling
 # ---------------------------------------------------------------------------
