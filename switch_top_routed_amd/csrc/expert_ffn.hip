@@ -98,22 +98,19 @@ __device__ __forceinline__ u32x4 pack8(const float (&v)[8], bool relu) {
 
 
 // Waves of one workgroup that share a work item along K (1, 2 or 4), the same
-// in every workgroup of a launch.  Work is dealt out in rounds of one wave task
-// per wave slot, so the choice maximises the busy fraction of the slots
-// base * KW / (rounds * slots); ties go to the smaller KW (fewer LDS
-// reductions).  Every wave keeps at least 4 k-steps.
+// in every workgroup of a launch: the smallest KW that gives every wave slot
+// of the grid at least one task, else the largest allowed (every wave keeps at
+// least 4 k-steps).  A K split costs an LDS reduction and a barrier per item;
+// measured on the 128-expert base layer, a partly filled second round of whole
+// items beats more rounds of split items (GEMM 1: 119 us with KW = 1 against
+// 135 us with KW = 2), while leaving a quarter of the slots idle does not (GEMM
+// 2: 159 us with KW = 1 against 137 us with KW = 2).
 __device__ __forceinline__ int waves_per_item(int64_t base, int64_t wave_slots, int waves, int ksteps) {
   int best = 1;
-  double best_util = 0.0;
   for (int kw = 1; kw <= waves; kw *= 2) {
     if (kw > 1 && ksteps < kw * 4) break;
-    const int64_t tasks = base * kw;
-    const int64_t rounds = (tasks + wave_slots - 1) / wave_slots;
-    const double util = (double)tasks / (double)(rounds * wave_slots);
-    if (util > best_util + 0.02) {
-      best_util = util;
-      best = kw;
-    }
+    best = kw;
+    if (base * kw >= wave_slots) break;
   }
   return best;
 }
@@ -154,19 +151,16 @@ __device__ __forceinline__ void store_row<8>(uint16_t* p, const float (&v)[8], b
 }
 
 template <int MT, int WAVES, int STAGES, int J>
-__global__ __launch_bounds__(WAVES * 64, SWM_FFN_MINB) void ffn_gemm_bf16(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, uint16_t* __restrict__ out,
-    const int32_t* __restrict__ kept_count, const int32_t* __restrict__ active, const int32_t* __restrict__ n_active,
-    int N, int C, int K, int Ncols, int relu, int mch) {
-  __shared__ float red[WAVES * 4 * J * 64];
+__device__ __forceinline__ void ffn_stream(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
+                                           uint16_t* __restrict__ out, const int32_t* __restrict__ kept_count,
+                                           const int32_t* __restrict__ active, int n_act, int N, int C, int K,
+                                           int Ncols, int relu, int mch, float* red) {
   constexpr int COLS = 16 * J;  // output columns per item
   const int tid = threadIdx.x, lane = tid & 63, c = lane & 15, kg = lane >> 4;
   // wave index as a wave-uniform (scalar) value: everything derived from it -- item,
   // expert, buffer descriptors, row offsets -- then lives in SGPRs
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int NCB = Ncols / COLS;
-  int n_act = n_active[0];
-  if (n_act > N) n_act = N;
   const int ksteps = K >> 5;
   const int64_t base = (int64_t)n_act * NCB * mch;
   if (base <= 0) return;
@@ -320,6 +314,30 @@ __global__ __launch_bounds__(WAVES * 64, SWM_FFN_MINB) void ffn_gemm_bf16(
   }
 }
 
+// 128-column work items (16-byte weight loads, J = 8) unless, even at the
+// largest K split, they would give fewer than 2/5 of the grid's wave slots a
+// task; then 64-column items (twice as many).  The threshold sits between
+// measured launches: 128-column items won on GEMM 2 of the base layer (150
+// tasks per 100 slots: 127 us against 140 us) and on both GEMMs of the
+// 384-expert decode layer with 14 experts active (44 and 88 per 100 slots: 47
+// against 48-50 us), and lost on GEMM 2 of the skewed layer with 17 experts
+// active (20 per 100 slots: 22.4 against 18.9 us).  The choice needs n_active,
+// so it is taken on the device; JMAX = 4 compiles the 64-column path only.
+template <int MT, int WAVES, int STAGES, int JMAX>
+__global__ __launch_bounds__(WAVES * 64, SWM_FFN_MINB) void ffn_gemm_bf16(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, uint16_t* __restrict__ out,
+    const int32_t* __restrict__ kept_count, const int32_t* __restrict__ active, const int32_t* __restrict__ n_active,
+    int N, int C, int K, int Ncols, int relu, int mch) {
+  __shared__ float red[WAVES * 4 * JMAX * 64];
+  int n_act = n_active[0];
+  if (n_act > N) n_act = N;
+  if (JMAX == 8 && Ncols % 128 == 0 &&
+      (int64_t)n_act * (Ncols / 128) * mch * WAVES * 5 >= (int64_t)gridDim.x * WAVES * 2)
+    ffn_stream<MT, WAVES, STAGES, JMAX>(A, W, out, kept_count, active, n_act, N, C, K, Ncols, relu, mch, red);
+  else
+    ffn_stream<MT, WAVES, STAGES, 4>(A, W, out, kept_count, active, n_act, N, C, K, Ncols, relu, mch, red);
+}
+
 __global__ __launch_bounds__(256) void ffn_gemm_f32(const float* __restrict__ A, const float* __restrict__ W,
                                                     float* __restrict__ out, const int32_t* __restrict__ kept_count,
                                                     const int32_t* __restrict__ active,
@@ -415,14 +433,16 @@ static hipError_t launch_gemm(const void* A, const void* W, void* out, const int
   return hipGetLastError();
 }
 
-// 128-column waves (16-byte weight loads) for wide outputs; 64-column waves when
-// the output is narrow, which doubles the work items of few-expert launches
+// 128-column items are possible up to 3 row tiles (4 x 8 accumulator tiles
+// would spill); the kernel picks 128- or 64-column items per launch
 template <int MT>
 static hipError_t launch_gemm_cols(const void* A, const void* W, void* out, const int32_t* kept,
                                    const int32_t* active, const int32_t* n_active, int N, int C, int K, int Ncols,
                                    int relu, int mch, hipStream_t st) {
-  if (kAllow128 && MT <= 3 && Ncols >= 2048 && Ncols % 128 == 0)  // 4 tiles x 128 columns would spill
-    return launch_gemm<MT, 8>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, mch, st);
+  if constexpr (kAllow128 && MT <= 3) {
+    if (Ncols % 128 == 0)
+      return launch_gemm<MT, 8>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, mch, st);
+  }
   return launch_gemm<MT, 4>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, mch, st);
 }
 
