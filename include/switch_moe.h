@@ -37,7 +37,9 @@
  *     crosses the ABI.
  *   - Shape rules: T >= 1; 1 <= N <= 1024; 1 <= C <= T; pointers 16-byte
  *     aligned.  bf16: d_model and d_ff multiples of 128.  f32: d_model a
- *     multiple of 4.
+ *     multiple of 4.  d_model <= 2^20 and d_model * d_ff <= 2^30 (one
+ *     expert's weight matrix stays under 2 GiB in bf16: the kernels address
+ *     it through 32-bit buffer offsets).
  *   - Determinism: identical inputs give bitwise identical outputs (no
  *     floating-point atomics; every reduction has a fixed order).
  */

@@ -36,6 +36,10 @@ switch_status hip_fail(hipError_t e, const char* where) {
 
 constexpr int kMaxExperts = 1024;
 constexpr int64_t kMaxTokens = (int64_t)1 << 30;
+// 32-bit buffer offsets: a row of d_model elements times N <= 1024 experts
+// (router) and one expert's d_model x d_ff weight matrix stay below 2^31 bytes
+constexpr int32_t kMaxRow = 1 << 20;
+constexpr int64_t kMaxWeight = (int64_t)1 << 30;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -88,6 +92,7 @@ switch_status validate_route(const void* x, const void* w_gate, const float* bia
   TRY(check_dtype(dtype));
   TRY(check_tn(T, N));
   if (d < 1) return fail(SWITCH_E_SHAPE, "d_model=%d must be >= 1", d);
+  if (d > kMaxRow) return fail(SWITCH_E_SHAPE, "d_model=%d exceeds 2^20", d);
   if (dtype == SWITCH_BF16 && d % 32 != 0) return fail(SWITCH_E_SHAPE, "d_model=%d must be a multiple of 32 for bf16 routing", d);
   REQUIRE_PTR(x);
   REQUIRE_PTR(w_gate);
@@ -152,6 +157,9 @@ switch_status validate_ffn(const void* expert_in, const void* w1, const void* w2
   if (C < 1 || C > kMaxTokens) return fail(SWITCH_E_SHAPE, "C=%d must be >= 1", C);
   TRY(check_rows(d, dtype, "d_model"));
   TRY(check_rows(dff, dtype, "d_ff"));
+  if (d > kMaxRow) return fail(SWITCH_E_SHAPE, "d_model=%d exceeds 2^20", d);
+  if ((int64_t)d * dff > kMaxWeight)
+    return fail(SWITCH_E_SHAPE, "d_model * d_ff = %lld exceeds 2^30", (long long)d * dff);
   REQUIRE_PTR(expert_in);
   REQUIRE_PTR(w1);
   REQUIRE_PTR(w2);
@@ -193,25 +201,40 @@ switch_status validate_combine(const void* expert_out, const void* x, const void
 // ---------------------------------------------------------------------------
 struct FwdLayout {
   int32_t C;
+  bool fused;  // token order: slots from the router's tiles, dispatch folded into GEMM 1
   RoutePlan route;
   AssignPlan assign;
   FfnPlan ffn, sffn;
-  size_t off_route, off_assign, off_tos, off_active, off_nact, off_xin, off_xout, off_ffn;
+  size_t off_route, off_assign, off_rank, off_toff, off_tos, off_active, off_nact, off_xin, off_xout, off_ffn;
   size_t off_dense, off_sffn, off_sout, bytes;
 };
+
+// The fused path needs token order, the token matrix addressable through
+// 32-bit buffer offsets (GEMM 1 gathers its rows), and few enough router tiles
+// for the single-workgroup prefix.
+constexpr int64_t kFusedMaxTiles = 16384;
 
 FwdLayout fwd_layout(const switch_moe_desc& d, int32_t C) {
   FwdLayout L{};
   L.C = C;
   const size_t esz = d.dtype == SWITCH_BF16 ? 2 : 4;
   L.route = route_plan(d.T, d.d_model, d.N, d.dtype);
-  L.assign = assign_plan(d.T, d.N, C, d.priority);
+  L.fused = d.priority == SWITCH_TOKEN_ORDER && (int64_t)d.T * d.d_model * (int64_t)esz < ((int64_t)1 << 31) &&
+            L.route.nblk <= kFusedMaxTiles;
   L.ffn = ffn_plan(d.N, C, d.d_model, d.d_ff, d.dtype);
   size_t off = 0;
   L.off_route = off;
   off = align_up(off + L.route.bytes);
-  L.off_assign = off;
-  off = align_up(off + L.assign.bytes);
+  if (L.fused) {
+    L.off_rank = off;
+    off = align_up(off + (size_t)d.T * 4);
+    L.off_toff = off;
+    off = align_up(off + (size_t)L.route.nblk * d.N * 4);
+  } else {
+    L.assign = assign_plan(d.T, d.N, C, d.priority);
+    L.off_assign = off;
+    off = align_up(off + L.assign.bytes);
+  }
   L.off_tos = off;
   off = align_up(off + (size_t)d.N * C * 4);
   L.off_active = off;
@@ -219,7 +242,7 @@ FwdLayout fwd_layout(const switch_moe_desc& d, int32_t C) {
   L.off_nact = off;
   off = align_up(off + 4);
   L.off_xin = off;
-  off = align_up(off + (size_t)d.N * C * d.d_model * esz);
+  if (!L.fused) off = align_up(off + (size_t)d.N * C * d.d_model * esz);
   L.off_xout = off;
   off = align_up(off + (size_t)d.N * C * d.d_model * esz);
   L.off_ffn = off;
@@ -245,6 +268,9 @@ switch_status validate_desc(const switch_moe_desc* d, int32_t* C) {
   TRY(check_rows(d->d_ff, d->dtype, "d_ff"));
   if (d->d_ff_shared < 0) return fail(SWITCH_E_SHAPE, "d_ff_shared=%d must be >= 0", d->d_ff_shared);
   if (d->d_ff_shared > 0) TRY(check_rows(d->d_ff_shared, d->dtype, "d_ff_shared"));
+  if (d->d_model > kMaxRow) return fail(SWITCH_E_SHAPE, "d_model=%d exceeds 2^20", d->d_model);
+  if ((int64_t)d->d_model * d->d_ff > kMaxWeight || (int64_t)d->d_model * d->d_ff_shared > kMaxWeight)
+    return fail(SWITCH_E_SHAPE, "d_model * d_ff (or d_ff_shared) exceeds 2^30");
   if (d->priority != SWITCH_TOKEN_ORDER && d->priority != SWITCH_GATE_DESC)
     return fail(SWITCH_E_UNSUPPORTED, "priority %d is not supported", d->priority);
   if (d->flags & ~(SWITCH_GATE_SCALE | SWITCH_RESIDUAL_ALL))
@@ -394,19 +420,34 @@ static switch_status moe_forward(const switch_moe_desc* desc, const switch_moe_i
 
   hipError_t e = mark(0);
   if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
-  e = launch_route(L.route, in->x, in->w_gate, in->bias, d.T, d.d_model, d.N, d.dtype, out->expert_id,
-                              out->gate, out->routed_count, out->f, out->P, out->l_aux, w + L.off_route, st);
+  int32_t* rank = L.fused ? reinterpret_cast<int32_t*>(w + L.off_rank) : nullptr;
+  e = launch_route(L.route, in->x, in->w_gate, in->bias, d.T, d.d_model, d.N, d.dtype, out->expert_id, out->gate,
+                   out->routed_count, out->f, out->P, out->l_aux, w + L.off_route, st, rank);
   if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/route");
   if ((e = mark(1)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
-  e = launch_assign(L.assign, out->expert_id, out->gate, d.T, d.N, C, d.priority, out->slot, tos, out->kept_count,
-                    out->n_dropped, active, nact, w + L.off_assign, st);
-  if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/assign");
-  if ((e = mark(2)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
-  e = launch_dispatch(in->x, d.dtype, d.T, d.d_model, tos, out->kept_count, d.N, C, xin, st);
-  if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/dispatch");
-  if ((e = mark(3)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
-  e = launch_ffn(L.ffn, xin, in->w1, in->w2, d.dtype, d.N, C, d.d_model, d.d_ff, out->kept_count, active, nact, xout,
-                 w + L.off_ffn, st);
+  if (L.fused) {
+    // token order: one kernel turns the router's tiles into slots (and the
+    // statistics); GEMM 1 then reads each slot's token row straight from x
+    e = launch_route_assign_token(L.route, d.T, d.N, C, out->expert_id, rank,
+                                  reinterpret_cast<int32_t*>(w + L.off_toff), out->routed_count, out->f, out->P,
+                                  out->l_aux, out->slot, tos, out->kept_count, out->n_dropped, active, nact,
+                                  w + L.off_route, st);
+    if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/assign");
+    if ((e = mark(2)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
+    if ((e = mark(3)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
+    e = launch_ffn(L.ffn, in->x, in->w1, in->w2, d.dtype, d.N, C, d.d_model, d.d_ff, out->kept_count, active, nact,
+                   xout, w + L.off_ffn, st, tos, d.T);
+  } else {
+    e = launch_assign(L.assign, out->expert_id, out->gate, d.T, d.N, C, d.priority, out->slot, tos, out->kept_count,
+                      out->n_dropped, active, nact, w + L.off_assign, st);
+    if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/assign");
+    if ((e = mark(2)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
+    e = launch_dispatch(in->x, d.dtype, d.T, d.d_model, tos, out->kept_count, d.N, C, xin, st);
+    if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/dispatch");
+    if ((e = mark(3)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
+    e = launch_ffn(L.ffn, xin, in->w1, in->w2, d.dtype, d.N, C, d.d_model, d.d_ff, out->kept_count, active, nact,
+                   xout, w + L.off_ffn, st);
+  }
   if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/expert_ffn");
   if ((e = mark(4)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
   void* sout = nullptr;

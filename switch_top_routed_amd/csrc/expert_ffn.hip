@@ -154,7 +154,8 @@ template <int MT, int WAVES, int STAGES, int J>
 __device__ __forceinline__ void ffn_stream(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
                                            uint16_t* __restrict__ out, const int32_t* __restrict__ kept_count,
                                            const int32_t* __restrict__ active, int n_act, int N, int C, int K,
-                                           int Ncols, int relu, int mch, float* red) {
+                                           int Ncols, int relu, int mch, float* red,
+                                           const int32_t* __restrict__ gather, int64_t a_rows) {
   constexpr int COLS = 16 * J;  // output columns per item
   const int tid = threadIdx.x, lane = tid & 63, c = lane & 15, kg = lane >> 4;
   // wave index as a wave-uniform (scalar) value: everything derived from it -- item,
@@ -209,7 +210,11 @@ __device__ __forceinline__ void ffn_stream(const uint16_t* __restrict__ A, const
       // offsets are wave-uniform SGPR values.  A rows at or beyond `rows` get a lane
       // offset past the descriptor's extent, so they read as zeros.
       const __amdgpu_buffer_rsrc_t wres = make_rsrc(W + (int64_t)e * K * Ncols, (int64_t)K * Ncols * 2);
-      const __amdgpu_buffer_rsrc_t ares = make_rsrc(A + ((int64_t)e * C + m0) * K, (int64_t)rows * K * 2);
+      // gather != NULL: A is the token matrix [a_rows, K] and row r of the
+      // expert's buffer is token gather[e * C + r] (the dispatch folded in)
+      const __amdgpu_buffer_rsrc_t ares =
+          gather != nullptr ? make_rsrc(A, a_rows * K * 2)
+                            : make_rsrc(A + ((int64_t)e * C + m0) * K, (int64_t)rows * K * 2);
       const int w_voff = ((kw * 32 + kg * 8) * Ncols + cb * COLS + c * J) * 2;
       const int w_row = Ncols * 2;
       const int w_step = KW * 32 * Ncols * 2;
@@ -217,7 +222,8 @@ __device__ __forceinline__ void ffn_stream(const uint16_t* __restrict__ A, const
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int rr = mt * 16 + c;
-        a_voff[mt] = rr < rows ? (rr * K + kw * 32 + kg * 8) * 2 : kOutOfRange;
+        const int64_t src = gather != nullptr && rr < rows ? gather[(int64_t)e * C + m0 + rr] : rr;
+        a_voff[mt] = rr < rows ? (int)((src * K + kw * 32 + kg * 8) * 2) : kOutOfRange;
       }
       const int a_step = KW * 32 * 2;
 
@@ -327,29 +333,32 @@ template <int MT, int WAVES, int STAGES, int JMAX>
 __global__ __launch_bounds__(WAVES * 64, SWM_FFN_MINB) void ffn_gemm_bf16(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, uint16_t* __restrict__ out,
     const int32_t* __restrict__ kept_count, const int32_t* __restrict__ active, const int32_t* __restrict__ n_active,
-    int N, int C, int K, int Ncols, int relu, int mch) {
+    int N, int C, int K, int Ncols, int relu, int mch, const int32_t* __restrict__ gather, int64_t a_rows) {
   __shared__ float red[WAVES * 4 * JMAX * 64];
   int n_act = n_active[0];
   if (n_act > N) n_act = N;
   if (JMAX == 8 && Ncols % 128 == 0 &&
       (int64_t)n_act * (Ncols / 128) * mch * WAVES * 5 >= (int64_t)gridDim.x * WAVES * 2)
-    ffn_stream<MT, WAVES, STAGES, JMAX>(A, W, out, kept_count, active, n_act, N, C, K, Ncols, relu, mch, red);
+    ffn_stream<MT, WAVES, STAGES, JMAX>(A, W, out, kept_count, active, n_act, N, C, K, Ncols, relu, mch, red, gather,
+                                        a_rows);
   else
-    ffn_stream<MT, WAVES, STAGES, 4>(A, W, out, kept_count, active, n_act, N, C, K, Ncols, relu, mch, red);
+    ffn_stream<MT, WAVES, STAGES, 4>(A, W, out, kept_count, active, n_act, N, C, K, Ncols, relu, mch, red, gather,
+                                     a_rows);
 }
 
 __global__ __launch_bounds__(256) void ffn_gemm_f32(const float* __restrict__ A, const float* __restrict__ W,
                                                     float* __restrict__ out, const int32_t* __restrict__ kept_count,
                                                     const int32_t* __restrict__ active,
                                                     const int32_t* __restrict__ n_active, int N, int C, int K,
-                                                    int Ncols, int relu) {
+                                                    int Ncols, int relu, const int32_t* __restrict__ gather) {
   const int a = blockIdx.y;
   if (a >= n_active[0]) return;
   const int e = active[a];
   if (e < 0 || e >= N) return;
   const int row = blockIdx.x;
   if (row >= kept_count[e] || row >= C) return;
-  const float* ar = A + ((int64_t)e * C + row) * K;
+  const int64_t src = gather != nullptr ? (int64_t)gather[(int64_t)e * C + row] : (int64_t)e * C + row;
+  const float* ar = A + src * K;
   const float* wb = W + (int64_t)e * K * Ncols;
   float* orow = out + ((int64_t)e * C + row) * Ncols;
   for (int col = threadIdx.x; col < Ncols; col += 256) {
@@ -423,13 +432,13 @@ static int persistent_grid(const void* kernel, int threads) {
 template <int MT, int J>
 static hipError_t launch_gemm(const void* A, const void* W, void* out, const int32_t* kept, const int32_t* active,
                               const int32_t* n_active, int N, int C, int K, int Ncols, int relu, int mch,
-                              hipStream_t st) {
+                              hipStream_t st, const int32_t* gather, int64_t a_rows) {
   constexpr int kWaves = SWM_FFN_WAVES;
   auto kern = ffn_gemm_bf16<MT, kWaves, SWM_FFN_STAGES, J>;
   const int grid = persistent_grid(reinterpret_cast<const void*>(kern), kWaves * 64);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kWaves * 64), 0, st, static_cast<const uint16_t*>(A),
                      static_cast<const uint16_t*>(W), static_cast<uint16_t*>(out), kept, active, n_active, N, C, K,
-                     Ncols, relu, mch);
+                     Ncols, relu, mch, gather, a_rows);
   return hipGetLastError();
 }
 
@@ -438,46 +447,50 @@ static hipError_t launch_gemm(const void* A, const void* W, void* out, const int
 template <int MT>
 static hipError_t launch_gemm_cols(const void* A, const void* W, void* out, const int32_t* kept,
                                    const int32_t* active, const int32_t* n_active, int N, int C, int K, int Ncols,
-                                   int relu, int mch, hipStream_t st) {
+                                   int relu, int mch, hipStream_t st, const int32_t* gather, int64_t a_rows) {
   if constexpr (kAllow128 && MT <= 3) {
     if (Ncols % 128 == 0)
-      return launch_gemm<MT, 8>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, mch, st);
+      return launch_gemm<MT, 8>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, mch, st, gather, a_rows);
   }
-  return launch_gemm<MT, 4>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, mch, st);
+  return launch_gemm<MT, 4>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, mch, st, gather, a_rows);
 }
 
 static hipError_t gemm_bf16(const FfnPlan& pl, const void* A, const void* W, void* out, const int32_t* kept,
                             const int32_t* active, const int32_t* n_active, int N, int C, int K, int Ncols, int relu,
-                            hipStream_t st) {
+                            hipStream_t st, const int32_t* gather = nullptr, int64_t a_rows = 0) {
   switch (pl.mt) {
-    case 1: return launch_gemm_cols<1>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, pl.mch, st);
-    case 2: return launch_gemm_cols<2>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, pl.mch, st);
-    case 3: return launch_gemm_cols<3>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, pl.mch, st);
-    default: return launch_gemm_cols<4>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, pl.mch, st);
+    case 1: return launch_gemm_cols<1>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, pl.mch, st, gather,
+                                                a_rows);
+    case 2: return launch_gemm_cols<2>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, pl.mch, st, gather,
+                                                a_rows);
+    case 3: return launch_gemm_cols<3>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, pl.mch, st, gather,
+                                                a_rows);
+    default: return launch_gemm_cols<4>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, pl.mch, st, gather,
+                                                a_rows);
   }
 }
 
 hipError_t launch_ffn(const FfnPlan& pl, const void* xin, const void* w1, const void* w2, int dtype, int N, int C, int d,
                       int dff, const int32_t* kept_count, const int32_t* active, const int32_t* n_active, void* xout,
-                      char* ws, hipStream_t st) {
+                      char* ws, hipStream_t st, const int32_t* gather, int64_t a_rows) {
   void* h = ws + pl.off_h;
   if (dtype == 0) {
     hipLaunchKernelGGL(ffn_gemm_f32, dim3((unsigned)C, (unsigned)N), dim3(256), 0, st, static_cast<const float*>(xin),
                        static_cast<const float*>(w1), static_cast<float*>(h), kept_count, active, n_active, N, C, d,
-                       dff, 1);
+                       dff, 1, gather);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(ffn_gemm_f32, dim3((unsigned)C, (unsigned)N), dim3(256), 0, st, static_cast<const float*>(h),
                        static_cast<const float*>(w2), static_cast<float*>(xout), kept_count, active, n_active, N, C,
-                       dff, d, 0);
+                       dff, d, 0, nullptr);
     return hipGetLastError();
   }
   if (tiled_ffn_applies(C, d, dff)) {
-    hipError_t e = launch_tiled_gemm(xin, w1, h, kept_count, active, n_active, N, C, d, dff, 1, st);
+    hipError_t e = launch_tiled_gemm(xin, w1, h, kept_count, active, n_active, N, C, d, dff, 1, st, gather, a_rows);
     if (e != hipSuccess) return e;
     return launch_tiled_gemm(h, w2, xout, kept_count, active, n_active, N, C, dff, d, 0, st);
   }
-  hipError_t e = gemm_bf16(pl, xin, w1, h, kept_count, active, n_active, N, C, d, dff, 1, st);
+  hipError_t e = gemm_bf16(pl, xin, w1, h, kept_count, active, n_active, N, C, d, dff, 1, st, gather, a_rows);
   if (e != hipSuccess) return e;
   return gemm_bf16(pl, h, w2, xout, kept_count, active, n_active, N, C, dff, d, 0, st);
 }

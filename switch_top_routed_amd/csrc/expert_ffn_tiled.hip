@@ -104,7 +104,7 @@ template <int MTW, int NJ, int P>
 __global__ __launch_bounds__(256, (MTW * NJ <= 32 ? 2 : 1)) void ffn_tile_bf16(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, uint16_t* __restrict__ out,
     const int32_t* __restrict__ kept_count, const int32_t* __restrict__ active, const int32_t* __restrict__ n_active,
-    int N, int C, int K, int Ncols, int relu, int mch) {
+    int N, int C, int K, int Ncols, int relu, int mch, const int32_t* __restrict__ gather, int64_t a_rows) {
   static_assert(NJ == 4 || NJ == 8, "tile width 128 or 256 columns");
   static_assert(8 % P == 0, "prefetch depth divides the k-steps of a 256-multiple K");
   constexpr int BM = 32 * MTW;                 // tile rows (2 waves x MTW x 16)
@@ -150,7 +150,9 @@ __global__ __launch_bounds__(256, (MTW * NJ <= 32 ? 2 : 1)) void ffn_tile_bf16(
   const int n0 = nt * TN;
   const int ksteps = K >> 5;
 
-  const __amdgpu_buffer_rsrc_t ares = tile_rsrc(A + ((int64_t)e * C + m0) * K, (int64_t)rows * K * 2);
+  // gather != NULL: A is the token matrix [a_rows, K], tile row r is token gather[e * C + m0 + r]
+  const __amdgpu_buffer_rsrc_t ares = gather != nullptr ? tile_rsrc(A, a_rows * K * 2)
+                                                        : tile_rsrc(A + ((int64_t)e * C + m0) * K, (int64_t)rows * K * 2);
   const __amdgpu_buffer_rsrc_t wres = tile_rsrc(W + (int64_t)e * K * Ncols, (int64_t)K * Ncols * 2);
 
   // A: chunk ch = tid + 256 i is 16-byte chunk ch % 4 of tile row ch / 4
@@ -158,7 +160,8 @@ __global__ __launch_bounds__(256, (MTW * NJ <= 32 ? 2 : 1)) void ffn_tile_bf16(
 #pragma unroll
   for (int i = 0; i < ACH; ++i) {
     const int ch = tid + i * 256, r = ch >> 2, q = ch & 3;
-    a_voff[i] = r < rows ? (r * K + q * 8) * 2 : 0x7ffffff0;  // rows past `rows` read zero
+    const int64_t src = gather != nullptr && r < rows ? gather[(int64_t)e * C + m0 + r] : r;
+    a_voff[i] = r < rows ? (int)((src * K + q * 8) * 2) : 0x7ffffff0;  // rows past `rows` read zero
     a_lds[i] = lds_off(r, q);
   }
   // W, 256 columns: thread (w, c, kg) loads k-rows 8 kg .. 8 kg + 7 of columns
@@ -277,29 +280,31 @@ __global__ __launch_bounds__(256, (MTW * NJ <= 32 ? 2 : 1)) void ffn_tile_bf16(
 
 template <int MTW, int NJ, int P>
 static hipError_t launch_tiled(const void* A, const void* W, void* out, const int32_t* kept, const int32_t* active,
-                               const int32_t* n_active, int N, int C, int K, int Ncols, int relu, hipStream_t st) {
+                               const int32_t* n_active, int N, int C, int K, int Ncols, int relu, hipStream_t st,
+                               const int32_t* gather, int64_t a_rows) {
   constexpr int BM = 32 * MTW, TN = 32 * NJ;
   const int mch = (C + BM - 1) / BM;
   int64_t grid = (int64_t)N * mch * (Ncols / TN);
   grid = (grid + kTiledXcds - 1) / kTiledXcds * kTiledXcds;
   hipLaunchKernelGGL((ffn_tile_bf16<MTW, NJ, P>), dim3((unsigned)grid), dim3(256), 0, st,
                      static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(W), static_cast<uint16_t*>(out), kept,
-                     active, n_active, N, C, K, Ncols, relu, mch);
+                     active, n_active, N, C, K, Ncols, relu, mch, gather, a_rows);
   return hipGetLastError();
 }
 
 bool tiled_ffn_applies(int C, int d, int dff) { return C > 64 && d % kTileN == 0 && dff % kTileN == 0; }
 
 hipError_t launch_tiled_gemm(const void* A, const void* W, void* out, const int32_t* kept, const int32_t* active,
-                             const int32_t* n_active, int N, int C, int K, int Ncols, int relu, hipStream_t st) {
+                             const int32_t* n_active, int N, int C, int K, int Ncols, int relu, hipStream_t st,
+                             const int32_t* gather, int64_t a_rows) {
   // One m-chunk per expert where C allows (each weight panel is then streamed
   // once): 160 x 128 tiles (two workgroups per CU) for 128 < C <= 160, 192 x 256
   // tiles for 160 < C <= 192; 128 x 256 tiles, two workgroups per CU, otherwise.
   if (C > 128 && C <= 160)
-    return launch_tiled<5, 4, SWM_TILE_P>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st);
+    return launch_tiled<5, 4, SWM_TILE_P>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st, gather, a_rows);
   if (C > 160 && C <= 192)
-    return launch_tiled<6, 8, SWM_TILE_P>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st);
-  return launch_tiled<4, 8, 2>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st);
+    return launch_tiled<6, 8, SWM_TILE_P>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st, gather, a_rows);
+  return launch_tiled<4, 8, 2>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st, gather, a_rows);
 }
 
 }  // namespace swm

@@ -13,13 +13,24 @@ namespace swm {
 struct RoutePlan {
   int split;        // 0: fused kernel; >0: number of k-chunks of the split path
   int tm;           // 16-token tiles per workgroup (fused path)
+  int tile_rows;    // tokens per workgroup (= per partial row)
   int64_t nblk;     // number of per-workgroup partial rows
   size_t off_part_p, off_part_cnt, off_logits, bytes;
 };
 RoutePlan route_plan(int64_t T, int d, int N, int dtype);
+// local_rank == NULL: statistics (routed_count, f, P, l_aux) by a final reduction
+// kernel; else every token's rank inside its tile is written and the statistics
+// are left to launch_route_assign_token
 hipError_t launch_route(const RoutePlan& pl, const void* x, const void* wg, const float* bias, int64_t T, int d, int N,
                         int dtype, int32_t* expert_id, float* gate, int32_t* routed_count, float* f, float* P,
-                        float* l_aux, char* ws, hipStream_t st);
+                        float* l_aux, char* ws, hipStream_t st, int32_t* local_rank = nullptr);
+// token-order slots from the router's tiles (after launch_route with local_rank);
+// off: int32 [nblk x N] scratch
+hipError_t launch_route_assign_token(const RoutePlan& pl, int64_t T, int N, int C, const int32_t* expert_id,
+                                     const int32_t* local_rank, int32_t* off, int32_t* routed_count, float* f,
+                                     float* P, float* l_aux, int32_t* slot, int32_t* token_of_slot,
+                                     int32_t* kept_count, int32_t* n_dropped, int32_t* active, int32_t* n_active,
+                                     char* ws, hipStream_t st);
 
 // ---------------- capacity / slots ----------------
 struct AssignPlan {
@@ -46,15 +57,18 @@ struct FfnPlan {
   size_t off_h, bytes;
 };
 FfnPlan ffn_plan(int N, int C, int d, int dff, int dtype);
-// two launches of one kernel (phase 1: H = ReLU(X W1), phase 2: Y = H W2)
+// two launches of one kernel (phase 1: H = ReLU(X W1), phase 2: Y = H W2).
+// gather != NULL: xin is the token matrix [a_rows, d] and row r of expert e is
+// token gather[e * C + r] (token_of_slot), so no dispatched copy is needed.
 hipError_t launch_ffn(const FfnPlan& pl, const void* xin, const void* w1, const void* w2, int dtype, int N, int C, int d,
                       int dff, const int32_t* kept_count, const int32_t* active, const int32_t* n_active, void* xout,
-                      char* ws, hipStream_t st);
+                      char* ws, hipStream_t st, const int32_t* gather = nullptr, int64_t a_rows = 0);
 // writes {M}, {0}, {1} for the dense (shared-expert) FFN
 // LDS-tiled MFMA GEMM for experts with more than 64 rows (and the dense shared FFN)
 bool tiled_ffn_applies(int C, int d, int dff);
 hipError_t launch_tiled_gemm(const void* A, const void* W, void* out, const int32_t* kept, const int32_t* active,
-                             const int32_t* n_active, int N, int C, int K, int Ncols, int relu, hipStream_t st);
+                             const int32_t* n_active, int N, int C, int K, int Ncols, int relu, hipStream_t st,
+                             const int32_t* gather = nullptr, int64_t a_rows = 0);
 hipError_t launch_dense_plan(int32_t* kept, int32_t* active, int32_t* n_active, int32_t M, hipStream_t st);
 
 inline size_t align_up(size_t v, size_t a = 256) { return (v + a - 1) / a * a; }

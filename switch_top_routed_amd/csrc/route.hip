@@ -33,11 +33,14 @@ constexpr int kRouteThreads = 256;
 // logits for `rows` tokens live in LDS lg[m * ldl + n] (no bias yet)
 // lg must hold >= 8 * N floats; it is reused for the cross-wave partial sums.
 // J = experts per lane (N <= 64 * J).
+// local_rank (may be NULL): rank of each token among the tokens of this tile
+// routed to the same expert, in token order (rows <= 64).
 template <int J>
 __device__ void route_epilogue(float* lg, int ldl, int rows, int64_t t0, int64_t T, int N,
                                const float* __restrict__ bias, int32_t* __restrict__ expert_id,
                                float* __restrict__ gate, float* __restrict__ part_p, int32_t* __restrict__ part_cnt,
-                               int64_t blk) {
+                               int32_t* __restrict__ local_rank, int64_t blk) {
+  __shared__ int tile_e[64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   float bs[J], ps[J];
   int cn[J];
@@ -82,9 +85,16 @@ __device__ void route_epilogue(float* lg, int ldl, int rows, int64_t t0, int64_t
     if (lane == 0) {
       expert_id[t] = bi;
       gate[t] = inv;
+      tile_e[m] = bi;
     }
   }
-  __syncthreads();  // every wave is done reading the logits
+  __syncthreads();  // every wave is done reading the logits; tile_e is complete
+  if (local_rank != nullptr && threadIdx.x < rows && t0 + threadIdx.x < T) {
+    const int m = threadIdx.x, em = tile_e[m];
+    int r = 0;
+    for (int q = 0; q < m; ++q) r += (tile_e[q] == em) ? 1 : 0;
+    local_rank[t0 + m] = r;
+  }
   float* red_p = lg;
   int* red_c = reinterpret_cast<int*>(lg + 4 * N);
 #pragma unroll
@@ -111,7 +121,7 @@ template <int TM, int NG, int J>
 __global__ __launch_bounds__(kRouteThreads) void route_fused_bf16(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg, const float* __restrict__ bias, int64_t T, int d,
     int N, int32_t* __restrict__ expert_id, float* __restrict__ gate, float* __restrict__ part_p,
-    int32_t* __restrict__ part_cnt) {
+    int32_t* __restrict__ part_cnt, int32_t* __restrict__ local_rank) {
   extern __shared__ float smem[];
   const int NT = (N + 15) >> 4;
   const int ldl = NT * 16;
@@ -122,39 +132,59 @@ __global__ __launch_bounds__(kRouteThreads) void route_fused_bf16(
   const int ksteps = d >> 5;
   const u32x4 zero = {0u, 0u, 0u, 0u};
 
+  // Operands through buffer loads: rows past T or N get a lane offset beyond the
+  // descriptor's extent and read zeros, so the k-loop needs no branches and the
+  // loads of RP steps stay in flight ahead of the MFMAs (a register ring).
+  constexpr int RP = TM >= 4 ? 4 : 8;
+  const int64_t rows_here = (T - t0) < TM * 16 ? (T - t0) : TM * 16;
+  const __amdgpu_buffer_rsrc_t xres =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x + t0 * d), (short)0, (int)(rows_here * d * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t wres =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(wg), (short)0, (int)((int64_t)N * d * 2), 0x00020000);
+  const int kpad = (ksteps + RP - 1) / RP * RP;
   for (int ntb = w * NG; ntb < NT; ntb += 4 * NG) {
     f32x4 acc[TM][NG];
 #pragma unroll
     for (int mt = 0; mt < TM; ++mt)
 #pragma unroll
       for (int g = 0; g < NG; ++g) acc[mt][g] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const uint16_t* bp[NG];
-    bool bvalid[NG];
+    int b_voff[NG], a_voff[TM];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       const int n = (ntb + g) * 16 + c;
-      bvalid[g] = (ntb + g) < NT && n < N;
-      bp[g] = wg + (int64_t)(bvalid[g] ? n : 0) * d + kg * 8;
+      b_voff[g] = n < N ? (n * d + kg * 8) * 2 : 0x7ffffff0;
     }
-    const uint16_t* ap[TM];
-    bool avalid[TM];
 #pragma unroll
     for (int mt = 0; mt < TM; ++mt) {
-      const int64_t row = t0 + mt * 16 + c;
-      avalid[mt] = row < T;
-      ap[mt] = x + (avalid[mt] ? row : 0) * (int64_t)d + kg * 8;
+      const int r = mt * 16 + c;
+      a_voff[mt] = r < rows_here ? (r * d + kg * 8) * 2 : 0x7ffffff0;
     }
-    for (int ks = 0; ks < ksteps; ++ks) {
-      u32x4 a[TM], b[NG];
+    u32x4 ra[RP][TM], rb[RP][NG];
+    auto load = [&](int slot, int ks) {
+      const int so = (ks < ksteps ? ks : ksteps - 1) * 64;  // past the end: re-read the last step
 #pragma unroll
       for (int mt = 0; mt < TM; ++mt)
-        a[mt] = avalid[mt] ? *reinterpret_cast<const u32x4*>(ap[mt] + ks * 32) : zero;
+        ra[slot][mt] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, a_voff[mt], so, 0));
 #pragma unroll
-      for (int g = 0; g < NG; ++g) b[g] = bvalid[g] ? *reinterpret_cast<const u32x4*>(bp[g] + ks * 32) : zero;
+      for (int g = 0; g < NG; ++g)
+        rb[slot][g] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, b_voff[g], so, 0));
+    };
 #pragma unroll
-      for (int mt = 0; mt < TM; ++mt)
+    for (int s0 = 0; s0 < RP - 1; ++s0) load(s0, s0);
+    for (int it = 0; it < kpad; it += RP) {
 #pragma unroll
-        for (int g = 0; g < NG; ++g) acc[mt][g] = mfma_bf16_16x16x32(a[mt], b[g], acc[mt][g]);
+      for (int u = 0; u < RP; ++u) {
+        const int ks = it + u;
+        load((u + RP - 1) % RP, ks + RP - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        const bool live = ks < ksteps;
+#pragma unroll
+        for (int mt = 0; mt < TM; ++mt) {
+          const u32x4 a = live ? ra[u][mt] : zero;
+#pragma unroll
+          for (int g = 0; g < NG; ++g) acc[mt][g] = mfma_bf16_16x16x32(a, rb[u][g], acc[mt][g]);
+        }
+      }
     }
 #pragma unroll
     for (int mt = 0; mt < TM; ++mt)
@@ -167,7 +197,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_fused_bf16(
       }
   }
   __syncthreads();
-  route_epilogue<J>(lg, ldl, TM * 16, t0, T, N, bias, expert_id, gate, part_p, part_cnt, blockIdx.x);
+  route_epilogue<J>(lg, ldl, TM * 16, t0, T, N, bias, expert_id, gate, part_p, part_cnt, local_rank, blockIdx.x);
 }
 
 // ----------------------------------------------------------------------------
@@ -228,7 +258,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_softmax_split(const float
                                                                      int32_t* __restrict__ expert_id,
                                                                      float* __restrict__ gate,
                                                                      float* __restrict__ part_p,
-                                                                     int32_t* __restrict__ part_cnt) {
+                                                                     int32_t* __restrict__ part_cnt,
+                                                                     int32_t* __restrict__ local_rank) {
   extern __shared__ float smem[];
   const int ldl = N;
   float* lg = smem;
@@ -242,7 +273,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_softmax_split(const float
     lg[m * ldl + n] = v;
   }
   __syncthreads();
-  route_epilogue<J>(lg, ldl, 16, t0, T, N, bias, expert_id, gate, part_p, part_cnt, blockIdx.x);
+  route_epilogue<J>(lg, ldl, 16, t0, T, N, bias, expert_id, gate, part_p, part_cnt, local_rank, blockIdx.x);
 }
 
 // ----------------------------------------------------------------------------
@@ -253,7 +284,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_f32(const float* __restri
                                                            const float* __restrict__ bias, int64_t T, int d, int N,
                                                            int32_t* __restrict__ expert_id, float* __restrict__ gate,
                                                            float* __restrict__ part_p,
-                                                           int32_t* __restrict__ part_cnt) {
+                                                           int32_t* __restrict__ part_cnt,
+                                                           int32_t* __restrict__ local_rank) {
   extern __shared__ float smem[];
   const int ldl = N;
   float* lg = smem;
@@ -270,7 +302,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_f32(const float* __restri
     lg[m * ldl + n] = acc;
   }
   __syncthreads();
-  route_epilogue<J>(lg, ldl, 16, t0, T, N, bias, expert_id, gate, part_p, part_cnt, blockIdx.x);
+  route_epilogue<J>(lg, ldl, 16, t0, T, N, bias, expert_id, gate, part_p, part_cnt, local_rank, blockIdx.x);
 }
 
 // ----------------------------------------------------------------------------
@@ -280,42 +312,46 @@ __global__ __launch_bounds__(kRouteThreads) void route_f32(const float* __restri
 // every load is coalesced), block group g = tid / NP takes blocks g, g + G, ...
 // (NP = N rounded up to 64, G = 1024 / NP); the G partial sums are combined in g
 // order, the N products in a fixed tree order.
-__global__ __launch_bounds__(1024) void route_finalize(const float* __restrict__ part_p,
-                                                       const int32_t* __restrict__ part_cnt, int64_t nblk, int64_t T,
-                                                       int N, int NP, int32_t* __restrict__ routed_count,
-                                                       float* __restrict__ f, float* __restrict__ P,
-                                                       float* __restrict__ l_aux) {
+// Fixed-order reduction of the per-workgroup partials (blockDim = 1024), shared
+// by route_finalize and route_assign_token.  Thread tid: expert n = tid % NP
+// (consecutive lanes read consecutive experts: coalesced), group g = tid / NP
+// (NP = N rounded up to 64, G = 1024 / NP groups) owns the contiguous tile range
+// [b0, b1), read 16 tiles at a time.  Group sums meet in LDS in group order; the N products go through
+// a fixed tree.  P_i: fp64 sums in tile order.  cnt_out (LDS, >= 1024 ints)
+// receives each thread's count over its range.
+__device__ __forceinline__ void finalize_partials(const float* __restrict__ part_p,
+                                                  const int32_t* __restrict__ part_cnt, int64_t nblk, int64_t T,
+                                                  int N, int NP, int32_t* __restrict__ routed_count,
+                                                  float* __restrict__ f, float* __restrict__ P,
+                                                  float* __restrict__ l_aux, int* cnt_out) {
   __shared__ double sp[1024];
-  __shared__ long long sc[1024];
   __shared__ double sl[1024];
   const int tid = threadIdx.x;
   const int G = 1024 / NP;
   const int n = tid % NP, g = tid / NP;
+  const int64_t per = (nblk + G - 1) / G;
+  const int64_t b0 = (int64_t)g * per, b1 = (b0 + per < nblk) ? b0 + per : nblk;
   double accp = 0.0;
-  long long accc = 0;
+  int accc = 0;
   if (n < N && g < G) {
-    int64_t b = g;
-    for (; b + 7 * (int64_t)G < nblk; b += 8 * (int64_t)G) {  // 8 coalesced loads in flight
-      float pv[8];
-      int cv[8];
+    for (int64_t b = b0; b < b1; b += 16) {  // 16 coalesced loads of each array in flight
+      float pv[16];
+      int cv[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        pv[u] = part_p[(b + u * (int64_t)G) * N + n];
-        cv[u] = part_cnt[(b + u * (int64_t)G) * N + n];
+      for (int u = 0; u < 16; ++u) {
+        const bool in = b + u < b1;
+        pv[u] = in ? part_p[(b + u) * N + n] : 0.f;
+        cv[u] = in ? part_cnt[(b + u) * N + n] : 0;
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < 16; ++u) {
         accp += (double)pv[u];
         accc += cv[u];
       }
     }
-    for (; b < nblk; b += G) {
-      accp += (double)part_p[b * N + n];
-      accc += part_cnt[b * N + n];
-    }
   }
   sp[tid] = accp;
-  sc[tid] = accc;
+  cnt_out[tid] = accc;
   __syncthreads();
   double term = 0.0;
   if (tid < N) {
@@ -323,7 +359,7 @@ __global__ __launch_bounds__(1024) void route_finalize(const float* __restrict__
     long long cnum = 0;
     for (int i = 0; i < G; ++i) {
       s += sp[i * NP + tid];
-      cnum += sc[i * NP + tid];
+      cnum += cnt_out[i * NP + tid];
     }
     const double fn = (double)cnum / (double)T;
     const double pn = s / (double)T;
@@ -339,6 +375,102 @@ __global__ __launch_bounds__(1024) void route_finalize(const float* __restrict__
     __syncthreads();
   }
   if (tid == 0) l_aux[0] = (float)((double)N * sl[0]);
+}
+
+__global__ __launch_bounds__(1024) void route_finalize(const float* __restrict__ part_p,
+                                                       const int32_t* __restrict__ part_cnt, int64_t nblk, int64_t T,
+                                                       int N, int NP, int32_t* __restrict__ routed_count,
+                                                       float* __restrict__ f, float* __restrict__ P,
+                                                       float* __restrict__ l_aux) {
+  __shared__ int cnt[1024];
+  finalize_partials(part_p, part_cnt, nblk, T, N, NP, routed_count, f, P, l_aux, cnt);
+}
+
+// Token-order capacity and slots straight from the router's tiles (one
+// workgroup; "Top-1 Routing" page, Token Dropping).  A token's rank inside its
+// expert is the number of earlier tokens routed there: the count in earlier
+// tiles (an exclusive prefix over the tiles of the per-tile counts that the
+// router already keeps for f_i) plus its rank inside its own tile
+// (local_rank, written by the router).  Kept iff rank < C.  Also writes the
+// statistics of route_finalize, kept_count, n_dropped, the active list and
+// token_of_slot (-1 for empty slots).  off = workspace [nblk x N] int32.
+__global__ __launch_bounds__(1024) void route_assign_token(
+    const float* __restrict__ part_p, const int32_t* __restrict__ part_cnt, int64_t nblk, int tile_rows, int64_t T,
+    int N, int NP, int C, const int32_t* __restrict__ expert_id, const int32_t* __restrict__ local_rank,
+    int32_t* __restrict__ off, int32_t* __restrict__ routed_count, float* __restrict__ f, float* __restrict__ P,
+    float* __restrict__ l_aux, int32_t* __restrict__ slot, int32_t* __restrict__ token_of_slot,
+    int32_t* __restrict__ kept_count, int32_t* __restrict__ n_dropped, int32_t* __restrict__ active,
+    int32_t* __restrict__ n_active) {
+  __shared__ int gsum[1024];
+  __shared__ int wsum[16];
+  finalize_partials(part_p, part_cnt, nblk, T, N, NP, routed_count, f, P, l_aux, gsum);
+  const int tid = threadIdx.x;
+  const int G = 1024 / NP;
+  const int n = tid % NP, g = tid / NP;
+  // exclusive prefix over tiles, per expert: earlier groups' sums (gsum, in
+  // LDS), then the running count along this thread's own tile range
+  const int64_t per = (nblk + G - 1) / G;
+  const int64_t b0 = (int64_t)g * per, b1 = (b0 + per < nblk) ? b0 + per : nblk;
+  if (n < N && g < G) {
+    int run = 0;
+    for (int i = 0; i < g; ++i) run += gsum[i * NP + n];
+    for (int64_t b = b0; b < b1; b += 16) {
+      int cv[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) cv[u] = (b + u < b1) ? part_cnt[(b + u) * N + n] : 0;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        if (b + u < b1) off[(b + u) * N + n] = run;
+        run += cv[u];
+      }
+    }
+  }
+  int kept = 0;
+  if (tid < N) {
+    const int total = routed_count[tid];  // written by this thread in finalize_partials
+    kept = total < C ? total : C;
+    kept_count[tid] = kept;
+  }
+  int tot_active, tot_kept;
+  const int pos = block_exclusive_scan(kept > 0 ? 1 : 0, wsum, &tot_active);
+  block_exclusive_scan(kept, wsum, &tot_kept);
+  if (tid < N && kept > 0) active[pos] = tid;
+  if (tid == 0) {
+    n_active[0] = tot_active;
+    n_dropped[0] = (int32_t)(T - tot_kept);
+  }
+  for (int64_t i = tid; i < (int64_t)N * C; i += 1024) token_of_slot[i] = -1;
+  __syncthreads();  // off[] and the -1 fill (global memory, this workgroup) are complete
+  // 8 tokens per thread at a time: their loads, then the dependent offset loads, then the stores
+  const int rows = tile_rows;
+  for (int64_t t0 = tid; t0 < T; t0 += 8 * 1024) {
+    int e[8], lr[8], o[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t t = t0 + (int64_t)u * 1024;
+      e[u] = t < T ? expert_id[t] : 0;
+      lr[u] = t < T ? local_rank[t] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t t = t0 + (int64_t)u * 1024;
+      const int tile = (int)((uint32_t)t / (uint32_t)rows);  // T < 2^31
+      o[u] = t < T ? off[(int64_t)tile * N + e[u]] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t t = t0 + (int64_t)u * 1024;
+      if (t < T) {
+        const int r = o[u] + lr[u];
+        if (r < C) {
+          slot[t] = r;
+          token_of_slot[(int64_t)e[u] * C + r] = (int32_t)t;
+        } else {
+          slot[t] = -1;
+        }
+      }
+    }
+  }
 }
 
 // ----------------------------------------------------------------------------
@@ -376,6 +508,7 @@ RoutePlan route_plan(int64_t T, int d, int N, int dtype) {
   off = align_up(off + (size_t)pl.nblk * N * 4);
   pl.off_logits = off;
   if (pl.split > 0) off = align_up(off + (size_t)pl.split * T * N * 4);
+  pl.tile_rows = pl.split == 0 ? pl.tm * 16 : 16;
   pl.bytes = off;
   return pl;
 }
@@ -383,7 +516,7 @@ RoutePlan route_plan(int64_t T, int d, int N, int dtype) {
 template <int J>
 static hipError_t launch_route_j(const RoutePlan& pl, const void* x, const void* wg, const float* bias, int64_t T,
                                  int d, int N, int dtype, int32_t* expert_id, float* gate, float* part_p,
-                                 int32_t* part_cnt, char* ws, hipStream_t st) {
+                                 int32_t* part_cnt, int32_t* local_rank, char* ws, hipStream_t st) {
   if (dtype == 1 && pl.split == 0) {
     const int NT = (N + 15) / 16;
     const size_t lds = (size_t)pl.tm * 16 * NT * 16 * 4;
@@ -392,13 +525,13 @@ static hipError_t launch_route_j(const RoutePlan& pl, const void* x, const void*
     auto* wb = static_cast<const uint16_t*>(wg);
     if (pl.tm == 4)
       hipLaunchKernelGGL((route_fused_bf16<4, 2, J>), grid, dim3(kRouteThreads), lds, st, xb, wb, bias, T, d, N,
-                         expert_id, gate, part_p, part_cnt);
+                         expert_id, gate, part_p, part_cnt, local_rank);
     else if (pl.tm == 2)
       hipLaunchKernelGGL((route_fused_bf16<2, 2, J>), grid, dim3(kRouteThreads), lds, st, xb, wb, bias, T, d, N,
-                         expert_id, gate, part_p, part_cnt);
+                         expert_id, gate, part_p, part_cnt, local_rank);
     else
       hipLaunchKernelGGL((route_fused_bf16<1, 2, J>), grid, dim3(kRouteThreads), lds, st, xb, wb, bias, T, d, N,
-                         expert_id, gate, part_p, part_cnt);
+                         expert_id, gate, part_p, part_cnt, local_rank);
   } else if (dtype == 1) {
     float* plog = reinterpret_cast<float*>(ws + pl.off_logits);
     hipLaunchKernelGGL((route_logits_split_bf16<2>), dim3((unsigned)pl.nblk, (unsigned)pl.split), dim3(kRouteThreads),
@@ -408,32 +541,47 @@ static hipError_t launch_route_j(const RoutePlan& pl, const void* x, const void*
     if (e != hipSuccess) return e;
     const size_t lds = (size_t)16 * N * 4;
     hipLaunchKernelGGL(route_softmax_split<J>, dim3((unsigned)pl.nblk), dim3(kRouteThreads), lds, st, plog, pl.split,
-                       T, N, bias, expert_id, gate, part_p, part_cnt);
+                       T, N, bias, expert_id, gate, part_p, part_cnt, local_rank);
   } else {
     const size_t lds = (size_t)16 * N * 4;
     hipLaunchKernelGGL(route_f32<J>, dim3((unsigned)pl.nblk), dim3(kRouteThreads), lds, st,
                        static_cast<const float*>(x), static_cast<const float*>(wg), bias, T, d, N, expert_id, gate,
-                       part_p, part_cnt);
+                       part_p, part_cnt, local_rank);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_route(const RoutePlan& pl, const void* x, const void* wg, const float* bias, int64_t T, int d, int N,
                         int dtype, int32_t* expert_id, float* gate, int32_t* routed_count, float* f, float* P,
-                        float* l_aux, char* ws, hipStream_t st) {
+                        float* l_aux, char* ws, hipStream_t st, int32_t* local_rank) {
   float* part_p = reinterpret_cast<float*>(ws + pl.off_part_p);
   int32_t* part_cnt = reinterpret_cast<int32_t*>(ws + pl.off_part_cnt);
   hipError_t e;
   if (N <= 128)
-    e = launch_route_j<2>(pl, x, wg, bias, T, d, N, dtype, expert_id, gate, part_p, part_cnt, ws, st);
+    e = launch_route_j<2>(pl, x, wg, bias, T, d, N, dtype, expert_id, gate, part_p, part_cnt, local_rank, ws, st);
   else if (N <= 512)
-    e = launch_route_j<8>(pl, x, wg, bias, T, d, N, dtype, expert_id, gate, part_p, part_cnt, ws, st);
+    e = launch_route_j<8>(pl, x, wg, bias, T, d, N, dtype, expert_id, gate, part_p, part_cnt, local_rank, ws, st);
   else
-    e = launch_route_j<16>(pl, x, wg, bias, T, d, N, dtype, expert_id, gate, part_p, part_cnt, ws, st);
+    e = launch_route_j<16>(pl, x, wg, bias, T, d, N, dtype, expert_id, gate, part_p, part_cnt, local_rank, ws, st);
   if (e != hipSuccess) return e;
+  if (local_rank != nullptr) return hipSuccess;  // the statistics come from launch_route_assign_token
   const int NP = (N + 63) / 64 * 64;
   hipLaunchKernelGGL(route_finalize, dim3(1), dim3(1024), 0, st, part_p, part_cnt, pl.nblk, T, N, NP, routed_count, f,
                      P, l_aux);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_assign_token(const RoutePlan& pl, int64_t T, int N, int C, const int32_t* expert_id,
+                                     const int32_t* local_rank, int32_t* off, int32_t* routed_count, float* f,
+                                     float* P, float* l_aux, int32_t* slot, int32_t* token_of_slot,
+                                     int32_t* kept_count, int32_t* n_dropped, int32_t* active, int32_t* n_active,
+                                     char* ws, hipStream_t st) {
+  const float* part_p = reinterpret_cast<const float*>(ws + pl.off_part_p);
+  const int32_t* part_cnt = reinterpret_cast<const int32_t*>(ws + pl.off_part_cnt);
+  const int NP = (N + 63) / 64 * 64;
+  hipLaunchKernelGGL(route_assign_token, dim3(1), dim3(1024), 0, st, part_p, part_cnt, pl.nblk, pl.tile_rows, T, N,
+                     NP, C, expert_id, local_rank, off, routed_count, f, P, l_aux, slot, token_of_slot, kept_count,
+                     n_dropped, active, n_active);
   return hipGetLastError();
 }
 

@@ -127,3 +127,14 @@ def test_timed_forward_validation(L):
     ev = (ctypes.c_void_p * 7)()
     assert L.switch_moe_forward_timed(ctypes.byref(d), None, None, FAKE, 1 << 30, None, ev) == E_NULL
     assert b"inputs is NULL" in L.switch_last_error()
+
+
+def test_size_limits_for_32bit_offsets(L):
+    """One expert's weight matrix must stay addressable with 32-bit buffer offsets."""
+    ffn = L.switch_expert_ffn
+    assert ffn(FAKE, FAKE, FAKE, 1, 8, 8, 65536, 32768, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 62, None) == E_SHAPE
+    assert b"exceeds 2^30" in L.switch_last_error()
+    d = native.SwitchMoeDesc(T=64, d_model=65536, d_ff=32768, N=8, C=0, capacity_factor=1.0, dtype=1,
+                             priority=0, flags=1, d_ff_shared=0)
+    assert L.switch_moe_workspace_bytes(ctypes.byref(d)) == 0
+    assert _route(L, d=(1 << 20) + 128) == E_SHAPE

@@ -206,6 +206,41 @@ def test_base_layer_deterministic_and_poison_proof(base):
         np.testing.assert_array_equal(host_bits(v), a[k], err_msg=k)
 
 
+def _staged_layer(wl, d, C, priority="token", gate_scale=True):
+    """The layer composed from the per-stage entry points (router, assignment,
+    dispatch, expert FFN, combine), for comparison with switch_moe_forward."""
+    r = sw.switch_route(d["x"], d["w_gate"], d["bias"])
+    a = sw.switch_assign_capacity(r["expert_id"], r["gate"], wl.N, C, priority)
+    xin = sw.switch_dispatch(d["x"], a["token_of_slot"], a["kept_count"], wl.N, C)
+    xout = sw.switch_expert_ffn(xin, d["w1"], d["w2"], a["kept_count"], a["active"], a["n_active"])
+    y = sw.switch_combine(xout, d["x"], r["expert_id"], a["slot"], r["gate"], native.GATE_SCALE if gate_scale else 0)
+    torch.cuda.synchronize()
+    return dict(r, **a, y=y)
+
+
+def test_base_layer_matches_staged_path(base):
+    """switch_moe_forward (token order: slots from the router's tiles, GEMM 1
+    gathering x rows) is bit-identical to the composition of the per-stage entry
+    points (separate assignment kernels and an explicit dispatch copy)."""
+    wl, inp, d, ref = base
+    _say("base layer vs staged path")
+    layer, o = run_layer(wl, d)
+    st = _staged_layer(wl, d, layer.C)
+    for k in ("y", "expert_id", "gate", "slot", "kept_count", "routed_count", "f", "P", "l_aux", "n_dropped"):
+        np.testing.assert_array_equal(host_bits(o[k]), host_bits(st[k]), err_msg=k)
+
+
+@pytest.mark.parametrize("name", ["ragged", "f32-odd", "n1000", "tiled-c150"])
+def test_edge_layer_matches_staged_path(name):
+    wl = next(w for w in EDGE if w.name == name)
+    _say(f"edge layer vs staged path {name}")
+    inp, d = prepared(wl)
+    layer, o = run_layer(wl, d)
+    st = _staged_layer(wl, d, layer.C, priority=wl.priority, gate_scale=wl.gate_scale)
+    for k in ("y", "expert_id", "gate", "slot", "kept_count", "routed_count", "f", "P", "l_aux", "n_dropped"):
+        np.testing.assert_array_equal(host_bits(o[k]), host_bits(st[k]), err_msg=k)
+
+
 def test_base_layer_timed_matches_untimed(base):
     """switch_moe_forward_timed: same outputs bit for bit, stage events in order."""
     wl, inp, d, ref = base
