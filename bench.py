@@ -41,7 +41,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 # Sources of the expert-FFN GEMM kernels.  HBM traffic measured with rocprofv3
 # counters is reported only while these files are byte-identical to the ones
 # the counters were taken on.
-FFN_SOURCES = ("switch_top_routed_amd/csrc/expert_ffn.hip", "switch_top_routed_amd/csrc/expert_ffn_tiled.hip",
+FFN_SOURCES = ("switch_top_routed_amd/csrc/expert_ffn.hip", "switch_top_routed_amd/csrc/expert_ffn_dma.hip",
                "switch_top_routed_amd/csrc/common.hpp", "switch_top_routed_amd/csrc/kernels.hpp")
 # FETCH_SIZE / WRITE_SIZE (KiB per dispatch, as rocprofv3 prints them) of the two
 # routed-FFN launches of one step, and the scale factors that a plain 1 GiB
@@ -207,7 +207,7 @@ def main():
 
     launch_s = float(np.mean(ffn_stage_ms)) * 1e-3 / 2
     achieved = gbs(ffn_launch_bytes, launch_s)
-    kernel = "ffn_tile_bf16" if C > 64 and d % 256 == 0 and F % 256 == 0 else "ffn_gemm_bf16"
+    kernel = "ffn_tile_dma" if C > 64 and d % 256 == 0 and F % 256 == 0 else "ffn_gemm_bf16"
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_bytes(wl.name),
                 "kernel": f"{kernel} (routed expert FFN GEMM, 2 launches per step)",

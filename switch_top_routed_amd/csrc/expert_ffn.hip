@@ -486,9 +486,9 @@ hipError_t launch_ffn(const FfnPlan& pl, const void* xin, const void* w1, const 
     return hipGetLastError();
   }
   if (tiled_ffn_applies(C, d, dff)) {
-    hipError_t e = launch_tiled_gemm(xin, w1, h, kept_count, active, n_active, N, C, d, dff, 1, st, gather, a_rows);
+    hipError_t e = launch_tiled_dma(xin, w1, h, kept_count, active, n_active, N, C, d, dff, 1, st, gather, a_rows);
     if (e != hipSuccess) return e;
-    return launch_tiled_gemm(h, w2, xout, kept_count, active, n_active, N, C, dff, d, 0, st);
+    return launch_tiled_dma(h, w2, xout, kept_count, active, n_active, N, C, dff, d, 0, st);
   }
   hipError_t e = gemm_bf16(pl, xin, w1, h, kept_count, active, n_active, N, C, d, dff, 1, st, gather, a_rows);
   if (e != hipSuccess) return e;

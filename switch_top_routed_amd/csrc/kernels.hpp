@@ -64,11 +64,12 @@ hipError_t launch_ffn(const FfnPlan& pl, const void* xin, const void* w1, const 
                       int dff, const int32_t* kept_count, const int32_t* active, const int32_t* n_active, void* xout,
                       char* ws, hipStream_t st, const int32_t* gather = nullptr, int64_t a_rows = 0);
 // writes {M}, {0}, {1} for the dense (shared-expert) FFN
-// LDS-tiled MFMA GEMM for experts with more than 64 rows (and the dense shared FFN)
+// LDS-tiled MFMA GEMM (direct global-to-LDS loads, transposing LDS reads) for
+// experts with more than 64 rows and the dense shared FFN
 bool tiled_ffn_applies(int C, int d, int dff);
-hipError_t launch_tiled_gemm(const void* A, const void* W, void* out, const int32_t* kept, const int32_t* active,
-                             const int32_t* n_active, int N, int C, int K, int Ncols, int relu, hipStream_t st,
-                             const int32_t* gather = nullptr, int64_t a_rows = 0);
+hipError_t launch_tiled_dma(const void* A, const void* W, void* out, const int32_t* kept, const int32_t* active,
+                            const int32_t* n_active, int N, int C, int K, int Ncols, int relu, hipStream_t st,
+                            const int32_t* gather = nullptr, int64_t a_rows = 0);
 hipError_t launch_dense_plan(int32_t* kept, int32_t* active, int32_t* n_active, int32_t M, hipStream_t st);
 
 inline size_t align_up(size_t v, size_t a = 256) { return (v + a - 1) / a * a; }
