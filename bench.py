@@ -66,6 +66,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="switch-base-uniform")
+    ap.add_argument("--capacity-factor", type=float, default=None, help="override the workload's capacity factor")
+    ap.add_argument("--priority", choices=("token", "gate"), default=None, help="override the overflow priority")
+    ap.add_argument("--no-gate-scale", action="store_true", help="combine without the gate multiplier")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stage-steps", type=int, default=20, help="extra steps with every stage boundary timed")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -112,6 +115,15 @@ def main():
     import workloads
 
     wl = workloads.WORKLOADS[args.workload]
+    over = {}
+    if args.capacity_factor is not None:
+        over["capacity_factor"] = args.capacity_factor
+    if args.priority is not None:
+        over["priority"] = args.priority
+    if args.no_gate_scale:
+        over["gate_scale"] = False
+    if over:
+        wl = wl.with_(**over)
     dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     esz = 2 if wl.dtype == "bf16" else 4
     weight_bytes = 2 * wl.N * wl.d_model * wl.d_ff * esz
@@ -207,9 +219,12 @@ def main():
 
     launch_s = float(np.mean(ffn_stage_ms)) * 1e-3 / 2
     achieved = gbs(ffn_launch_bytes, launch_s)
-    kernel = "ffn_tile_dma" if C > 64 and d % 256 == 0 and F % 256 == 0 else "ffn_gemm_bf16"
+    if wl.dtype != "bf16":
+        kernel = "ffn_gemm_f32"
+    else:
+        kernel = "ffn_tile_dma" if C > 64 and d % 256 == 0 and F % 256 == 0 else "ffn_gemm_bf16"
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_bytes(wl.name),
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None if over else traffic_bytes(wl.name),
                 "kernel": f"{kernel} (routed expert FFN GEMM, 2 launches per step)",
                 "bytes_per_launch": ffn_launch_bytes, "launch_us": launch_s * 1e6,
                 "launch_timing": f"HIP events around the routed FFN in each of the {args.steps} timed steps"}

@@ -260,20 +260,28 @@ __global__ __launch_bounds__(kRouteThreads) void route_softmax_split(const float
                                                                      float* __restrict__ part_p,
                                                                      int32_t* __restrict__ part_cnt,
                                                                      int32_t* __restrict__ local_rank) {
+  // one token per workgroup: its N logits are sums over the S k-chunks, in
+  // chunk order, with 8 independent loads in flight per expert
   extern __shared__ float smem[];
-  const int ldl = N;
   float* lg = smem;
-  const int64_t t0 = (int64_t)blockIdx.x * 16;
-  for (int idx = threadIdx.x; idx < 16 * N; idx += kRouteThreads) {
-    const int m = idx / N, n = idx - m * N;
-    const int64_t t = t0 + m;
+  const int64_t t = blockIdx.x;
+  for (int n = threadIdx.x; n < N; n += kRouteThreads) {
+    const float* p = plog + t * N + n;
+    const int64_t stride = T * N;
     float v = 0.f;
-    if (t < T)
-      for (int s = 0; s < S; ++s) v += plog[((int64_t)s * T + t) * N + n];
-    lg[m * ldl + n] = v;
+    int s = 0;
+    for (; s + 8 <= S; s += 8) {
+      float q[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) q[u] = p[(s + u) * stride];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v += q[u];
+    }
+    for (; s < S; ++s) v += p[s * stride];
+    lg[n] = v;
   }
   __syncthreads();
-  route_epilogue<J>(lg, ldl, 16, t0, T, N, bias, expert_id, gate, part_p, part_cnt, local_rank, blockIdx.x);
+  route_epilogue<J>(lg, N, 1, t, T, N, bias, expert_id, gate, part_p, part_cnt, local_rank, blockIdx.x);
 }
 
 // ----------------------------------------------------------------------------
@@ -488,6 +496,8 @@ RoutePlan route_plan(int64_t T, int d, int N, int dtype) {
     pl.tm = tm;
     pl.nblk = (T + tm * 16 - 1) / (tm * 16);
   } else if (dtype == 1) {
+    // split path: 16-token tiles x S k-chunks for the logits, then one
+    // workgroup per token for the chunk sums and the softmax
     const int ksteps = d / 32;
     int64_t s = (256 + tiles16 - 1) / tiles16;
     if (s > ksteps) s = ksteps;
@@ -495,7 +505,7 @@ RoutePlan route_plan(int64_t T, int d, int N, int dtype) {
     if (s < 1) s = 1;
     pl.split = (int)s;
     pl.tm = 1;
-    pl.nblk = tiles16;
+    pl.nblk = T;
   } else {
     pl.split = 0;
     pl.tm = 1;
@@ -508,7 +518,7 @@ RoutePlan route_plan(int64_t T, int d, int N, int dtype) {
   off = align_up(off + (size_t)pl.nblk * N * 4);
   pl.off_logits = off;
   if (pl.split > 0) off = align_up(off + (size_t)pl.split * T * N * 4);
-  pl.tile_rows = pl.split == 0 ? pl.tm * 16 : 16;
+  pl.tile_rows = pl.split == 0 ? pl.tm * 16 : (dtype == 1 ? 1 : 16);
   pl.bytes = off;
   return pl;
 }
@@ -534,12 +544,12 @@ static hipError_t launch_route_j(const RoutePlan& pl, const void* x, const void*
                          expert_id, gate, part_p, part_cnt, local_rank);
   } else if (dtype == 1) {
     float* plog = reinterpret_cast<float*>(ws + pl.off_logits);
-    hipLaunchKernelGGL((route_logits_split_bf16<2>), dim3((unsigned)pl.nblk, (unsigned)pl.split), dim3(kRouteThreads),
+    hipLaunchKernelGGL((route_logits_split_bf16<2>), dim3((unsigned)((T + 15) / 16), (unsigned)pl.split), dim3(kRouteThreads),
                        0, st, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wg), T, d, N, pl.split,
                        plog);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const size_t lds = (size_t)16 * N * 4;
+    const size_t lds = (size_t)8 * N * 4;  // the epilogue reuses it for the cross-wave partials
     hipLaunchKernelGGL(route_softmax_split<J>, dim3((unsigned)pl.nblk), dim3(kRouteThreads), lds, st, plog, pl.split,
                        T, N, bias, expert_id, gate, part_p, part_cnt, local_rank);
   } else {
