@@ -160,11 +160,82 @@ __global__ __launch_bounds__(1024) void assign_sort_gate(const int32_t* __restri
                                                          int32_t* __restrict__ token_of_slot,
                                                          uint64_t* __restrict__ gkeys) {
   extern __shared__ uint64_t keys[];  // kSegMax
+  __shared__ int hist[256];
+  __shared__ int sel[2];
+  __shared__ uint64_t kept_keys[1024];
   const int e = blockIdx.x, tid = threadIdx.x;
   const int n = total[e], base = seg_start[e];
   const int kept = n < C ? n : C;
   for (int s = kept + tid; s < C; s += 1024) token_of_slot[(int64_t)e * C + s] = -1;
   if (n == 0) return;
+  if (n <= kSegMax && kept <= 1024) {
+    // Only the `kept` smallest keys get slots.  Find the kept-th smallest key
+    // by a radix select (8 passes of 8-bit digits, histograms in LDS), gather
+    // the keys at or below it, and rank each by counting the smaller ones
+    // (keys are unique, so the result does not depend on the gather order).
+    for (int i = tid; i < n; i += 1024) keys[i] = gate_key(gate, perm[base + i]);
+    uint64_t prefix = 0, mask = 0;
+    int want = kept;  // 1-based rank of the threshold among the keys matching prefix
+    if (kept < n) {
+      for (int shift = 56; shift >= 0; shift -= 8) {
+        for (int b = tid; b < 256; b += 1024) hist[b] = 0;
+        __syncthreads();
+        for (int i = tid; i < n; i += 1024) {
+          const uint64_t k = keys[i];
+          if ((k & mask) == prefix) atomicAdd(&hist[(int)((k >> shift) & 255)], 1);
+        }
+        __syncthreads();
+        if (tid < 64) {  // one wave: 4 bins per lane, ascending digit order
+          int h[4], sum = 0;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            h[q] = hist[tid * 4 + q];
+            sum += h[q];
+          }
+          int incl = sum;
+#pragma unroll
+          for (int o = 1; o < 64; o <<= 1) {
+            const int u = __shfl_up(incl, o, 64);
+            if (tid >= o) incl += u;
+          }
+          int below = incl - sum;  // count in digits < 4 * tid
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (below < want && want <= below + h[q]) {
+              sel[0] = tid * 4 + q;
+              sel[1] = below;
+            }
+            below += h[q];
+          }
+        }
+        __syncthreads();
+        const int d = sel[0];
+        want -= sel[1];
+        prefix |= (uint64_t)d << shift;
+        mask |= (uint64_t)255 << shift;
+        __syncthreads();  // sel and hist are rewritten in the next pass
+      }
+    } else {
+      prefix = ~0ull;  // every key is kept
+    }
+    if (tid == 0) sel[0] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += 1024) {
+      const uint64_t k = keys[i];
+      if (k <= prefix) kept_keys[atomicAdd(&sel[0], 1)] = k;
+      else slot[(int32_t)(k & 0xffffffffull)] = -1;
+    }
+    __syncthreads();
+    if (tid < kept) {
+      const uint64_t own = kept_keys[tid];
+      int r = 0;
+      for (int j = 0; j < kept; ++j) r += kept_keys[j] < own ? 1 : 0;
+      const int32_t t = (int32_t)(own & 0xffffffffull);
+      slot[t] = r;
+      token_of_slot[(int64_t)e * C + r] = t;
+    }
+    return;
+  }
   if (n <= kSegMax) {
     int P = 1;
     while (P < n) P <<= 1;
