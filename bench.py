@@ -49,12 +49,12 @@ FFN_SOURCES = ("switch_top_routed_amd/csrc/expert_ffn.hip", "switch_top_routed_a
 # profiles/*_hbm_traffic.md.
 TRAFFIC = {
     "switch-base-uniform": {
-        "sources_sha256": "676637ce338e1f42dbbf52c8a15f68b9d96daf2f225772b5c0b3c071fbbf3b19",
-        "fetch_kib": [300203.0, 309293.0], "write_kib": [24108.0, 6027.0], "fetch_scale": 2.0, "write_scale": 1.0,
+        "sources_sha256": "cf1f0b348c332771e9d6381c0b66fddbc2af1365497652d37c94cc3d215c069b",
+        "fetch_kib": [298403.0, 308676.0], "write_kib": [24108.0, 6027.0], "fetch_scale": 2.0, "write_scale": 1.0,
     },
     "switch-large-shared": {
-        "sources_sha256": "676637ce338e1f42dbbf52c8a15f68b9d96daf2f225772b5c0b3c071fbbf3b19",
-        "fetch_kib": [5720066.0, 6110001.0], "write_kib": [262144.0, 163840.0], "fetch_scale": 2.0,
+        "sources_sha256": "cf1f0b348c332771e9d6381c0b66fddbc2af1365497652d37c94cc3d215c069b",
+        "fetch_kib": [5330315.0, 5516778.0], "write_kib": [262145.0, 163841.0], "fetch_scale": 2.0,
         "write_scale": 1.0,
     },
 }
