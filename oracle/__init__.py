@@ -32,6 +32,8 @@ with its reason in the design notes):
   * argmax ties go to the lowest index; gate-descending ties to the lower
     token index; slot = priority rank.
 
+The backward pass of the layer lives in oracle/backward.py.
+
 Parity status: every function here is pinned by the CPU tests
 (brute-force evaluation, closed forms, invariants, a hand-worked example);
 none is "parity unpinned".
