@@ -1,6 +1,7 @@
 /*
- * switch_moe.h -- C ABI of a Switch top-1 mixture-of-experts layer forward
- * for AMD Instinct MI355X (gfx950), one GPU, every expert resident.
+ * switch_moe.h -- C ABI of a Switch top-1 mixture-of-experts layer (forward
+ * and backward) for AMD Instinct MI355X (gfx950), one GPU, every expert
+ * resident.
  *
  * Sources for the operations (page title, then section):
  *   [TOP1] "Top-1 Routing" concept page (compassingai.com): Core mechanism,
@@ -234,6 +235,72 @@ switch_status switch_moe_forward(const switch_moe_desc* desc, const switch_moe_i
 switch_status switch_moe_forward_timed(const switch_moe_desc* desc, const switch_moe_inputs* in,
                                        const switch_moe_outputs* out, void* ws, size_t ws_bytes, void* stream,
                                        void* const* stage_events);
+
+/* ------------------------------------------------------------------------
+ * Training: the forward that keeps what the backward needs, and the
+ * backward pass of the whole layer.
+ *
+ * The gate value multiplies the expert output, which is what lets the
+ * gradient reach the router ([SWT] Switch-layer passage); f counts argmax
+ * decisions and is not differentiable, so the auxiliary loss reaches the
+ * router through P alone ([SWT] Eq. 4 passage); the training step
+ * backpropagates into router and experts ([CAP] training-step flowchart).
+ * The argmax, the capacity ranks and the ReLU pattern are taken from the
+ * forward and are not differentiated.
+ * ---------------------------------------------------------------------- */
+typedef struct switch_moe_saved {
+  float* probs;            /* [T, N] fp32: router softmax p (required) */
+  int32_t* token_of_slot;  /* [N * C]: token in each slot, -1 if empty (required) */
+  int32_t* active;         /* [N]: experts with kept_count > 0, ascending (required) */
+  int32_t* n_active;       /* [1] (required) */
+  void* h;                 /* [N, C, d_ff] dtype: ReLU(x_t . w1[e]) of each filled
+                              slot; rows of empty slots undefined (required) */
+  void* h_shared;          /* [T, d_ff_shared] dtype: ReLU(x . ws1); required iff
+                              d_ff_shared > 0 */
+} switch_moe_saved;
+
+/* switch_moe_forward that also writes `saved` (caller-owned device buffers).
+   Every output of switch_moe_forward is bit-identical; the extra writes are
+   the softmax (T * N * 4 bytes) and the slot tables; the hidden activations
+   go to `saved` instead of the workspace.  Same workspace size. */
+switch_status switch_moe_forward_train(const switch_moe_desc* desc, const switch_moe_inputs* in,
+                                       const switch_moe_outputs* out, const switch_moe_saved* saved, void* ws,
+                                       size_t ws_bytes, void* stream);
+
+typedef struct switch_moe_grads {
+  void* dx;         /* [T, d_model] dtype (required) */
+  float* dw_gate;   /* [N, d_model] fp32 (required; the router trains in fp32) */
+  float* dbias;     /* [N] fp32, or NULL: not computed */
+  void* dw1;        /* [N, d_model, d_ff] dtype (required; zero for experts
+                       that kept no token) */
+  void* dw2;        /* [N, d_ff, d_model] dtype (required; idem) */
+  void* dws1;       /* [d_model, d_ff_shared] dtype; required iff d_ff_shared > 0 */
+  void* dws2;       /* [d_ff_shared, d_model] dtype; idem */
+} switch_moe_grads;
+
+/* Gradient of  L = sum_t <dy_t, y_t> + dl_aux * l_aux  for the forward run by
+   switch_moe_forward_train with the same desc and inputs:
+     combine  kept t:  dO_t = s_t dy_t (s_t = gate[t] with SWITCH_GATE_SCALE,
+                       else 1), dgate_t = <dy_t, O_t> (0 without the flag);
+              dropped t, and every t with SWITCH_RESIDUAL_ALL: dx_t += dy_t
+     expert e (rows X = its kept tokens, Z = X w1[e], H = ReLU(Z)):
+              dw2[e] = H^T dO;  dZ = (dO w2[e]^T) * [H > 0];  dw1[e] = X^T dZ;
+              dx_t += (dZ w1[e]^T)_t
+     router   dp_ti = [i = e_t] dgate_t + dl_aux * N * f_i / T;
+              dlogit_t = p_t * (dp_t - <p_t, dp_t>);
+              dw_gate = dlogit^T x;  dbias = sum_t dlogit_t;  dx += dlogit w_gate
+     shared   the dense FFN's three products on every token (S = ReLU(x ws1) ws2).
+   `fwd` is the forward's outputs (read: expert_id, gate, slot, kept_count,
+   f) and `saved` its saved tensors; dy [T, d_model] dtype; dl_aux: device
+   fp32 [1], or NULL for 0.  Every gradient is overwritten (not accumulated).
+   Accumulation is fp32 everywhere; bf16 gradients are rounded once, except
+   that dO = s dy and dZ are rounded to bf16 as GEMM operands.  Shape rules
+   and errors are those of switch_moe_forward; deterministic. */
+size_t switch_moe_backward_workspace_bytes(const switch_moe_desc* desc);
+switch_status switch_moe_backward(const switch_moe_desc* desc, const switch_moe_inputs* in,
+                                  const switch_moe_outputs* fwd, const switch_moe_saved* saved, const void* dy,
+                                  const float* dl_aux, const switch_moe_grads* grads, void* ws, size_t ws_bytes,
+                                  void* stream);
 
 /* Static description of a status code. */
 const char* switch_status_str(switch_status s);

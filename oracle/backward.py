@@ -39,9 +39,13 @@ in the inputs, so they are taken from the forward and not differentiated.
 ReLU at its kink.  relu'(0) is any value in [0, 1].  A GPU kernel decides
 the sign of Z from an fp32 sum whose error is bounded by a band around 0
 (2 K u sum_k |x_k W1_kf| for K products and unit roundoff u), so for a
-pre-activation inside that band either choice is a valid gradient.
-`kink_band_u` = u selects that band and `kink` in {0, 1} the value used
-inside it; kink_band_u = 0 (the default) takes the plain z > 0.
+pre-activation inside that band either choice is a valid gradient.  With
+`kink_band_u` = u the base result takes every in-band pre-activation as
+inactive, and the envelope (lo, hi) bounds, element by element, every result
+that any on/off choice inside the band gives: each in-band pair (t, f) adds
+dH_tf W1[:, f] to dx_t and x_t dH_tf to dW1[:, f] when switched on, and the
+envelope adds up the negative parts (lo) and the positive parts (hi) of those
+contributions.  kink_band_u = 0 (the default) takes the plain z > 0.
 
 Parity status: pinned by central finite differences of the forward oracle
 (every gradient), by torch autograd on the cases that reduce to library
@@ -56,15 +60,6 @@ from typing import Optional
 import numpy as np
 
 
-def relu_grad(z: np.ndarray, band: Optional[np.ndarray] = None, kink: int = 0) -> np.ndarray:
-    """relu'(z) as 0/1 floats: 1 where z > 0; inside |z| <= band the value `kink`."""
-    if band is None:
-        return (z > 0).astype(np.float64)
-    if kink:
-        return (z >= -band).astype(np.float64)
-    return (z > band).astype(np.float64)
-
-
 def sum_band(a: np.ndarray, w: np.ndarray, u: float) -> Optional[np.ndarray]:
     """Error band of a floating-point evaluation of a @ w: 2 K u (|a| @ |w|)."""
     if u <= 0:
@@ -72,19 +67,35 @@ def sum_band(a: np.ndarray, w: np.ndarray, u: float) -> Optional[np.ndarray]:
     return 2.0 * a.shape[1] * u * (np.abs(a) @ np.abs(w))
 
 
-def ffn_backward(rows: np.ndarray, d_out: np.ndarray, w1: np.ndarray, w2: np.ndarray, band_u: float = 0.0,
-                 kink: int = 0):
+def _pos(a):
+    return np.maximum(a, 0.0)
+
+
+def _neg(a):
+    return np.minimum(a, 0.0)
+
+
+def ffn_backward(rows: np.ndarray, d_out: np.ndarray, w1: np.ndarray, w2: np.ndarray, band_u: float = 0.0):
     """Backward of O = ReLU(rows W1) W2 for rows [m, d], d_out = dL/dO [m, d].
 
-    Returns (d_rows [m, d], dW1 [d, d_ff], dW2 [d_ff, d], H [m, d_ff])."""
+    Returns (d_rows [m, d], dW1 [d, d_ff], dW2 [d_ff, d], H [m, d_ff], env) where
+    env is None for band_u = 0, else {"d_rows": (lo, hi), "dw1": (lo, hi)}."""
     z = rows @ w1
     h = np.maximum(z, 0.0)
     dw2 = h.T @ d_out
     dh = d_out @ w2.T
-    dz = dh * relu_grad(z, sum_band(rows, w1, band_u), kink)
+    band = sum_band(rows, w1, band_u)
+    dz = dh * (z > (0.0 if band is None else band))
     dw1 = rows.T @ dz
     d_rows = dz @ w1.T
-    return d_rows, dw1, dw2, h
+    env = None
+    if band is not None:
+        D = dh * (np.abs(z) <= band)          # contribution of each in-band pair when switched on
+        env = {"d_rows": (d_rows + _pos(D) @ _neg(w1).T + _neg(D) @ _pos(w1).T,
+                          d_rows + _pos(D) @ _pos(w1).T + _neg(D) @ _neg(w1).T),
+               "dw1": (dw1 + _pos(rows).T @ _neg(D) + _neg(rows).T @ _pos(D),
+                       dw1 + _pos(rows).T @ _pos(D) + _neg(rows).T @ _neg(D))}
+    return d_rows, dw1, dw2, h, env
 
 
 def combine_backward(dy: np.ndarray, out: np.ndarray, expert_id: np.ndarray, slot: np.ndarray, gate: np.ndarray,
@@ -126,30 +137,45 @@ def router_backward(x: np.ndarray, w_gate: np.ndarray, p: np.ndarray, expert_id:
 
 
 def moe_backward(fwd: dict, x, w_gate, w1_of, w2_of, N: int, dy, dl_aux: float = 0.0, gate_scale: bool = True,
-                 residual_all: bool = False, ws1=None, ws2=None, kink_band_u: float = 0.0, kink: int = 0):
+                 residual_all: bool = False, ws1=None, ws2=None, kink_band_u: float = 0.0):
     """Gradient of sum_t <dy_t, y_t> + dl_aux * l_aux for the forward `fwd` (the dict
     of oracle.moe_forward on the same fp64 x and weights).
 
     Returns a dict: dx [T, d], dw_gate [N, d], dbias [N], dw1 [N, d, d_ff],
-    dw2 [N, d_ff, d], dws1 / dws2 (or None), dg [T], dlogits [T, N]."""
+    dw2 [N, d_ff, d], dws1 / dws2 (or None), dg [T], dlogits [T, N]; with
+    kink_band_u > 0 also the envelopes dx_env, dw1_env, dws1_env as (lo, hi)."""
     T, d = x.shape
     e, slot, g = fwd["expert_id"], fwd["slot"], fwd["gate"]
     d_out, dg, dx = combine_backward(dy, fwd["out"], e, slot, g, gate_scale, residual_all)
     dff = w1_of(0).shape[1]
     dw1 = np.zeros((N, d, dff))
     dw2 = np.zeros((N, dff, d))
+    band = kink_band_u > 0
+    dx_lo, dx_hi = np.zeros((T, d)), np.zeros((T, d))      # envelope offsets
+    dw1_lo, dw1_hi = (np.zeros((N, d, dff)), np.zeros((N, d, dff))) if band else (None, None)
     tos, kept = fwd["token_of_slot"], fwd["kept_count"]
     for i in range(N):
         k = int(kept[i])
         if k == 0:
             continue
         toks = tos[i, :k]
-        d_rows, dw1[i], dw2[i], _ = ffn_backward(x[toks], d_out[i, :k], w1_of(i), w2_of(i), kink_band_u, kink)
+        d_rows, dw1[i], dw2[i], _, env = ffn_backward(x[toks], d_out[i, :k], w1_of(i), w2_of(i), kink_band_u)
         dx[toks] += d_rows
-    dws1 = dws2 = None
+        if band:
+            dx_lo[toks] += env["d_rows"][0] - d_rows
+            dx_hi[toks] += env["d_rows"][1] - d_rows
+            dw1_lo[i], dw1_hi[i] = env["dw1"]
+    dws1 = dws2 = dws1_env = None
     if ws1 is not None:
-        d_rows, dws1, dws2, _ = ffn_backward(x, dy, ws1, ws2, kink_band_u, kink)
+        d_rows, dws1, dws2, _, env = ffn_backward(x, dy, ws1, ws2, kink_band_u)
         dx += d_rows
+        if band:
+            dx_lo += env["d_rows"][0] - d_rows
+            dx_hi += env["d_rows"][1] - d_rows
+            dws1_env = env["dw1"]
     dlogits, dwg, db, dx_r = router_backward(x, w_gate, fwd["p"], e, dg, fwd["f"], dl_aux)
     dx += dx_r
-    return dict(dx=dx, dw_gate=dwg, dbias=db, dw1=dw1, dw2=dw2, dws1=dws1, dws2=dws2, dg=dg, dlogits=dlogits)
+    out = dict(dx=dx, dw_gate=dwg, dbias=db, dw1=dw1, dw2=dw2, dws1=dws1, dws2=dws2, dg=dg, dlogits=dlogits)
+    if band:
+        out.update(dx_env=(dx + dx_lo, dx + dx_hi), dw1_env=(dw1_lo, dw1_hi), dws1_env=dws1_env)
+    return out

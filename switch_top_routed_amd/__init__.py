@@ -1,4 +1,4 @@
-"""Switch top-1 mixture-of-experts layer forward for AMD Instinct MI355X (gfx950).
+"""Switch top-1 mixture-of-experts layer (forward and backward) for AMD Instinct MI355X (gfx950).
 
 The computation lives in libswitch_moe.so (hand-written HIP kernels behind the
 C ABI of include/switch_moe.h); this package only builds and binds it.
@@ -6,5 +6,6 @@ C ABI of include/switch_moe.h); this package only builds and binds it.
 from .native import (  # noqa: F401
     BF16, F32, GATE_DESC, GATE_SCALE, RESIDUAL_ALL, TOKEN_ORDER, StageEvents, SwitchError, SwitchMoE, lib,
     switch_assign_capacity,
-    switch_capacity, switch_combine, switch_dispatch, switch_expert_ffn, switch_moe_forward, switch_route,
+    switch_capacity, switch_combine, switch_dispatch, switch_expert_ffn, switch_moe_backward, switch_moe_forward,
+    switch_moe_forward_train, switch_route,
 )

@@ -286,6 +286,56 @@ switch_status validate_desc(const switch_moe_desc* d, int32_t* C) {
   return SWITCH_OK;
 }
 
+switch_status validate_saved(const switch_moe_desc& d, const switch_moe_saved* sv) {
+  REQUIRE_PTR(sv->probs);
+  REQUIRE_PTR(sv->token_of_slot);
+  REQUIRE_PTR(sv->active);
+  REQUIRE_PTR(sv->n_active);
+  REQUIRE_PTR(sv->h);
+  REQUIRE_ALIGN(sv->probs, 4);
+  REQUIRE_ALIGN(sv->token_of_slot, 4);
+  REQUIRE_ALIGN(sv->active, 4);
+  REQUIRE_ALIGN(sv->n_active, 4);
+  REQUIRE_ALIGN(sv->h, 16);
+  if (d.d_ff_shared > 0) {
+    REQUIRE_PTR(sv->h_shared);
+    REQUIRE_ALIGN(sv->h_shared, 16);
+  }
+  return SWITCH_OK;
+}
+
+// ---------------------------------------------------------------------------
+// backward workspace layout
+// ---------------------------------------------------------------------------
+struct BwdLayout {
+  size_t off_u, off_dz, off_dg, off_dxe, off_dlogit, off_colsum, off_dense, off_us, off_dzs, off_dxs, bytes;
+};
+
+BwdLayout bwd_layout(const switch_moe_desc& d, int32_t C) {
+  BwdLayout L{};
+  const size_t esz = d.dtype == SWITCH_BF16 ? 2 : 4;
+  const size_t NC = (size_t)d.N * C;
+  size_t off = 0;
+  auto take = [&](size_t& at, size_t bytes) {
+    at = off;
+    off = align_up(off + bytes);
+  };
+  take(L.off_u, NC * d.d_ff * 4);
+  take(L.off_dz, NC * d.d_ff * esz);
+  take(L.off_dg, NC * 4);
+  take(L.off_dxe, NC * d.d_model * 4);
+  take(L.off_dlogit, (size_t)d.T * d.N * 4);
+  take(L.off_colsum, colsum_scratch_bytes(d.T, d.N));
+  if (d.d_ff_shared > 0) {
+    take(L.off_dense, 3 * 4);
+    take(L.off_us, (size_t)d.T * d.d_ff_shared * 4);
+    take(L.off_dzs, (size_t)d.T * d.d_ff_shared * esz);
+    take(L.off_dxs, (size_t)d.T * d.d_model * 4);
+  }
+  L.bytes = off;
+  return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -382,7 +432,7 @@ size_t switch_moe_workspace_bytes(const switch_moe_desc* desc) {
 // The whole layer; `ev` (7 events or NULL) marks the stage boundaries on the stream.
 static switch_status moe_forward(const switch_moe_desc* desc, const switch_moe_inputs* in,
                                  const switch_moe_outputs* out, void* ws, size_t ws_bytes, void* stream,
-                                 void* const* ev) {
+                                 void* const* ev, const switch_moe_saved* sv = nullptr) {
   int32_t C = 0;
   TRY(validate_desc(desc, &C));
   if (in == nullptr) return fail(SWITCH_E_NULL, "inputs is NULL");
@@ -405,13 +455,16 @@ static switch_status moe_forward(const switch_moe_desc* desc, const switch_moe_i
     REQUIRE_ALIGN(in->ws1, 16);
     REQUIRE_ALIGN(in->ws2, 16);
   }
+  if (sv != nullptr) TRY(validate_saved(d, sv));
   const FwdLayout L = fwd_layout(d, C);
   TRY(check_ws(ws, ws_bytes, L.bytes));
   char* w = static_cast<char*>(ws);
   hipStream_t st = as_stream(stream);
-  int32_t* tos = reinterpret_cast<int32_t*>(w + L.off_tos);
-  int32_t* active = reinterpret_cast<int32_t*>(w + L.off_active);
-  int32_t* nact = reinterpret_cast<int32_t*>(w + L.off_nact);
+  int32_t* tos = sv != nullptr ? sv->token_of_slot : reinterpret_cast<int32_t*>(w + L.off_tos);
+  int32_t* active = sv != nullptr ? sv->active : reinterpret_cast<int32_t*>(w + L.off_active);
+  int32_t* nact = sv != nullptr ? sv->n_active : reinterpret_cast<int32_t*>(w + L.off_nact);
+  float* probs = sv != nullptr ? sv->probs : nullptr;
+  void* h_save = sv != nullptr ? sv->h : nullptr;
   void* xin = w + L.off_xin;
   void* xout = w + L.off_xout;
   auto mark = [&](int i) -> hipError_t {
@@ -422,7 +475,7 @@ static switch_status moe_forward(const switch_moe_desc* desc, const switch_moe_i
   if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
   int32_t* rank = L.fused ? reinterpret_cast<int32_t*>(w + L.off_rank) : nullptr;
   e = launch_route(L.route, in->x, in->w_gate, in->bias, d.T, d.d_model, d.N, d.dtype, out->expert_id, out->gate,
-                   out->routed_count, out->f, out->P, out->l_aux, w + L.off_route, st, rank);
+                   out->routed_count, out->f, out->P, out->l_aux, w + L.off_route, st, rank, probs);
   if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/route");
   if ((e = mark(1)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
   if (L.fused) {
@@ -436,7 +489,7 @@ static switch_status moe_forward(const switch_moe_desc* desc, const switch_moe_i
     if ((e = mark(2)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
     if ((e = mark(3)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
     e = launch_ffn(L.ffn, in->x, in->w1, in->w2, d.dtype, d.N, C, d.d_model, d.d_ff, out->kept_count, active, nact,
-                   xout, w + L.off_ffn, st, tos, d.T);
+                   xout, w + L.off_ffn, st, tos, d.T, h_save);
   } else {
     e = launch_assign(L.assign, out->expert_id, out->gate, d.T, d.N, C, d.priority, out->slot, tos, out->kept_count,
                       out->n_dropped, active, nact, w + L.off_assign, st);
@@ -446,7 +499,7 @@ static switch_status moe_forward(const switch_moe_desc* desc, const switch_moe_i
     if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/dispatch");
     if ((e = mark(3)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
     e = launch_ffn(L.ffn, xin, in->w1, in->w2, d.dtype, d.N, C, d.d_model, d.d_ff, out->kept_count, active, nact,
-                   xout, w + L.off_ffn, st);
+                   xout, w + L.off_ffn, st, nullptr, 0, h_save);
   }
   if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/expert_ffn");
   if ((e = mark(4)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
@@ -457,7 +510,7 @@ static switch_status moe_forward(const switch_moe_desc* desc, const switch_moe_i
     if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/shared_plan");
     sout = w + L.off_sout;
     e = launch_ffn(L.sffn, in->x, in->ws1, in->ws2, d.dtype, 1, (int)d.T, d.d_model, d.d_ff_shared, dk, dk + 1,
-                   dk + 2, sout, w + L.off_sffn, st);
+                   dk + 2, sout, w + L.off_sffn, st, nullptr, 0, sv != nullptr ? sv->h_shared : nullptr);
     if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/shared_ffn");
   }
   if ((e = mark(5)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
@@ -480,6 +533,150 @@ switch_status switch_moe_forward_timed(const switch_moe_desc* desc, const switch
                                        void* const* stage_events) {
   if (stage_events == nullptr) return fail(SWITCH_E_NULL, "stage_events is NULL");
   return moe_forward(desc, in, out, ws, ws_bytes, stream, stage_events);
+}
+
+switch_status switch_moe_forward_train(const switch_moe_desc* desc, const switch_moe_inputs* in,
+                                       const switch_moe_outputs* out, const switch_moe_saved* saved, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  if (saved == nullptr) return fail(SWITCH_E_NULL, "saved is NULL");
+  return moe_forward(desc, in, out, ws, ws_bytes, stream, nullptr, saved);
+}
+
+size_t switch_moe_backward_workspace_bytes(const switch_moe_desc* desc) {
+  int32_t C = 0;
+  if (validate_desc(desc, &C) != SWITCH_OK) return 0;
+  return bwd_layout(*desc, C).bytes;
+}
+
+switch_status switch_moe_backward(const switch_moe_desc* desc, const switch_moe_inputs* in,
+                                  const switch_moe_outputs* fwd, const switch_moe_saved* saved, const void* dy,
+                                  const float* dl_aux, const switch_moe_grads* grads, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  int32_t C = 0;
+  TRY(validate_desc(desc, &C));
+  if (in == nullptr) return fail(SWITCH_E_NULL, "inputs is NULL");
+  if (fwd == nullptr) return fail(SWITCH_E_NULL, "fwd is NULL");
+  if (saved == nullptr) return fail(SWITCH_E_NULL, "saved is NULL");
+  if (grads == nullptr) return fail(SWITCH_E_NULL, "grads is NULL");
+  const switch_moe_desc& d = *desc;
+  const bool gate_scale = (d.flags & SWITCH_GATE_SCALE) != 0;
+  REQUIRE_PTR(in->x);
+  REQUIRE_PTR(in->w_gate);
+  REQUIRE_PTR(in->w1);
+  REQUIRE_PTR(in->w2);
+  REQUIRE_ALIGN(in->x, 16);
+  REQUIRE_ALIGN(in->w_gate, 16);
+  REQUIRE_ALIGN(in->w1, 16);
+  REQUIRE_ALIGN(in->w2, 16);
+  REQUIRE_PTR(fwd->expert_id);
+  REQUIRE_PTR(fwd->slot);
+  REQUIRE_PTR(fwd->kept_count);
+  REQUIRE_PTR(fwd->f);
+  if (gate_scale) REQUIRE_PTR(fwd->gate);
+  TRY(validate_saved(d, saved));
+  REQUIRE_PTR(dy);
+  REQUIRE_ALIGN(dy, 16);
+  REQUIRE_PTR(grads->dx);
+  REQUIRE_PTR(grads->dw_gate);
+  REQUIRE_PTR(grads->dw1);
+  REQUIRE_PTR(grads->dw2);
+  REQUIRE_ALIGN(grads->dx, 16);
+  REQUIRE_ALIGN(grads->dw_gate, 16);
+  REQUIRE_ALIGN(grads->dw1, 16);
+  REQUIRE_ALIGN(grads->dw2, 16);
+  if (grads->dbias) REQUIRE_ALIGN(grads->dbias, 4);
+  if (d.d_ff_shared > 0) {
+    REQUIRE_PTR(in->ws1);
+    REQUIRE_PTR(in->ws2);
+    REQUIRE_PTR(grads->dws1);
+    REQUIRE_PTR(grads->dws2);
+    REQUIRE_ALIGN(grads->dws1, 16);
+    REQUIRE_ALIGN(grads->dws2, 16);
+  }
+  const BwdLayout L = bwd_layout(d, C);
+  TRY(check_ws(ws, ws_bytes, L.bytes));
+  char* w = static_cast<char*>(ws);
+  hipStream_t st = as_stream(stream);
+  const int dt = d.dtype, dm = d.d_model, dff = d.d_ff, N = d.N;
+  const int64_t T = d.T;
+  const int32_t* kept = fwd->kept_count;
+  const int32_t* tos = saved->token_of_slot;
+  float* U = reinterpret_cast<float*>(w + L.off_u);
+  void* dZ = w + L.off_dz;
+  float* dg = gate_scale ? reinterpret_cast<float*>(w + L.off_dg) : nullptr;
+  float* dxe = reinterpret_cast<float*>(w + L.off_dxe);
+  float* dlogit = reinterpret_cast<float*>(w + L.off_dlogit);
+  const float* gsc = gate_scale ? fwd->gate : nullptr;
+  hipError_t e;
+#define BWD_TRY(expr, what)                                    \
+  do {                                                         \
+    if ((e = (expr)) != hipSuccess) return hip_fail(e, what);  \
+  } while (0)
+  // routed experts.  U = dY W2^T over each expert's kept tokens
+  BWD_TRY(launch_gemm_generic(GemmOperand{dy, dm, 0, tos, nullptr, 0}, 0,
+                              GemmOperand{in->w2, dm, (int64_t)dff * dm, nullptr, nullptr, 1},
+                              GemmOut{U, dff, (int64_t)C * dff}, 1, dt, N, C, dff, dm, C, kept, 1, st),
+          "switch_moe_backward/U");
+  // dZ = s U [H > 0], dg = <U, H>
+  BWD_TRY(launch_dz_rows(U, saved->h, dZ, dg, kept, tos, gsc, N, C, dff, dt, st), "switch_moe_backward/dZ");
+  // dW2 = H^T (s dY)
+  BWD_TRY(launch_gemm_generic(GemmOperand{saved->h, dff, (int64_t)C * dff, nullptr, nullptr, 1}, 0,
+                              GemmOperand{dy, dm, 0, tos, gsc, 0}, GemmOut{grads->dw2, dm, (int64_t)dff * dm}, 0, dt,
+                              N, dff, dm, C, C, kept, 2, st),
+          "switch_moe_backward/dW2");
+  // dW1 = X^T dZ
+  BWD_TRY(launch_gemm_generic(GemmOperand{in->x, dm, 0, tos, nullptr, 1}, 0,
+                              GemmOperand{dZ, dff, (int64_t)C * dff, nullptr, nullptr, 0},
+                              GemmOut{grads->dw1, dff, (int64_t)dm * dff}, 0, dt, N, dm, dff, C, C, kept, 2, st),
+          "switch_moe_backward/dW1");
+  // dX_e = dZ W1^T
+  BWD_TRY(launch_gemm_generic(GemmOperand{dZ, dff, (int64_t)C * dff, nullptr, nullptr, 0}, 0,
+                              GemmOperand{in->w1, dff, (int64_t)dm * dff, nullptr, nullptr, 1},
+                              GemmOut{dxe, dm, (int64_t)C * dm}, 1, dt, N, C, dm, dff, C, kept, 1, st),
+          "switch_moe_backward/dX");
+  // shared dense expert on every token
+  float* dxs = nullptr;
+  if (d.d_ff_shared > 0) {
+    const int dfs = d.d_ff_shared;
+    int32_t* dk = reinterpret_cast<int32_t*>(w + L.off_dense);
+    float* Us = reinterpret_cast<float*>(w + L.off_us);
+    void* dZs = w + L.off_dzs;
+    dxs = reinterpret_cast<float*>(w + L.off_dxs);
+    BWD_TRY(launch_dense_plan(dk, dk + 1, dk + 2, (int32_t)T, st), "switch_moe_backward/shared_plan");
+    BWD_TRY(launch_gemm_generic(GemmOperand{dy, dm, 0, nullptr, nullptr, 0}, 0,
+                                GemmOperand{in->ws2, dm, 0, nullptr, nullptr, 1}, GemmOut{Us, dfs, 0}, 1, dt, 1,
+                                (int)T, dfs, dm, (int)T, nullptr, 0, st),
+            "switch_moe_backward/shared_U");
+    BWD_TRY(launch_dz_rows(Us, saved->h_shared, dZs, nullptr, dk, nullptr, nullptr, 1, (int)T, dfs, dt, st),
+            "switch_moe_backward/shared_dZ");
+    BWD_TRY(launch_gemm_generic(GemmOperand{saved->h_shared, dfs, 0, nullptr, nullptr, 1}, 0,
+                                GemmOperand{dy, dm, 0, nullptr, nullptr, 0}, GemmOut{grads->dws2, dm, 0}, 0, dt, 1,
+                                dfs, dm, (int)T, (int)T, nullptr, 0, st),
+            "switch_moe_backward/shared_dW2");
+    BWD_TRY(launch_gemm_generic(GemmOperand{in->x, dm, 0, nullptr, nullptr, 1}, 0,
+                                GemmOperand{dZs, dfs, 0, nullptr, nullptr, 0}, GemmOut{grads->dws1, dfs, 0}, 0, dt, 1,
+                                dm, dfs, (int)T, (int)T, nullptr, 0, st),
+            "switch_moe_backward/shared_dW1");
+    BWD_TRY(launch_gemm_generic(GemmOperand{dZs, dfs, 0, nullptr, nullptr, 0}, 0,
+                                GemmOperand{in->ws1, dfs, 0, nullptr, nullptr, 1}, GemmOut{dxs, dm, 0}, 1, dt, 1,
+                                (int)T, dm, dfs, (int)T, nullptr, 0, st),
+            "switch_moe_backward/shared_dX");
+  }
+  // router: softmax gradient, dW_g = dlogit^T x, db, and dx
+  BWD_TRY(launch_router_grad(saved->probs, fwd->expert_id, fwd->slot, dg, fwd->f, dl_aux, T, N, C, dlogit, st),
+          "switch_moe_backward/router");
+  BWD_TRY(launch_gemm_generic(GemmOperand{dlogit, N, 0, nullptr, nullptr, 1}, 1,
+                              GemmOperand{in->x, dm, 0, nullptr, nullptr, 0}, GemmOut{grads->dw_gate, dm, 0}, 1, dt, 1,
+                              N, dm, (int)T, (int)T, nullptr, 0, st),
+          "switch_moe_backward/dW_g");
+  if (grads->dbias != nullptr)
+    BWD_TRY(launch_colsum(dlogit, T, N, reinterpret_cast<float*>(w + L.off_colsum), grads->dbias, st),
+            "switch_moe_backward/db");
+  BWD_TRY(launch_dx_assemble(dlogit, in->w_gate, dxe, dy, dxs, fwd->expert_id, fwd->slot, T, dm, N, C,
+                             (d.flags & SWITCH_RESIDUAL_ALL) != 0, grads->dx, dt, st),
+          "switch_moe_backward/dx");
+#undef BWD_TRY
+  return ok();
 }
 
 const char* switch_status_str(switch_status s) {

@@ -21,9 +21,11 @@ RoutePlan route_plan(int64_t T, int d, int N, int dtype);
 // local_rank == NULL: statistics (routed_count, f, P, l_aux) by a final reduction
 // kernel; else every token's rank inside its tile is written and the statistics
 // are left to launch_route_assign_token
+// probs != NULL: the softmax of every token is written too ([T, N] fp32)
 hipError_t launch_route(const RoutePlan& pl, const void* x, const void* wg, const float* bias, int64_t T, int d, int N,
                         int dtype, int32_t* expert_id, float* gate, int32_t* routed_count, float* f, float* P,
-                        float* l_aux, char* ws, hipStream_t st, int32_t* local_rank = nullptr);
+                        float* l_aux, char* ws, hipStream_t st, int32_t* local_rank = nullptr,
+                        float* probs = nullptr);
 // token-order slots from the router's tiles (after launch_route with local_rank);
 // off: int32 [nblk x N] scratch
 hipError_t launch_route_assign_token(const RoutePlan& pl, int64_t T, int N, int C, const int32_t* expert_id,
@@ -60,9 +62,12 @@ FfnPlan ffn_plan(int N, int C, int d, int dff, int dtype);
 // two launches of one kernel (phase 1: H = ReLU(X W1), phase 2: Y = H W2).
 // gather != NULL: xin is the token matrix [a_rows, d] and row r of expert e is
 // token gather[e * C + r] (token_of_slot), so no dispatched copy is needed.
+// h_out != NULL: the hidden activation [N, C, dff] goes there instead of the
+// workspace (kept for the backward pass).
 hipError_t launch_ffn(const FfnPlan& pl, const void* xin, const void* w1, const void* w2, int dtype, int N, int C, int d,
                       int dff, const int32_t* kept_count, const int32_t* active, const int32_t* n_active, void* xout,
-                      char* ws, hipStream_t st, const int32_t* gather = nullptr, int64_t a_rows = 0);
+                      char* ws, hipStream_t st, const int32_t* gather = nullptr, int64_t a_rows = 0,
+                      void* h_out = nullptr);
 // writes {M}, {0}, {1} for the dense (shared-expert) FFN
 // LDS-tiled MFMA GEMM (direct global-to-LDS loads, transposing LDS reads) for
 // experts with more than 64 rows and the dense shared FFN
@@ -71,6 +76,37 @@ hipError_t launch_tiled_dma(const void* A, const void* W, void* out, const int32
                             const int32_t* n_active, int N, int C, int K, int Ncols, int relu, hipStream_t st,
                             const int32_t* gather = nullptr, int64_t a_rows = 0);
 hipError_t launch_dense_plan(int32_t* kept, int32_t* active, int32_t* n_active, int32_t M, hipStream_t st);
+
+// ---------------- backward ----------------
+// operand of the generic GEMM: element (i, j) of batch b is
+// ptr[(gather ? gather[b * C + i] : b * bstride-offset + i) * ld + j], times
+// row_scale[physical row] when row_scale != NULL; trans swaps the roles of
+// (i, j) (see gemm_generic)
+struct GemmOperand {
+  const void* ptr;
+  int64_t ld, bstride;
+  const int32_t* gather;
+  const float* row_scale;
+  int trans;
+};
+struct GemmOut {
+  void* ptr;
+  int64_t ld, bstride;
+};
+// extent: 0 fixed sizes, 1 rows M_b = min(kept[b], C), 2 reduction K_b = min(kept[b], C)
+hipError_t launch_gemm_generic(const GemmOperand& a, int a_f32, const GemmOperand& b, const GemmOut& o, int o_f32,
+                               int dtype, int batches, int M, int Nn, int K, int C, const int32_t* kept, int extent,
+                               hipStream_t st);
+hipError_t launch_dz_rows(const float* U, const void* H, void* dZ, float* dg, const int32_t* kept,
+                          const int32_t* tos, const float* gate, int N, int C, int dff, int dtype, hipStream_t st);
+hipError_t launch_router_grad(const float* probs, const int32_t* eid, const int32_t* slot, const float* dg,
+                              const float* f, const float* dl_aux, int64_t T, int N, int C, float* dlogit,
+                              hipStream_t st);
+size_t colsum_scratch_bytes(int64_t T, int N);
+hipError_t launch_colsum(const float* a, int64_t T, int N, float* scratch, float* out, hipStream_t st);
+hipError_t launch_dx_assemble(const float* dlogit, const void* wg, const float* dxe, const void* dy, const float* dxs,
+                              const int32_t* eid, const int32_t* slot, int64_t T, int d, int N, int C,
+                              int residual_all, void* dx, int dtype, hipStream_t st);
 
 inline size_t align_up(size_t v, size_t a = 256) { return (v + a - 1) / a * a; }
 

@@ -39,7 +39,7 @@ template <int J>
 __device__ void route_epilogue(float* lg, int ldl, int rows, int64_t t0, int64_t T, int N,
                                const float* __restrict__ bias, int32_t* __restrict__ expert_id,
                                float* __restrict__ gate, float* __restrict__ part_p, int32_t* __restrict__ part_cnt,
-                               int32_t* __restrict__ local_rank, int64_t blk) {
+                               int32_t* __restrict__ local_rank, int64_t blk, float* __restrict__ probs) {
   __shared__ int tile_e[64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   float bs[J], ps[J];
@@ -81,6 +81,7 @@ __device__ void route_epilogue(float* lg, int ldl, int rows, int64_t t0, int64_t
       const int n = lane + 64 * j;
       ps[j] += v[j] * inv;
       cn[j] += (n == bi) ? 1 : 0;
+      if (probs != nullptr && n < N) probs[t * N + n] = v[j] * inv;
     }
     if (lane == 0) {
       expert_id[t] = bi;
@@ -121,7 +122,7 @@ template <int TM, int NG, int J>
 __global__ __launch_bounds__(kRouteThreads) void route_fused_bf16(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg, const float* __restrict__ bias, int64_t T, int d,
     int N, int32_t* __restrict__ expert_id, float* __restrict__ gate, float* __restrict__ part_p,
-    int32_t* __restrict__ part_cnt, int32_t* __restrict__ local_rank) {
+    int32_t* __restrict__ part_cnt, int32_t* __restrict__ local_rank, float* __restrict__ probs) {
   extern __shared__ float smem[];
   const int NT = (N + 15) >> 4;
   const int ldl = NT * 16;
@@ -197,7 +198,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_fused_bf16(
       }
   }
   __syncthreads();
-  route_epilogue<J>(lg, ldl, TM * 16, t0, T, N, bias, expert_id, gate, part_p, part_cnt, local_rank, blockIdx.x);
+  route_epilogue<J>(lg, ldl, TM * 16, t0, T, N, bias, expert_id, gate, part_p, part_cnt, local_rank, blockIdx.x, probs);
 }
 
 // ----------------------------------------------------------------------------
@@ -259,7 +260,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_softmax_split(const float
                                                                      float* __restrict__ gate,
                                                                      float* __restrict__ part_p,
                                                                      int32_t* __restrict__ part_cnt,
-                                                                     int32_t* __restrict__ local_rank) {
+                                                                     int32_t* __restrict__ local_rank, float* __restrict__ probs) {
   // one token per workgroup: its N logits are sums over the S k-chunks, in
   // chunk order, with 8 independent loads in flight per expert
   extern __shared__ float smem[];
@@ -281,7 +282,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_softmax_split(const float
     lg[n] = v;
   }
   __syncthreads();
-  route_epilogue<J>(lg, N, 1, t, T, N, bias, expert_id, gate, part_p, part_cnt, local_rank, blockIdx.x);
+  route_epilogue<J>(lg, N, 1, t, T, N, bias, expert_id, gate, part_p, part_cnt, local_rank, blockIdx.x, probs);
 }
 
 // ----------------------------------------------------------------------------
@@ -293,7 +294,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_f32(const float* __restri
                                                            int32_t* __restrict__ expert_id, float* __restrict__ gate,
                                                            float* __restrict__ part_p,
                                                            int32_t* __restrict__ part_cnt,
-                                                           int32_t* __restrict__ local_rank) {
+                                                           int32_t* __restrict__ local_rank, float* __restrict__ probs) {
   extern __shared__ float smem[];
   const int ldl = N;
   float* lg = smem;
@@ -310,7 +311,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_f32(const float* __restri
     lg[m * ldl + n] = acc;
   }
   __syncthreads();
-  route_epilogue<J>(lg, ldl, 16, t0, T, N, bias, expert_id, gate, part_p, part_cnt, local_rank, blockIdx.x);
+  route_epilogue<J>(lg, ldl, 16, t0, T, N, bias, expert_id, gate, part_p, part_cnt, local_rank, blockIdx.x, probs);
 }
 
 // ----------------------------------------------------------------------------
@@ -526,7 +527,7 @@ RoutePlan route_plan(int64_t T, int d, int N, int dtype) {
 template <int J>
 static hipError_t launch_route_j(const RoutePlan& pl, const void* x, const void* wg, const float* bias, int64_t T,
                                  int d, int N, int dtype, int32_t* expert_id, float* gate, float* part_p,
-                                 int32_t* part_cnt, int32_t* local_rank, char* ws, hipStream_t st) {
+                                 int32_t* part_cnt, int32_t* local_rank, char* ws, hipStream_t st, float* probs) {
   if (dtype == 1 && pl.split == 0) {
     const int NT = (N + 15) / 16;
     const size_t lds = (size_t)pl.tm * 16 * NT * 16 * 4;
@@ -535,13 +536,13 @@ static hipError_t launch_route_j(const RoutePlan& pl, const void* x, const void*
     auto* wb = static_cast<const uint16_t*>(wg);
     if (pl.tm == 4)
       hipLaunchKernelGGL((route_fused_bf16<4, 2, J>), grid, dim3(kRouteThreads), lds, st, xb, wb, bias, T, d, N,
-                         expert_id, gate, part_p, part_cnt, local_rank);
+                         expert_id, gate, part_p, part_cnt, local_rank, probs);
     else if (pl.tm == 2)
       hipLaunchKernelGGL((route_fused_bf16<2, 2, J>), grid, dim3(kRouteThreads), lds, st, xb, wb, bias, T, d, N,
-                         expert_id, gate, part_p, part_cnt, local_rank);
+                         expert_id, gate, part_p, part_cnt, local_rank, probs);
     else
       hipLaunchKernelGGL((route_fused_bf16<1, 2, J>), grid, dim3(kRouteThreads), lds, st, xb, wb, bias, T, d, N,
-                         expert_id, gate, part_p, part_cnt, local_rank);
+                         expert_id, gate, part_p, part_cnt, local_rank, probs);
   } else if (dtype == 1) {
     float* plog = reinterpret_cast<float*>(ws + pl.off_logits);
     hipLaunchKernelGGL((route_logits_split_bf16<2>), dim3((unsigned)((T + 15) / 16), (unsigned)pl.split), dim3(kRouteThreads),
@@ -551,28 +552,28 @@ static hipError_t launch_route_j(const RoutePlan& pl, const void* x, const void*
     if (e != hipSuccess) return e;
     const size_t lds = (size_t)8 * N * 4;  // the epilogue reuses it for the cross-wave partials
     hipLaunchKernelGGL(route_softmax_split<J>, dim3((unsigned)pl.nblk), dim3(kRouteThreads), lds, st, plog, pl.split,
-                       T, N, bias, expert_id, gate, part_p, part_cnt, local_rank);
+                       T, N, bias, expert_id, gate, part_p, part_cnt, local_rank, probs);
   } else {
     const size_t lds = (size_t)16 * N * 4;
     hipLaunchKernelGGL(route_f32<J>, dim3((unsigned)pl.nblk), dim3(kRouteThreads), lds, st,
                        static_cast<const float*>(x), static_cast<const float*>(wg), bias, T, d, N, expert_id, gate,
-                       part_p, part_cnt, local_rank);
+                       part_p, part_cnt, local_rank, probs);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_route(const RoutePlan& pl, const void* x, const void* wg, const float* bias, int64_t T, int d, int N,
                         int dtype, int32_t* expert_id, float* gate, int32_t* routed_count, float* f, float* P,
-                        float* l_aux, char* ws, hipStream_t st, int32_t* local_rank) {
+                        float* l_aux, char* ws, hipStream_t st, int32_t* local_rank, float* probs) {
   float* part_p = reinterpret_cast<float*>(ws + pl.off_part_p);
   int32_t* part_cnt = reinterpret_cast<int32_t*>(ws + pl.off_part_cnt);
   hipError_t e;
   if (N <= 128)
-    e = launch_route_j<2>(pl, x, wg, bias, T, d, N, dtype, expert_id, gate, part_p, part_cnt, local_rank, ws, st);
+    e = launch_route_j<2>(pl, x, wg, bias, T, d, N, dtype, expert_id, gate, part_p, part_cnt, local_rank, ws, st, probs);
   else if (N <= 512)
-    e = launch_route_j<8>(pl, x, wg, bias, T, d, N, dtype, expert_id, gate, part_p, part_cnt, local_rank, ws, st);
+    e = launch_route_j<8>(pl, x, wg, bias, T, d, N, dtype, expert_id, gate, part_p, part_cnt, local_rank, ws, st, probs);
   else
-    e = launch_route_j<16>(pl, x, wg, bias, T, d, N, dtype, expert_id, gate, part_p, part_cnt, local_rank, ws, st);
+    e = launch_route_j<16>(pl, x, wg, bias, T, d, N, dtype, expert_id, gate, part_p, part_cnt, local_rank, ws, st, probs);
   if (e != hipSuccess) return e;
   if (local_rank != nullptr) return hipSuccess;  // the statistics come from launch_route_assign_token
   const int NP = (N + 63) / 64 * 64;

@@ -44,6 +44,16 @@ class SwitchMoeOutputs(ctypes.Structure):
                 ("kept_count", _vp), ("n_dropped", _vp), ("f", _vp), ("P", _vp), ("l_aux", _vp)]
 
 
+class SwitchMoeSaved(ctypes.Structure):
+    _fields_ = [("probs", _vp), ("token_of_slot", _vp), ("active", _vp), ("n_active", _vp), ("h", _vp),
+                ("h_shared", _vp)]
+
+
+class SwitchMoeGrads(ctypes.Structure):
+    _fields_ = [("dx", _vp), ("dw_gate", _vp), ("dbias", _vp), ("dw1", _vp), ("dw2", _vp), ("dws1", _vp),
+                ("dws2", _vp)]
+
+
 _SIGS = {
     "switch_capacity": (_i32, [_i64, _i32, _f64]),
     "switch_route_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32]),
@@ -59,6 +69,13 @@ _SIGS = {
                                   ctypes.POINTER(SwitchMoeOutputs), _vp, _sz, _vp]),
     "switch_moe_forward_timed": (_i32, [ctypes.POINTER(SwitchMoeDesc), ctypes.POINTER(SwitchMoeInputs),
                                         ctypes.POINTER(SwitchMoeOutputs), _vp, _sz, _vp, ctypes.POINTER(_vp)]),
+    "switch_moe_forward_train": (_i32, [ctypes.POINTER(SwitchMoeDesc), ctypes.POINTER(SwitchMoeInputs),
+                                        ctypes.POINTER(SwitchMoeOutputs), ctypes.POINTER(SwitchMoeSaved), _vp, _sz,
+                                        _vp]),
+    "switch_moe_backward_workspace_bytes": (_sz, [ctypes.POINTER(SwitchMoeDesc)]),
+    "switch_moe_backward": (_i32, [ctypes.POINTER(SwitchMoeDesc), ctypes.POINTER(SwitchMoeInputs),
+                                   ctypes.POINTER(SwitchMoeOutputs), ctypes.POINTER(SwitchMoeSaved), _vp, _vp,
+                                   ctypes.POINTER(SwitchMoeGrads), _vp, _sz, _vp]),
     "switch_status_str": (ctypes.c_char_p, [_i32]),
     "switch_last_error": (ctypes.c_char_p, []),
 }
@@ -275,7 +292,7 @@ class SwitchMoE:
     """The whole layer with its outputs and workspace preallocated (one call = switch_moe_forward)."""
 
     def __init__(self, T, d_model, d_ff, N, *, dtype=torch.bfloat16, capacity_factor=1.0, C=0, priority="token",
-                 gate_scale=True, residual_all=False, d_ff_shared=0, device="cuda"):
+                 gate_scale=True, residual_all=False, d_ff_shared=0, device="cuda", train=False):
         self.desc = SwitchMoeDesc(T=T, d_model=d_model, d_ff=d_ff, N=N, C=C, capacity_factor=capacity_factor,
                                   dtype=_DT[dtype], priority=_PRIO[priority],
                                   flags=(GATE_SCALE if gate_scale else 0) | (RESIDUAL_ALL if residual_all else 0),
@@ -297,6 +314,25 @@ class SwitchMoE:
         self._outs = SwitchMoeOutputs(*[o[k].data_ptr() for k in
                                         ("y", "expert_id", "gate", "slot", "routed_count", "kept_count",
                                          "n_dropped", "f", "P", "l_aux")])
+        self.dims = (T, d_model, d_ff, N, d_ff_shared, dtype, dev)
+        self.saved = None
+        if train:
+            C_ = self.C
+            sv = dict(probs=_empty((T, N), torch.float32, dev), token_of_slot=_empty((N, C_), torch.int32, dev),
+                      active=_empty(N, torch.int32, dev), n_active=_empty(1, torch.int32, dev),
+                      h=_empty((N, C_, d_ff), dtype, dev),
+                      h_shared=_empty((T, d_ff_shared), dtype, dev) if d_ff_shared else None)
+            self.saved = sv
+            self._saved = SwitchMoeSaved(*[None if sv[k] is None else sv[k].data_ptr() for k in
+                                           ("probs", "token_of_slot", "active", "n_active", "h", "h_shared")])
+            self.bws = torch.empty(max(256, L.switch_moe_backward_workspace_bytes(ctypes.byref(self.desc))),
+                                   dtype=torch.uint8, device=dev)
+            wdt = dtype
+            self.grads = dict(dx=_empty((T, d_model), dtype, dev), dw_gate=_empty((N, d_model), torch.float32, dev),
+                              dbias=_empty(N, torch.float32, dev), dw1=_empty((N, d_model, d_ff), wdt, dev),
+                              dw2=_empty((N, d_ff, d_model), wdt, dev),
+                              dws1=_empty((d_model, d_ff_shared), wdt, dev) if d_ff_shared else None,
+                              dws2=_empty((d_ff_shared, d_model), wdt, dev) if d_ff_shared else None)
 
     def __call__(self, x, w_gate, w1, w2, bias=None, ws1=None, ws2=None, stream=None, stage_events=None):
         """One layer forward.  stage_events: optional StageEvents (7 HIP events) recorded at the stage
@@ -314,6 +350,53 @@ class SwitchMoE:
                                                   _p(self.ws), self.ws.numel(), _stream(stream),
                                                   stage_events.handles))
         return self.out
+
+
+    def forward_train(self, x, w_gate, w1, w2, bias=None, ws1=None, ws2=None, stream=None):
+        """switch_moe_forward_train: the forward plus the saved tensors (self.saved) the backward reads."""
+        if self.saved is None:
+            raise RuntimeError("layer was built without train=True")
+        ins = SwitchMoeInputs(x.data_ptr(), w_gate.data_ptr(), None if bias is None else bias.data_ptr(),
+                              w1.data_ptr(), w2.data_ptr(), None if ws1 is None else ws1.data_ptr(),
+                              None if ws2 is None else ws2.data_ptr())
+        _check("switch_moe_forward_train",
+               lib().switch_moe_forward_train(ctypes.byref(self.desc), ctypes.byref(ins), ctypes.byref(self._outs),
+                                              ctypes.byref(self._saved), _p(self.ws), self.ws.numel(),
+                                              _stream(stream)))
+        return self.out
+
+    def backward(self, x, w_gate, w1, w2, dy, dl_aux=None, bias=None, ws1=None, ws2=None, stream=None):
+        """switch_moe_backward after forward_train on the same inputs; dl_aux: device fp32 [1] or None.
+        Returns self.grads (dbias is None without a router bias)."""
+        if self.saved is None:
+            raise RuntimeError("layer was built without train=True")
+        _need(dy, "dy")
+        ins = SwitchMoeInputs(x.data_ptr(), w_gate.data_ptr(), None if bias is None else bias.data_ptr(),
+                              w1.data_ptr(), w2.data_ptr(), None if ws1 is None else ws1.data_ptr(),
+                              None if ws2 is None else ws2.data_ptr())
+        g = self.grads
+        gr = SwitchMoeGrads(g["dx"].data_ptr(), g["dw_gate"].data_ptr(),
+                            None if bias is None else g["dbias"].data_ptr(), g["dw1"].data_ptr(), g["dw2"].data_ptr(),
+                            None if g["dws1"] is None else g["dws1"].data_ptr(),
+                            None if g["dws2"] is None else g["dws2"].data_ptr())
+        _check("switch_moe_backward",
+               lib().switch_moe_backward(ctypes.byref(self.desc), ctypes.byref(ins), ctypes.byref(self._outs),
+                                         ctypes.byref(self._saved), _p(dy), _p(dl_aux), ctypes.byref(gr),
+                                         _p(self.bws), self.bws.numel(), _stream(stream)))
+        out = dict(g)
+        if bias is None:
+            out["dbias"] = None
+        return out
+
+
+def switch_moe_forward_train(layer: "SwitchMoE", x, w_gate, w1, w2, **kw):
+    """Training forward on a SwitchMoE built with train=True (outputs in layer.out, saved in layer.saved)."""
+    return layer.forward_train(x, w_gate, w1, w2, **kw)
+
+
+def switch_moe_backward(layer: "SwitchMoE", x, w_gate, w1, w2, dy, dl_aux=None, **kw):
+    """Backward of the last forward_train of `layer`; returns the gradient dict."""
+    return layer.backward(x, w_gate, w1, w2, dy, dl_aux=dl_aux, **kw)
 
 
 def switch_moe_forward(x, w_gate, w1, w2, *, bias=None, capacity_factor=1.0, C=0, priority="token",

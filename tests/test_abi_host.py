@@ -138,3 +138,43 @@ def test_size_limits_for_32bit_offsets(L):
                              priority=0, flags=1, d_ff_shared=0)
     assert L.switch_moe_workspace_bytes(ctypes.byref(d)) == 0
     assert _route(L, d=(1 << 20) + 128) == E_SHAPE
+
+
+def test_train_forward_and_backward_validation(L):
+    d = native.SwitchMoeDesc(T=64, d_model=128, d_ff=128, N=8, C=0, capacity_factor=1.0, dtype=1, priority=0,
+                             flags=1, d_ff_shared=0)
+    ins = native.SwitchMoeInputs(1 << 20, 1 << 20, None, 1 << 20, 1 << 20, None, None)
+    outs = native.SwitchMoeOutputs(*([1 << 20] * 10))
+    sv = native.SwitchMoeSaved(1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, None)
+    gr = native.SwitchMoeGrads(1 << 20, 1 << 20, None, 1 << 20, 1 << 20, None, None)
+    ftr = L.switch_moe_forward_train
+    assert ftr(ctypes.byref(d), ctypes.byref(ins), ctypes.byref(outs), None, FAKE, 1 << 30, None) == E_NULL
+    assert b"saved is NULL" in L.switch_last_error()
+    sv.h = None
+    assert ftr(ctypes.byref(d), ctypes.byref(ins), ctypes.byref(outs), ctypes.byref(sv), FAKE, 1 << 30, None) == E_NULL
+    assert b"h is NULL" in L.switch_last_error()
+    sv.h = (1 << 20) + 8
+    assert ftr(ctypes.byref(d), ctypes.byref(ins), ctypes.byref(outs), ctypes.byref(sv), FAKE, 1 << 30, None) == E_ALIGN
+    sv.h = 1 << 20
+    # same workspace as the plain forward
+    assert L.switch_moe_workspace_bytes(ctypes.byref(d)) > 0
+    bwd = L.switch_moe_backward
+    nb = L.switch_moe_backward_workspace_bytes(ctypes.byref(d))
+    assert nb > 0
+    args = lambda **k: [ctypes.byref(d), k.get("ins", ctypes.byref(ins)), k.get("fwd", ctypes.byref(outs)),
+                        k.get("sv", ctypes.byref(sv)), k.get("dy", FAKE), None, k.get("gr", ctypes.byref(gr)),
+                        FAKE, k.get("wsb", nb), None]
+    assert bwd(*args(fwd=None)) == E_NULL
+    assert bwd(*args(sv=None)) == E_NULL
+    assert bwd(*args(gr=None)) == E_NULL
+    assert bwd(*args(dy=None)) == E_NULL
+    assert bwd(*args(wsb=nb - 1)) == E_WS
+    gr.dw1 = None
+    assert bwd(*args()) == E_NULL and b"dw1" in L.switch_last_error()
+    gr.dw1 = 1 << 20
+    d.d_ff_shared = 128
+    assert bwd(*args()) == E_NULL  # shared weights and their gradients missing
+    d.d_ff_shared = 0
+    d.flags = 16
+    assert bwd(*args()) == E_UNSUP
+    assert L.switch_moe_backward_workspace_bytes(ctypes.byref(d)) == 0

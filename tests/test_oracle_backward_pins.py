@@ -235,19 +235,44 @@ def test_backward_invariants(priority):
             assert not ga["dw1"][i].any() and not ga["dw2"][i].any()
 
 
-def test_relu_kink_choice():
-    """A pre-activation exactly at 0: kink = 0 drops its term, kink = 1 keeps it,
-    and nothing else changes."""
+def test_relu_kink_envelope_bounds_every_choice():
+    """In-band pre-activations (two of them exactly 0, one tiny): the envelope
+    must hold the result of every on/off choice, enumerated by brute force, and
+    be attained by the all-negative and all-positive selections."""
     rng = np.random.default_rng(4)
-    rows, w1, w2 = rng.standard_normal((3, 4)), rng.standard_normal((4, 5)), rng.standard_normal((5, 4))
+    rows, w1, w2 = rng.standard_normal((4, 5)), rng.standard_normal((5, 6)), rng.standard_normal((6, 5))
     w1[:, 2] = 0.0
     w1[0, 2] = 1.0
-    rows[1, 0] = 0.0                 # z[1, 2] = 0 exactly
-    dout = rng.standard_normal((3, 4))
-    a = ob.ffn_backward(rows, dout, w1, w2, band_u=2.0 ** -24, kink=0)
-    b = ob.ffn_backward(rows, dout, w1, w2, band_u=2.0 ** -24, kink=1)
-    dh12 = float(dout[1] @ w2[2])
-    np.testing.assert_allclose(b[0][1] - a[0][1], dh12 * w1[:, 2], rtol=1e-14, atol=1e-15)
-    np.testing.assert_allclose(b[1][:, 2] - a[1][:, 2], rows[1] * dh12, rtol=1e-14, atol=1e-15)
-    np.testing.assert_array_equal(a[2], b[2])
-    np.testing.assert_array_equal(np.delete(a[0], 1, axis=0), np.delete(b[0], 1, axis=0))
+    w1[3, 2] = 0.5
+    rows[1, 0] = 0.0
+    rows[1, 3] = 0.0                 # z[1, 2] = 0 exactly
+    rows[3, 0] = -0.5 * rows[3, 3] + 1e-12  # z[3, 2] ~ 1e-12: inside the band, positive
+    w1[:, 4] = 0.0
+    w1[1, 4] = 1.0
+    rows[2, 1] = 0.0                 # z[2, 4] = 0 exactly
+    dout = rng.standard_normal((4, 5))
+    d_rows, dw1, dw2, h, env = ob.ffn_backward(rows, dout, w1, w2, band_u=2.0 ** -24)
+    z = rows @ w1
+    inband = [(1, 2), (3, 2), (2, 4)]
+    assert all(abs(z[p]) <= ob.sum_band(rows, w1, 2.0 ** -24)[p] for p in inband)
+    dh = dout @ w2.T
+    base_mask = (z > 0).astype(float)
+    for p in inband:
+        base_mask[p] = 0.0
+    lo_r, hi_r = env["d_rows"]
+    lo_w, hi_w = env["dw1"]
+    for bits in range(1 << len(inband)):
+        m = base_mask.copy()
+        for j, p in enumerate(inband):
+            if bits >> j & 1:
+                m[p] = 1.0
+        dz = dh * m
+        r, w = dz @ w1.T, rows.T @ dz
+        assert np.all(r >= lo_r - 1e-12) and np.all(r <= hi_r + 1e-12)
+        assert np.all(w >= lo_w - 1e-12) and np.all(w <= hi_w + 1e-12)
+    np.testing.assert_allclose(d_rows, (dh * base_mask) @ w1.T, rtol=1e-14, atol=1e-14)
+    # band 0: the plain z > 0 (so the 1e-30 pre-activation counts as active)
+    d0 = ob.ffn_backward(rows, dout, w1, w2)
+    assert d0[4] is None
+    m0 = (z > 0).astype(float)
+    np.testing.assert_allclose(d0[0], (dh * m0) @ w1.T, rtol=1e-14, atol=1e-14)

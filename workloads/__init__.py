@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the Switch top-1 MoE layer forward.
+"""Seeded synthetic inputs for the Switch top-1 MoE layer (forward and backward).
 
 This module is shared by the fp64 oracle side (tests, smoke check, CPU
 baseline) and the HIP side (tests, bench).  It holds no part of the
@@ -95,7 +95,12 @@ def stored(a32: np.ndarray, dtype: str) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # generation
 # ---------------------------------------------------------------------------
-STREAMS = ("x", "w_gate", "rank", "w1", "w2", "ws1", "ws2", "resample")
+STREAMS = ("x", "w_gate", "rank", "w1", "w2", "ws1", "ws2", "resample", "dy")
+
+# upstream gradient of the auxiliary loss for backward runs: the balance-loss
+# coefficient alpha = 1e-2 of the Switch Transformers summary page (Eq. 4
+# passage), i.e. the gradient l_aux receives from  task + alpha * l_aux
+DL_AUX = 1e-2
 
 
 def _children(seed: int):
@@ -181,6 +186,12 @@ def make_inputs(wl: Workload, *, weights: bool = True, threads: int = 8,
     if bad_rows is not None:
         resample_rows(inp, bad_rows, max_rounds=max_rounds)
     return inp
+
+
+def make_upstream(wl: Workload) -> np.ndarray:
+    """Upstream gradient dy [T, d] of the layer output for backward runs:
+    N(0, 1) draws rounded once to the storage dtype (own child stream)."""
+    return _normal(_children(wl.seed)["dy"], (wl.T, wl.d_model), 1.0, wl.dtype)
 
 
 def resample_rows(inp: Inputs, bad_rows: Callable[["Inputs"], np.ndarray], max_rounds: int = 50) -> None:
