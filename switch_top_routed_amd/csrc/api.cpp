@@ -308,24 +308,36 @@ switch_status validate_saved(const switch_moe_desc& d, const switch_moe_saved* s
 // backward workspace layout
 // ---------------------------------------------------------------------------
 struct BwdLayout {
-  size_t off_u, off_dz, off_dg, off_dxe, off_dlogit, off_colsum, off_dense, off_us, off_dzs, off_dxs, bytes;
+  bool fused;  // bf16 MFMA expert passes (else the generic GEMMs)
+  int dg_parts;
+  RouterBwdPlan rp;  // bf16 router backward
+  size_t off_u, off_dz, off_dg, off_dxe, off_dlogit, off_colsum, off_dense, off_us, off_dzs, off_dxs;
+  size_t off_hi, off_lo, off_rpart, bytes;
 };
 
 BwdLayout bwd_layout(const switch_moe_desc& d, int32_t C) {
   BwdLayout L{};
   const size_t esz = d.dtype == SWITCH_BF16 ? 2 : 4;
   const size_t NC = (size_t)d.N * C;
+  L.fused = d.dtype == SWITCH_BF16 && fused_expert_bwd_applies(d.T, C, d.d_model, d.d_ff);
+  L.dg_parts = L.fused ? d.d_ff / 64 : 1;
   size_t off = 0;
   auto take = [&](size_t& at, size_t bytes) {
     at = off;
     off = align_up(off + bytes);
   };
-  take(L.off_u, NC * d.d_ff * 4);
+  if (!L.fused) take(L.off_u, NC * d.d_ff * 4);
   take(L.off_dz, NC * d.d_ff * esz);
-  take(L.off_dg, NC * 4);
+  take(L.off_dg, NC * L.dg_parts * 4);
   take(L.off_dxe, NC * d.d_model * 4);
   take(L.off_dlogit, (size_t)d.T * d.N * 4);
   take(L.off_colsum, colsum_scratch_bytes(d.T, d.N));
+  if (d.dtype == SWITCH_BF16) {
+    L.rp = router_bwd_plan(d.T, d.N, d.d_model);
+    take(L.off_hi, L.rp.planes_bytes);
+    take(L.off_lo, L.rp.planes_bytes);
+    take(L.off_rpart, L.rp.partial_bytes);
+  }
   if (d.d_ff_shared > 0) {
     take(L.off_dense, 3 * 4);
     take(L.off_us, (size_t)d.T * d.d_ff_shared * 4);
@@ -601,7 +613,7 @@ switch_status switch_moe_backward(const switch_moe_desc* desc, const switch_moe_
   const int64_t T = d.T;
   const int32_t* kept = fwd->kept_count;
   const int32_t* tos = saved->token_of_slot;
-  float* U = reinterpret_cast<float*>(w + L.off_u);
+  float* U = L.fused ? nullptr : reinterpret_cast<float*>(w + L.off_u);
   void* dZ = w + L.off_dz;
   float* dg = gate_scale ? reinterpret_cast<float*>(w + L.off_dg) : nullptr;
   float* dxe = reinterpret_cast<float*>(w + L.off_dxe);
@@ -612,6 +624,30 @@ switch_status switch_moe_backward(const switch_moe_desc* desc, const switch_moe_
   do {                                                         \
     if ((e = (expr)) != hipSuccess) return hip_fail(e, what);  \
   } while (0)
+  if (L.fused) {
+    ExpertBwdArgs A{};
+    A.w1 = in->w1;
+    A.w2 = in->w2;
+    A.x = in->x;
+    A.dy = dy;
+    A.h = saved->h;
+    A.gate = gsc;
+    A.tos = tos;
+    A.kept = kept;
+    A.active = saved->active;
+    A.n_active = saved->n_active;
+    A.dz = dZ;
+    A.dw1 = grads->dw1;
+    A.dw2 = grads->dw2;
+    A.dgp = reinterpret_cast<float*>(w + L.off_dg);
+    A.dxe = dxe;
+    A.T = T;
+    A.N = N;
+    A.C = C;
+    A.d = dm;
+    A.dff = dff;
+    BWD_TRY(launch_expert_bwd_fused(A, st), "switch_moe_backward/experts");
+  } else {
   // routed experts.  U = dY W2^T over each expert's kept tokens
   BWD_TRY(launch_gemm_generic(GemmOperand{dy, dm, 0, tos, nullptr, 0}, 0,
                               GemmOperand{in->w2, dm, (int64_t)dff * dm, nullptr, nullptr, 1},
@@ -634,6 +670,7 @@ switch_status switch_moe_backward(const switch_moe_desc* desc, const switch_moe_
                               GemmOperand{in->w1, dff, (int64_t)dm * dff, nullptr, nullptr, 1},
                               GemmOut{dxe, dm, (int64_t)C * dm}, 1, dt, N, C, dm, dff, C, kept, 1, st),
           "switch_moe_backward/dX");
+  }
   // shared dense expert on every token
   float* dxs = nullptr;
   if (d.d_ff_shared > 0) {
@@ -663,18 +700,28 @@ switch_status switch_moe_backward(const switch_moe_desc* desc, const switch_moe_
             "switch_moe_backward/shared_dX");
   }
   // router: softmax gradient, dW_g = dlogit^T x, db, and dx
-  BWD_TRY(launch_router_grad(saved->probs, fwd->expert_id, fwd->slot, dg, fwd->f, dl_aux, T, N, C, dlogit, st),
+  BWD_TRY(launch_router_grad(saved->probs, fwd->expert_id, fwd->slot, dg, L.dg_parts, fwd->f, dl_aux, T, N, C,
+                             dlogit, st),
           "switch_moe_backward/router");
-  BWD_TRY(launch_gemm_generic(GemmOperand{dlogit, N, 0, nullptr, nullptr, 1}, 1,
-                              GemmOperand{in->x, dm, 0, nullptr, nullptr, 0}, GemmOut{grads->dw_gate, dm, 0}, 1, dt, 1,
-                              N, dm, (int)T, (int)T, nullptr, 0, st),
-          "switch_moe_backward/dW_g");
   if (grads->dbias != nullptr)
     BWD_TRY(launch_colsum(dlogit, T, N, reinterpret_cast<float*>(w + L.off_colsum), grads->dbias, st),
             "switch_moe_backward/db");
-  BWD_TRY(launch_dx_assemble(dlogit, in->w_gate, dxe, dy, dxs, fwd->expert_id, fwd->slot, T, dm, N, C,
-                             (d.flags & SWITCH_RESIDUAL_ALL) != 0, grads->dx, dt, st),
-          "switch_moe_backward/dx");
+  const int residual_all = (d.flags & SWITCH_RESIDUAL_ALL) != 0;
+  if (dt == SWITCH_BF16) {
+    BWD_TRY(launch_router_bwd_mfma(L.rp, dlogit, in->x, in->w_gate, dxe, dy, dxs, fwd->expert_id, fwd->slot, T, dm,
+                                   N, C, residual_all, reinterpret_cast<uint16_t*>(w + L.off_hi),
+                                   reinterpret_cast<uint16_t*>(w + L.off_lo), reinterpret_cast<float*>(w + L.off_rpart),
+                                   grads->dw_gate, grads->dx, st),
+            "switch_moe_backward/router_mfma");
+  } else {
+    BWD_TRY(launch_gemm_generic(GemmOperand{dlogit, N, 0, nullptr, nullptr, 1}, 1,
+                                GemmOperand{in->x, dm, 0, nullptr, nullptr, 0}, GemmOut{grads->dw_gate, dm, 0}, 1, dt,
+                                1, N, dm, (int)T, (int)T, nullptr, 0, st),
+            "switch_moe_backward/dW_g");
+    BWD_TRY(launch_dx_assemble(dlogit, in->w_gate, dxe, dy, dxs, fwd->expert_id, fwd->slot, T, dm, N, C,
+                               residual_all, grads->dx, dt, st),
+            "switch_moe_backward/dx");
+  }
 #undef BWD_TRY
   return ok();
 }

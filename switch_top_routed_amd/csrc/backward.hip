@@ -182,14 +182,17 @@ __global__ __launch_bounds__(256) void dz_rows(const float* __restrict__ U, cons
 // dp_ti = [i = e_t] dg_t + dl_aux * N * f_i / T.
 __global__ __launch_bounds__(256) void router_grad(const float* __restrict__ probs, const int32_t* __restrict__ eid,
                                                    const int32_t* __restrict__ slot, const float* __restrict__ dg,
-                                                   const float* __restrict__ f, const float* __restrict__ dl_aux,
-                                                   int64_t T, int N, int C, float* __restrict__ dlogit) {
+                                                   int nparts, const float* __restrict__ f,
+                                                   const float* __restrict__ dl_aux, int64_t T, int N, int C,
+                                                   float* __restrict__ dlogit) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float caux = dl_aux != nullptr ? dl_aux[0] * (float)N / (float)T : 0.f;
   const int e = eid[t], s = slot[t];
-  const float dgt = (dg != nullptr && s >= 0) ? dg[(int64_t)e * C + s] : 0.f;
+  float dgt = 0.f;
+  if (dg != nullptr && s >= 0)  // the slot's partial sums, in order
+    for (int p = 0; p < nparts; ++p) dgt += dg[((int64_t)e * C + s) * nparts + p];
   float dot = 0.f;
   for (int i = lane; i < N; i += 64) {
     const float dp = (i == e ? dgt : 0.f) + caux * f[i];
@@ -287,10 +290,10 @@ hipError_t launch_dz_rows(const float* U, const void* H, void* dZ, float* dg, co
 }
 
 hipError_t launch_router_grad(const float* probs, const int32_t* eid, const int32_t* slot, const float* dg,
-                              const float* f, const float* dl_aux, int64_t T, int N, int C, float* dlogit,
-                              hipStream_t st) {
-  hipLaunchKernelGGL(router_grad, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, probs, eid, slot, dg, f, dl_aux, T,
-                     N, C, dlogit);
+                              int nparts, const float* f, const float* dl_aux, int64_t T, int N, int C,
+                              float* dlogit, hipStream_t st) {
+  hipLaunchKernelGGL(router_grad, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, probs, eid, slot, dg, nparts, f,
+                     dl_aux, T, N, C, dlogit);
   return hipGetLastError();
 }
 

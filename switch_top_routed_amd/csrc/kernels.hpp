@@ -99,14 +99,43 @@ hipError_t launch_gemm_generic(const GemmOperand& a, int a_f32, const GemmOperan
                                hipStream_t st);
 hipError_t launch_dz_rows(const float* U, const void* H, void* dZ, float* dg, const int32_t* kept,
                           const int32_t* tos, const float* gate, int N, int C, int dff, int dtype, hipStream_t st);
+// dg: per-slot partial sums [N*C][nparts] of dgate (NULL: no gate gradient)
 hipError_t launch_router_grad(const float* probs, const int32_t* eid, const int32_t* slot, const float* dg,
-                              const float* f, const float* dl_aux, int64_t T, int N, int C, float* dlogit,
-                              hipStream_t st);
+                              int nparts, const float* f, const float* dl_aux, int64_t T, int N, int C,
+                              float* dlogit, hipStream_t st);
 size_t colsum_scratch_bytes(int64_t T, int N);
 hipError_t launch_colsum(const float* a, int64_t T, int N, float* scratch, float* out, hipStream_t st);
 hipError_t launch_dx_assemble(const float* dlogit, const void* wg, const float* dxe, const void* dy, const float* dxs,
                               const int32_t* eid, const int32_t* slot, int64_t T, int d, int N, int C,
                               int residual_all, void* dx, int dtype, hipStream_t st);
+
+// fused MFMA expert backward (bf16): pass over W2 (U, dZ, dg partials, dW2),
+// then over W1 (dX_e, dW1); experts that kept no token get zero gradients
+struct ExpertBwdArgs {
+  const void *w1, *w2, *x, *dy, *h;
+  const float* gate;  // per-token gate scale, or NULL (scaling off)
+  const int32_t *tos, *kept, *active, *n_active;
+  void *dz, *dw1, *dw2;
+  float *dgp, *dxe;   // dg partials [N*C][d_ff/64]; dX_e [N][C][d]
+  int64_t T;
+  int N, C, d, dff;
+};
+bool fused_expert_bwd_applies(int64_t T, int C, int d, int dff);
+hipError_t launch_expert_bwd_fused(const ExpertBwdArgs& a, hipStream_t st);
+
+// router backward on MFMA (bf16 layers): dlogit split into bf16 hi / lo planes
+// [T][NP], dW_g from per-chunk partials [S][N][d], dx assembled with the expert,
+// pass-through and shared terms
+struct RouterBwdPlan {
+  int NP, TC, S;  // experts padded to 64; tokens per chunk; chunks
+  size_t planes_bytes, partial_bytes;  // one plane; all partials
+};
+RouterBwdPlan router_bwd_plan(int64_t T, int N, int d);
+hipError_t launch_router_bwd_mfma(const RouterBwdPlan& p, const float* dlogit, const void* x, const void* wg,
+                                  const float* dxe, const void* dy, const float* dxs, const int32_t* eid,
+                                  const int32_t* slot, int64_t T, int d, int N, int C, int residual_all,
+                                  uint16_t* hi, uint16_t* lo, float* partial, float* dw_gate, void* dx,
+                                  hipStream_t st);
 
 inline size_t align_up(size_t v, size_t a = 256) { return (v + a - 1) / a * a; }
 
