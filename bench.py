@@ -1,5 +1,5 @@
 #!/usr/bin/env python3
-"""Benchmark of the Switch top-1 MoE layer forward on one MI355X.
+"""Benchmark of the Switch top-1 MoE layer on one MI355X (forward; backward alongside).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
@@ -21,6 +21,11 @@ JSON line with:
                  HBM GB/s and % of peak for route, dispatch, combine; TFLOP/s
                  and % of the bf16 MFMA peak for the expert GEMMs
   cpu_baseline   the fp64 CPU oracle timed on the host on the same batch
+  backward       the layer backward on the same batch (switch_moe_backward after
+                 a training forward): tokens/s, the roofline of its dominant
+                 weight pass (read w + write dw, timed with HIP events inside
+                 the timed steps), per-stage times, and the fp64 backward
+                 oracle timed on the host
 Inputs are the seeded synthetic workload (x ~ N(0,1), Gaussian weights), no
 dataset.  Only one GPU is supported.
 """
@@ -70,6 +75,9 @@ def parse():
     ap.add_argument("--priority", choices=("token", "gate"), default=None, help="override the overflow priority")
     ap.add_argument("--no-gate-scale", action="store_true", help="combine without the gate multiplier")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip the layer backward measurement")
+    ap.add_argument("--backward-steps", type=int, default=None,
+                    help="timed backward steps (default: min(steps, 50); 5 with a shared expert)")
     ap.add_argument("--stage-steps", type=int, default=20, help="extra steps with every stage boundary timed")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat oracle layer passes until this much CPU time has elapsed (at most 30 passes)")
@@ -233,6 +241,10 @@ def main():
     if not args.no_cpu_baseline and not on_device:
         cpu = cpu_baseline(inp, args.cpu_seconds)
 
+    backward = None
+    if not args.no_backward:
+        backward = measure_backward(args, wl, inp, layer.C, x, wg, w1, w2, bias, ws1, ws2, stream, on_device)
+
     line = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
@@ -240,9 +252,118 @@ def main():
         "config": {"workload": wl.name, "T": T, "d_model": d, "d_ff": F, "N": N,
                    "capacity_factor": wl.capacity_factor, "C": C, "priority": wl.priority,
                    "gate_scale": wl.gate_scale, "d_ff_shared": wl.d_ff_shared, "parallelism": "single GPU"},
-        "roofline": roofline, "stages": stages, "cpu_baseline": cpu,
+        "roofline": roofline, "stages": stages, "cpu_baseline": cpu, "backward": backward,
     }
     print(json.dumps(line), flush=True)
+
+
+def measure_backward(args, wl, inp, C, x, wg, w1, w2, bias, ws1, ws2, stream, on_device):
+    """The layer backward (switch_moe_backward) after one training forward on the
+    same batch, with a seeded upstream gradient dy ~ N(0, 1) and dl_aux = 1e-2.
+    One step = one backward.  The two weight passes (the fused MFMA kernels over
+    w2 and w1) are timed with HIP events inside every timed step; the other
+    stages over extra steps with every boundary recorded."""
+    import numpy as np
+    import torch
+
+    import switch_top_routed_amd as sw
+    import workloads
+
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    esz = 2 if wl.dtype == "bf16" else 4
+    T, d, F, N = wl.T, wl.d_model, wl.d_ff, wl.N
+    tl = sw.SwitchMoE(T, d, F, N, dtype=dt, capacity_factor=wl.capacity_factor, priority=wl.priority,
+                      gate_scale=wl.gate_scale, residual_all=wl.residual_all, d_ff_shared=wl.d_ff_shared,
+                      train=True)
+    tl.forward_train(x, wg, w1, w2, bias=bias, ws1=ws1, ws2=ws2, stream=stream)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(wl.seed + 17)
+    dy = torch.randn((T, d), generator=g, device="cuda").to(dt)
+    dla = torch.full((1,), workloads.DL_AUX, dtype=torch.float32, device="cuda")
+
+    def bstep(ev=None):
+        tl.backward(x, wg, w1, w2, dy, dla, bias=bias, ws1=ws1, ws2=ws2, stream=stream, stage_events=ev)
+
+    steps = args.backward_steps or (5 if wl.d_ff_shared else min(args.steps, 50))
+    for _ in range(3):
+        bstep()
+    pass_ev = [sw.StageEvents(which=(1, 2, 3), n=6) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        bstep(pass_ev[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    w2_s = float(np.mean([e.ms(1, 2) for e in pass_ev])) * 1e-3
+    w1_s = float(np.mean([e.ms(2, 3) for e in pass_ev])) * 1e-3
+    full = [sw.StageEvents(n=6) for _ in range(min(args.stage_steps, steps))]
+    for e in full:
+        bstep(e)
+    torch.cuda.synchronize()
+    names = ["zero_idle", "w2_pass", "w1_pass", "shared", "router_dx"]
+    st_us = {n: float(np.mean([e.ms(i, i + 1) for e in full])) * 1e3 for i, n in enumerate(names)}
+
+    kc = tl.out["kept_count"]
+    kept = int(kc.sum().item())
+    n_active = int((kc > 0).sum().item())
+    wbytes = n_active * d * F * esz  # one weight matrix of the active experts
+    # algorithmic bytes: weight read + gradient write, plus the kept token rows each pass reads
+    # and writes (w2 pass: dY rows, H, dZ, dg partials; w1 pass: dZ, x rows, dX_e in fp32)
+    w2_bytes = 2 * wbytes + kept * (d + 2 * F) * esz + kept * (F // 64) * 4
+    w1_bytes = 2 * wbytes + kept * (F + d) * esz + kept * d * 4
+    flops = 8.0 * kept * d * F  # four GEMMs of 2 kept d F each
+    dom, dom_s, dom_b = ("w2_pass", w2_s, w2_bytes) if w2_s >= w1_s else ("w1_pass", w1_s, w1_bytes)
+    achieved = dom_b / dom_s / 1e9
+    fused = wl.dtype == "bf16" and C <= 160 and T * d * esz < 2 ** 31
+    kname = ("bwd_expert_fused" if fused else "gemm_generic") + f" ({'w2' if dom == 'w2_pass' else 'w1'} pass)"
+    out = {
+        "value": T * steps / elapsed, "unit": "tokens/s", "ms_per_step": elapsed / steps * 1e3, "steps": steps,
+        "step": "one layer backward (switch_moe_backward) after a training forward on the same batch",
+        "dl_aux": workloads.DL_AUX,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": kname,
+                     "bytes_per_launch": dom_b, "launch_us": dom_s * 1e6,
+                     "launch_timing": f"HIP events around each weight pass in the {steps} timed steps"},
+        "passes": {"w2_pass_us": w2_s * 1e6, "w1_pass_us": w1_s * 1e6,
+                   "w2_pass_GB_s": w2_bytes / w2_s / 1e9, "w1_pass_GB_s": w1_bytes / w1_s / 1e9,
+                   "expert_TFLOP_s": flops / (w2_s + w1_s) / 1e12},
+        "stages_us": st_us,
+    }
+    if wl.d_ff_shared:
+        out["stages_us"]["shared_TFLOP_s"] = 8.0 * T * d * wl.d_ff_shared / (st_us["shared"] * 1e-6) / 1e12
+    if not args.no_cpu_baseline and not on_device:
+        out["cpu_baseline"] = cpu_backward_baseline(inp, dy)
+    return out
+
+
+def cpu_backward_baseline(inp, dy_dev):
+    """The fp64 backward oracle, as it stands: one training forward plus one
+    backward pass over the same batch with the same upstream gradient."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads
+    from oracle import backward as ob
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    wl = inp.wl
+    dt = wl.dtype
+    dy = dy_dev.float().cpu().numpy().astype(np.float64)
+    t0 = time.perf_counter()
+    ref = oracle.moe_forward_stored(inp)
+    x, wgt = oracle.widen(inp.x, dt), oracle.widen(inp.w_gate, dt)
+    ws1 = oracle.widen(inp.ws1, dt) if inp.ws1 is not None else None
+    ws2 = oracle.widen(inp.ws2, dt) if inp.ws2 is not None else None
+    ob.moe_backward(ref, x, wgt, lambda e: oracle.widen(inp.w1[e], dt), lambda e: oracle.widen(inp.w2[e], dt),
+                    wl.N, dy, workloads.DL_AUX, gate_scale=wl.gate_scale, residual_all=wl.residual_all, ws1=ws1,
+                    ws2=ws2)
+    el = time.perf_counter() - t0
+    return {"value": wl.T / el, "unit": "tokens/s", "cores": cores, "kind": "oracle", "seconds": el,
+            "sample": f"one fp64 training forward + backward over the {wl.name} batch (T={wl.T} tokens)"}
 
 
 def traffic_bytes(workload):

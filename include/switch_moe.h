@@ -302,6 +302,20 @@ switch_status switch_moe_backward(const switch_moe_desc* desc, const switch_moe_
                                   const float* dl_aux, const switch_moe_grads* grads, void* ws, size_t ws_bytes,
                                   void* stream);
 
+/* switch_moe_backward with its stage boundaries recorded on `stream`.
+   stage_events holds 6 hipEvent_t handles (entries may be NULL and are then
+   skipped; the array itself may not be NULL -> SWITCH_E_NULL):
+     [0] start, [1] before the pass over w2 (after zeroing the weight
+     gradients of experts that kept no token), [2] before the pass over w1,
+     [3] after it, [4] after the shared dense expert (if any), [5] after the
+     router gradient and dx (end).
+   Everything else is that of switch_moe_backward; a failed event record
+   returns SWITCH_E_HIP. */
+switch_status switch_moe_backward_timed(const switch_moe_desc* desc, const switch_moe_inputs* in,
+                                        const switch_moe_outputs* fwd, const switch_moe_saved* saved,
+                                        const void* dy, const float* dl_aux, const switch_moe_grads* grads, void* ws,
+                                        size_t ws_bytes, void* stream, void* const* stage_events);
+
 /* Static description of a status code. */
 const char* switch_status_str(switch_status s);
 /* Thread-local message of the last error on this thread ("" if none). */

@@ -560,10 +560,13 @@ size_t switch_moe_backward_workspace_bytes(const switch_moe_desc* desc) {
   return bwd_layout(*desc, C).bytes;
 }
 
-switch_status switch_moe_backward(const switch_moe_desc* desc, const switch_moe_inputs* in,
+}  // extern "C"
+
+// The layer backward; `ev` (6 events or NULL) marks the stage boundaries on the stream.
+static switch_status moe_backward(const switch_moe_desc* desc, const switch_moe_inputs* in,
                                   const switch_moe_outputs* fwd, const switch_moe_saved* saved, const void* dy,
                                   const float* dl_aux, const switch_moe_grads* grads, void* ws, size_t ws_bytes,
-                                  void* stream) {
+                                  void* stream, void* const* ev) {
   int32_t C = 0;
   TRY(validate_desc(desc, &C));
   if (in == nullptr) return fail(SWITCH_E_NULL, "inputs is NULL");
@@ -624,6 +627,10 @@ switch_status switch_moe_backward(const switch_moe_desc* desc, const switch_moe_
   do {                                                         \
     if ((e = (expr)) != hipSuccess) return hip_fail(e, what);  \
   } while (0)
+  auto mark = [&](int i) -> hipError_t {
+    return (ev != nullptr && ev[i] != nullptr) ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), st) : hipSuccess;
+  };
+  BWD_TRY(mark(0), "switch_moe_backward/event");
   if (L.fused) {
     ExpertBwdArgs A{};
     A.w1 = in->w1;
@@ -646,8 +653,13 @@ switch_status switch_moe_backward(const switch_moe_desc* desc, const switch_moe_
     A.C = C;
     A.d = dm;
     A.dff = dff;
-    BWD_TRY(launch_expert_bwd_fused(A, st), "switch_moe_backward/experts");
+    BWD_TRY(launch_zero_idle_experts(A, st), "switch_moe_backward/zero");
+    BWD_TRY(mark(1), "switch_moe_backward/event");
+    BWD_TRY(launch_expert_bwd_pass(A, 2, st), "switch_moe_backward/w2_pass");
+    BWD_TRY(mark(2), "switch_moe_backward/event");
+    BWD_TRY(launch_expert_bwd_pass(A, 1, st), "switch_moe_backward/w1_pass");
   } else {
+  BWD_TRY(mark(1), "switch_moe_backward/event");
   // routed experts.  U = dY W2^T over each expert's kept tokens
   BWD_TRY(launch_gemm_generic(GemmOperand{dy, dm, 0, tos, nullptr, 0}, 0,
                               GemmOperand{in->w2, dm, (int64_t)dff * dm, nullptr, nullptr, 1},
@@ -660,6 +672,7 @@ switch_status switch_moe_backward(const switch_moe_desc* desc, const switch_moe_
                               GemmOperand{dy, dm, 0, tos, gsc, 0}, GemmOut{grads->dw2, dm, (int64_t)dff * dm}, 0, dt,
                               N, dff, dm, C, C, kept, 2, st),
           "switch_moe_backward/dW2");
+  BWD_TRY(mark(2), "switch_moe_backward/event");
   // dW1 = X^T dZ
   BWD_TRY(launch_gemm_generic(GemmOperand{in->x, dm, 0, tos, nullptr, 1}, 0,
                               GemmOperand{dZ, dff, (int64_t)C * dff, nullptr, nullptr, 0},
@@ -671,6 +684,7 @@ switch_status switch_moe_backward(const switch_moe_desc* desc, const switch_moe_
                               GemmOut{dxe, dm, (int64_t)C * dm}, 1, dt, N, C, dm, dff, C, kept, 1, st),
           "switch_moe_backward/dX");
   }
+  BWD_TRY(mark(3), "switch_moe_backward/event");
   // shared dense expert on every token
   float* dxs = nullptr;
   if (d.d_ff_shared > 0) {
@@ -699,6 +713,7 @@ switch_status switch_moe_backward(const switch_moe_desc* desc, const switch_moe_
                                 (int)T, dm, dfs, (int)T, nullptr, 0, st),
             "switch_moe_backward/shared_dX");
   }
+  BWD_TRY(mark(4), "switch_moe_backward/event");
   // router: softmax gradient, dW_g = dlogit^T x, db, and dx
   BWD_TRY(launch_router_grad(saved->probs, fwd->expert_id, fwd->slot, dg, L.dg_parts, fwd->f, dl_aux, T, N, C,
                              dlogit, st),
@@ -722,8 +737,26 @@ switch_status switch_moe_backward(const switch_moe_desc* desc, const switch_moe_
                                residual_all, grads->dx, dt, st),
             "switch_moe_backward/dx");
   }
+  BWD_TRY(mark(5), "switch_moe_backward/event");
 #undef BWD_TRY
   return ok();
+}
+
+extern "C" {
+
+switch_status switch_moe_backward(const switch_moe_desc* desc, const switch_moe_inputs* in,
+                                  const switch_moe_outputs* fwd, const switch_moe_saved* saved, const void* dy,
+                                  const float* dl_aux, const switch_moe_grads* grads, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  return moe_backward(desc, in, fwd, saved, dy, dl_aux, grads, ws, ws_bytes, stream, nullptr);
+}
+
+switch_status switch_moe_backward_timed(const switch_moe_desc* desc, const switch_moe_inputs* in,
+                                        const switch_moe_outputs* fwd, const switch_moe_saved* saved,
+                                        const void* dy, const float* dl_aux, const switch_moe_grads* grads, void* ws,
+                                        size_t ws_bytes, void* stream, void* const* stage_events) {
+  if (stage_events == nullptr) return fail(SWITCH_E_NULL, "stage_events is NULL");
+  return moe_backward(desc, in, fwd, saved, dy, dl_aux, grads, ws, ws_bytes, stream, stage_events);
 }
 
 const char* switch_status_str(switch_status s) {

@@ -347,13 +347,14 @@ static hipError_t launch_fused(const ExpertBwdArgs& A, hipStream_t st) {
   return launch_fused_mt<10, MODE>(A, st);
 }
 
-hipError_t launch_expert_bwd_fused(const ExpertBwdArgs& A, hipStream_t st) {
+hipError_t launch_zero_idle_experts(const ExpertBwdArgs& A, hipStream_t st) {
   hipLaunchKernelGGL(zero_idle_experts, dim3(64, (unsigned)A.N), dim3(256), 0, st, static_cast<uint16_t*>(A.dw1),
                      static_cast<uint16_t*>(A.dw2), A.kept, (int64_t)A.d * A.dff);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if ((e = launch_fused<2>(A, st)) != hipSuccess) return e;
-  return launch_fused<1>(A, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_expert_bwd_pass(const ExpertBwdArgs& A, int which, hipStream_t st) {
+  return which == 2 ? launch_fused<2>(A, st) : launch_fused<1>(A, st);
 }
 
 }  // namespace swm

@@ -121,7 +121,9 @@ struct ExpertBwdArgs {
   int N, C, d, dff;
 };
 bool fused_expert_bwd_applies(int64_t T, int C, int d, int dff);
-hipError_t launch_expert_bwd_fused(const ExpertBwdArgs& a, hipStream_t st);
+hipError_t launch_zero_idle_experts(const ExpertBwdArgs& a, hipStream_t st);
+// which = 2: pass over W2 (dZ, dg partials, dW2); 1: pass over W1 (dX_e, dW1)
+hipError_t launch_expert_bwd_pass(const ExpertBwdArgs& a, int which, hipStream_t st);
 
 // router backward on MFMA (bf16 layers): dlogit split into bf16 hi / lo planes
 // [T][NP], dW_g from per-chunk partials [S][N][d], dx assembled with the expert,

@@ -76,6 +76,9 @@ _SIGS = {
     "switch_moe_backward": (_i32, [ctypes.POINTER(SwitchMoeDesc), ctypes.POINTER(SwitchMoeInputs),
                                    ctypes.POINTER(SwitchMoeOutputs), ctypes.POINTER(SwitchMoeSaved), _vp, _vp,
                                    ctypes.POINTER(SwitchMoeGrads), _vp, _sz, _vp]),
+    "switch_moe_backward_timed": (_i32, [ctypes.POINTER(SwitchMoeDesc), ctypes.POINTER(SwitchMoeInputs),
+                                         ctypes.POINTER(SwitchMoeOutputs), ctypes.POINTER(SwitchMoeSaved), _vp, _vp,
+                                         ctypes.POINTER(SwitchMoeGrads), _vp, _sz, _vp, ctypes.POINTER(_vp)]),
     "switch_status_str": (ctypes.c_char_p, [_i32]),
     "switch_last_error": (ctypes.c_char_p, []),
 }
@@ -254,13 +257,14 @@ def _hip_runtime():
 
 
 class StageEvents:
-    """Seven HIP events for switch_moe_forward_timed: [0] before route, [1] assign, [2] dispatch,
-    [3] routed expert FFN, [4] after it, [5] combine, [6] after combine."""
+    """HIP events at stage boundaries.  Forward (n=7, switch_moe_forward_timed): [0] before route,
+    [1] assign, [2] dispatch, [3] routed expert FFN, [4] after it, [5] combine, [6] after combine.
+    Backward (n=6, switch_moe_backward_timed): [0] start, [1] pass over w2, [2] pass over w1,
+    [3] after it, [4] after the shared expert, [5] end."""
 
-    N = 7
-
-    def __init__(self, which=None):
+    def __init__(self, which=None, n=7):
         """which: indices of the events to create (default all); the others stay NULL and are not recorded."""
+        self.N = n
         h = _hip_runtime()
         self.handles = (_vp * self.N)()
         for i in range(self.N) if which is None else which:
@@ -365,8 +369,10 @@ class SwitchMoE:
                                               _stream(stream)))
         return self.out
 
-    def backward(self, x, w_gate, w1, w2, dy, dl_aux=None, bias=None, ws1=None, ws2=None, stream=None):
+    def backward(self, x, w_gate, w1, w2, dy, dl_aux=None, bias=None, ws1=None, ws2=None, stream=None,
+                 stage_events=None):
         """switch_moe_backward after forward_train on the same inputs; dl_aux: device fp32 [1] or None.
+        stage_events: optional StageEvents(n=6) (switch_moe_backward_timed).
         Returns self.grads (dbias is None without a router bias)."""
         if self.saved is None:
             raise RuntimeError("layer was built without train=True")
@@ -379,10 +385,17 @@ class SwitchMoE:
                             None if bias is None else g["dbias"].data_ptr(), g["dw1"].data_ptr(), g["dw2"].data_ptr(),
                             None if g["dws1"] is None else g["dws1"].data_ptr(),
                             None if g["dws2"] is None else g["dws2"].data_ptr())
-        _check("switch_moe_backward",
-               lib().switch_moe_backward(ctypes.byref(self.desc), ctypes.byref(ins), ctypes.byref(self._outs),
-                                         ctypes.byref(self._saved), _p(dy), _p(dl_aux), ctypes.byref(gr),
-                                         _p(self.bws), self.bws.numel(), _stream(stream)))
+        if stage_events is None:
+            _check("switch_moe_backward",
+                   lib().switch_moe_backward(ctypes.byref(self.desc), ctypes.byref(ins), ctypes.byref(self._outs),
+                                             ctypes.byref(self._saved), _p(dy), _p(dl_aux), ctypes.byref(gr),
+                                             _p(self.bws), self.bws.numel(), _stream(stream)))
+        else:
+            _check("switch_moe_backward_timed",
+                   lib().switch_moe_backward_timed(ctypes.byref(self.desc), ctypes.byref(ins),
+                                                   ctypes.byref(self._outs), ctypes.byref(self._saved), _p(dy),
+                                                   _p(dl_aux), ctypes.byref(gr), _p(self.bws), self.bws.numel(),
+                                                   _stream(stream), stage_events.handles))
         out = dict(g)
         if bias is None:
             out["dbias"] = None
