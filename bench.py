@@ -47,20 +47,38 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 # counters is reported only while these files are byte-identical to the ones
 # the counters were taken on.
 FFN_SOURCES = ("switch_top_routed_amd/csrc/expert_ffn.hip", "switch_top_routed_amd/csrc/expert_ffn_dma.hip",
-               "switch_top_routed_amd/csrc/common.hpp", "switch_top_routed_amd/csrc/kernels.hpp")
+               "switch_top_routed_amd/csrc/common.hpp")
 # FETCH_SIZE / WRITE_SIZE (KiB per dispatch, as rocprofv3 prints them) of the two
 # routed-FFN launches of one step, and the scale factors that a plain 1 GiB
 # device copy gives those counters (bytes moved / bytes counted).  Source:
 # profiles/*_hbm_traffic.md.
 TRAFFIC = {
     "switch-base-uniform": {
-        "sources_sha256": "cf1f0b348c332771e9d6381c0b66fddbc2af1365497652d37c94cc3d215c069b",
-        "fetch_kib": [298403.0, 308676.0], "write_kib": [24108.0, 6027.0], "fetch_scale": 2.0, "write_scale": 1.0,
+        "sources_sha256": "ce42edfacc82c46dbaa249026799b8f7e23a135b1a3cde1ec8754ab452708549",
+        "fetch_kib": [298400.0, 308566.0], "write_kib": [24108.0, 6027.0],
+        "fetch_scale": 2.0, "write_scale": 1.0,
     },
     "switch-large-shared": {
-        "sources_sha256": "cf1f0b348c332771e9d6381c0b66fddbc2af1365497652d37c94cc3d215c069b",
-        "fetch_kib": [5330315.0, 5516778.0], "write_kib": [262145.0, 163841.0], "fetch_scale": 2.0,
-        "write_scale": 1.0,
+        "sources_sha256": "ce42edfacc82c46dbaa249026799b8f7e23a135b1a3cde1ec8754ab452708549",
+        "fetch_kib": [5327956.0, 5510926.0], "write_kib": [262145.0, 163842.0],
+        "fetch_scale": 2.0, "write_scale": 1.0,
+    },
+}
+
+
+# The same for the two fused weight passes of the backward (bwd_expert_fused: the
+# pass over w2, then the pass over w1), fingerprinted by BWD_SOURCES.
+BWD_SOURCES = ("switch_top_routed_amd/csrc/backward_fused.hip", "switch_top_routed_amd/csrc/common.hpp")
+BWD_TRAFFIC = {
+    "switch-base-uniform": {
+        "sources_sha256": "89f4db8815d7f5ac6dd593a5c3008e48fd6153eb50998cb69c253a6570ef8b1c",
+        "fetch_kib": [322823.0, 313085.0], "write_kib": [614899.0, 601879.0],
+        "fetch_scale": 2.0, "write_scale": 1.0,
+    },
+    "switch-large-shared": {
+        "sources_sha256": "89f4db8815d7f5ac6dd593a5c3008e48fd6153eb50998cb69c253a6570ef8b1c",
+        "fetch_kib": [5914936.0, 5783067.0], "write_kib": [10763009.0, 10813443.0],
+        "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
 
@@ -84,13 +102,14 @@ def parse():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a device-to-device copy of BYTES bytes (5 times): the reference kernel whose "
                          "FETCH_SIZE / WRITE_SIZE counters scale the measured HBM traffic")
-    ap.add_argument("--sources-sha", action="store_true", help="print the fingerprint of the FFN kernel sources")
+    ap.add_argument("--sources-sha", action="store_true",
+                    help="print the fingerprints of the FFN and backward kernel sources")
     return ap.parse_args()
 
 
-def sources_sha256():
+def sources_sha256(files=None):
     h = hashlib.sha256()
-    for rel in FFN_SOURCES:
+    for rel in files or FFN_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -99,7 +118,7 @@ def sources_sha256():
 def main():
     args = parse()
     if args.sources_sha:
-        print(sources_sha256())
+        print(sources_sha256(), sources_sha256(BWD_SOURCES))
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -321,7 +340,9 @@ def measure_backward(args, wl, inp, C, x, wg, w1, w2, bias, ws1, ws2, stream, on
         "step": "one layer backward (switch_moe_backward) after a training forward on the same batch",
         "dl_aux": workloads.DL_AUX,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": kname,
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": bwd_traffic_bytes(wl.name, dom) if wl == workloads.WORKLOADS.get(wl.name) else None,
+                     "kernel": kname,
                      "bytes_per_launch": dom_b, "launch_us": dom_s * 1e6,
                      "launch_timing": f"HIP events around each weight pass in the {steps} timed steps"},
         "passes": {"w2_pass_us": w2_s * 1e6, "w1_pass_us": w1_s * 1e6,
@@ -364,6 +385,16 @@ def cpu_backward_baseline(inp, dy_dev):
     el = time.perf_counter() - t0
     return {"value": wl.T / el, "unit": "tokens/s", "cores": cores, "kind": "oracle", "seconds": el,
             "sample": f"one fp64 training forward + backward over the {wl.name} batch (T={wl.T} tokens)"}
+
+
+def bwd_traffic_bytes(workload, which):
+    """HBM bytes of one backward weight pass ("w2_pass" / "w1_pass") from the
+    stored counter readings, or None (no readings, or changed sources)."""
+    t = BWD_TRAFFIC.get(workload)
+    if t is None or t["sources_sha256"] != sources_sha256(BWD_SOURCES):
+        return None
+    i = 0 if which == "w2_pass" else 1
+    return t["fetch_kib"][i] * 1024 * t["fetch_scale"] + t["write_kib"][i] * 1024 * t["write_scale"]
 
 
 def traffic_bytes(workload):
