@@ -7,7 +7,9 @@ Parity bars (the layer's published tolerances):
   * P: relative 1e-5 with an absolute floor of 1e-9; L_aux: relative 1e-5;
   * gate (fp32 router): relative 1e-5;
   * outputs: per kept token, max_k |y - y_ref| / max_k |y_ref| <= 1e-4 (fp32)
-    or 2e-2 (bf16 storage, fp32 accumulation); dropped tokens bit-exact.
+    or 2e-2 (bf16 storage, fp32 accumulation); dropped tokens bit-exact;
+  * gradients: the same bar per row, measured as the distance to the
+    oracle's [lo, hi] envelope (check_rows).
 """
 import numpy as np
 import torch
@@ -95,3 +97,23 @@ def check_output(y_dev: torch.Tensor, ref: dict, x_stored: np.ndarray, dtype: st
             xs = x_stored.view(np.uint32) if x_stored.dtype == np.float32 else x_stored
             np.testing.assert_array_equal(yb, xs[drop])
     return y
+
+
+def check_rows(name, got, ref, tol, env=None, zero_rows_exact=True):
+    """Row-wise relative distance to [lo, hi] (or to ref); all-zero reference rows must be zero."""
+    got = got.reshape(-1, got.shape[-1])
+    ref2 = ref.reshape(-1, ref.shape[-1])
+    if env is None:
+        lo = hi = ref2
+    else:
+        lo, hi = (e.reshape(-1, ref.shape[-1]) for e in env)
+    dist = np.maximum(np.maximum(got - hi, lo - got), 0.0).max(axis=1)
+    den = np.abs(ref2).max(axis=1)
+    zero = den == 0
+    if zero_rows_exact and zero.any():
+        bad = np.nonzero(np.abs(got[zero]).max(axis=1) != 0)[0]
+        assert bad.size == 0, f"{name}: {bad.size} rows should be exactly zero"
+    r = dist[~zero] / den[~zero]
+    if r.size:
+        assert r.max() <= tol, f"{name}: max row rel err {r.max():.3g} > {tol} (row {np.nonzero(~zero)[0][r.argmax()]})"
+    return float(r.max()) if r.size else 0.0

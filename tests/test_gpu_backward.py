@@ -18,7 +18,7 @@ import oracle
 import workloads
 from oracle import backward as ob
 from tests import inputs_util
-from tests.gpu_util import TOL_OUT, dev, host, host_bits
+from tests.gpu_util import TOL_OUT, check_rows, dev, host, host_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -68,26 +68,6 @@ def _oracle(wl, inp, dy, dl_aux, C=None):
                         wl.N, oracle.widen(dy, dt), 0.0 if dl_aux is None else dl_aux, gate_scale=wl.gate_scale,
                         residual_all=wl.residual_all, ws1=ws1, ws2=ws2, kink_band_u=U32)
     return ref, g
-
-
-def check_rows(name, got, ref, tol, env=None, zero_rows_exact=True):
-    """Row-wise relative distance to [lo, hi] (or to ref); all-zero reference rows must be zero."""
-    got = got.reshape(-1, got.shape[-1])
-    ref2 = ref.reshape(-1, ref.shape[-1])
-    if env is None:
-        lo = hi = ref2
-    else:
-        lo, hi = (e.reshape(-1, ref.shape[-1]) for e in env)
-    dist = np.maximum(np.maximum(got - hi, lo - got), 0.0).max(axis=1)
-    den = np.abs(ref2).max(axis=1)
-    zero = den == 0
-    if zero_rows_exact and zero.any():
-        bad = np.nonzero(np.abs(got[zero]).max(axis=1) != 0)[0]
-        assert bad.size == 0, f"{name}: {bad.size} rows should be exactly zero"
-    r = dist[~zero] / den[~zero]
-    if r.size:
-        assert r.max() <= tol, f"{name}: max row rel err {r.max():.3g} > {tol} (row {np.nonzero(~zero)[0][r.argmax()]})"
-    return float(r.max()) if r.size else 0.0
 
 
 def check_backward(wl, inp, dy, dl_aux, out, layer, g, ref, gref):
