@@ -32,7 +32,9 @@ with its reason in the design notes):
   * argmax ties go to the lowest index; gate-descending ties to the lower
     token index; slot = priority rank.
 
-The backward pass of the layer lives in oracle/backward.py.
+The backward pass of the layer lives in oracle/backward.py; the routing
+variants next to top-1 (top-K token choice, expert choice) in
+oracle/routing.py.
 
 Parity status: every function here is pinned by the CPU tests
 (brute-force evaluation, closed forms, invariants, a hand-worked example);

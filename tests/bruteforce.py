@@ -98,3 +98,114 @@ def brute_forward(x, wg, bias, w1, w2, C, priority="token", gate_scale=True, res
     return dict(logits=logits, p=probs, expert_id=eid, gate=gate, rank=rank, slot=slot, y=y,
                 routed_count=count, f=f, P=P, l_aux=l_aux, kept_count=kept_count,
                 n_dropped=T - sum(kept_count))
+
+
+def _softmax_row(l):
+    m = max(l)
+    ex = [math.exp(v - m) for v in l]
+    z = math.fsum(ex)
+    return [v / z for v in ex]
+
+
+def brute_forward_topk(x, wg, bias, w1, w2, K, C, priority="token", gate_scale=True, residual_all=False,
+                       renorm=False):
+    """Top-K token choice: repeated selection of the largest remaining logit per
+    token; assignment ranks by pairwise counting over the (choice, token) pairs."""
+    T, N, d = len(x), len(wg), len(x[0])
+    eid, gate, probs = [], [], []
+    for t in range(T):
+        l = [_dot(wg[i], x[t]) + (bias[i] if bias is not None else 0.0) for i in range(N)]
+        p = _softmax_row(l)
+        chosen = []
+        for _ in range(K):
+            best = None
+            for i in range(N):
+                if i in chosen:
+                    continue
+                if best is None or l[i] > l[best]:
+                    best = i
+            chosen.append(best)
+        g = [p[i] for i in chosen]
+        if renorm:
+            z = math.fsum(g)
+            g = [v / z for v in g]
+        eid.append(chosen)
+        gate.append(g)
+        probs.append(p)
+
+    def key_before(a, b):  # a, b = (j, t)
+        va, vb = a[0] * T + a[1], b[0] * T + b[1]
+        if priority == "token":
+            return va < vb
+        ga, gb = gate[a[1]][a[0]], gate[b[1]][b[0]]
+        return ga > gb or (ga == gb and va < vb)
+
+    pairs = [(j, t) for j in range(K) for t in range(T)]
+    slot = [[-1] * K for _ in range(T)]
+    for (j, t) in pairs:
+        r = 0
+        for (j2, t2) in pairs:
+            if (j2, t2) != (j, t) and eid[t2][j2] == eid[t][j] and key_before((j2, t2), (j, t)):
+                r += 1
+        if r < C:
+            slot[t][j] = r
+    y = []
+    for t in range(T):
+        row = [0.0] * d
+        any_kept = False
+        for j in range(K):
+            if slot[t][j] < 0:
+                continue
+            any_kept = True
+            o = _expert(x[t], w1[eid[t][j]], w2[eid[t][j]])
+            s = gate[t][j] if gate_scale else 1.0
+            for k in range(d):
+                row[k] += s * o[k]
+        if (not any_kept) or residual_all:
+            for k in range(d):
+                row[k] += x[t][k]
+        y.append(row)
+    count = [sum(1 for t in range(T) for j in range(K) if eid[t][j] == i) for i in range(N)]
+    f = [c / (K * T) for c in count]
+    P = [math.fsum(probs[t][i] for t in range(T)) / T for i in range(N)]
+    kept_count = [sum(1 for t in range(T) for j in range(K) if eid[t][j] == i and slot[t][j] >= 0)
+                  for i in range(N)]
+    return dict(expert_ids=eid, gates=gate, p=probs, slot=slot, y=y, routed_count=count, f=f, P=P,
+                l_aux=N * math.fsum(f[i] * P[i] for i in range(N)), kept_count=kept_count,
+                n_dropped=K * T - sum(kept_count))
+
+
+def brute_forward_expert_choice(x, wg, bias, w1, w2, C, gate_scale=True, residual_all=False):
+    """Expert choice: each expert ranks every token by counting the tokens with a
+    higher score (ties to the lower index) and keeps ranks below C."""
+    T, N, d = len(x), len(wg), len(x[0])
+    probs = []
+    for t in range(T):
+        l = [_dot(wg[i], x[t]) + (bias[i] if bias is not None else 0.0) for i in range(N)]
+        probs.append(_softmax_row(l))
+    pick = [[-1] * N for _ in range(T)]
+    for i in range(N):
+        for t in range(T):
+            r = 0
+            for u in range(T):
+                if u != t and (probs[u][i] > probs[t][i] or (probs[u][i] == probs[t][i] and u < t)):
+                    r += 1
+            if r < C:
+                pick[t][i] = r
+    y = []
+    for t in range(T):
+        row = [0.0] * d
+        any_kept = False
+        for i in range(N):
+            if pick[t][i] < 0:
+                continue
+            any_kept = True
+            o = _expert(x[t], w1[i], w2[i])
+            s = probs[t][i] if gate_scale else 1.0
+            for k in range(d):
+                row[k] += s * o[k]
+        if (not any_kept) or residual_all:
+            for k in range(d):
+                row[k] += x[t][k]
+        y.append(row)
+    return dict(p=probs, pick=pick, y=y)
