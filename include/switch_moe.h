@@ -81,6 +81,17 @@ typedef enum switch_priority {
  * Dropped tokens always get y = x. */
 #define SWITCH_GATE_SCALE 1u
 #define SWITCH_RESIDUAL_ALL 2u
+/* Top-K only: divide each token's K gates by their sum (the gate of choice j
+ * is otherwise p[t, e_tj], the top-1 definition applied to every choice). */
+#define SWITCH_RENORM 4u
+
+/* Routing ("Top-1 Routing" page, Variants: token choice, where each token
+ * picks its top-K experts, and expert choice, where each expert picks its top
+ * tokens and is balanced by construction). */
+typedef enum switch_routing {
+  SWITCH_TOKEN_CHOICE = 0,  /* top-K, K = desc.top_k (0 or 1: the Switch top-1 layer) */
+  SWITCH_EXPERT_CHOICE = 1  /* expert i takes the min(C, T) tokens with the highest p[t, i] */
+} switch_routing;
 
 /* ------------------------------------------------------------------------
  * Capacity ([TOP1] Token Dropping; [SWT] expert capacity; [CAP] Where
@@ -191,6 +202,9 @@ typedef struct switch_moe_desc {
   int32_t d_ff_shared;      /* 0: no shared expert; else one always-on dense
                                FFN added to every token ([TOP1] History,
                                shared experts) */
+  int32_t top_k;            /* token choice: experts per token, 0 or 1 = top-1,
+                               at most 8 and at most N */
+  int32_t routing;          /* switch_routing */
 } switch_moe_desc;
 
 typedef struct switch_moe_inputs {
@@ -219,6 +233,33 @@ typedef struct switch_moe_outputs {
 size_t switch_moe_workspace_bytes(const switch_moe_desc* desc);
 switch_status switch_moe_forward(const switch_moe_desc* desc, const switch_moe_inputs* in,
                                  const switch_moe_outputs* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Routing variants of switch_moe_forward (desc.top_k > 1, or desc.routing =
+ * SWITCH_EXPERT_CHOICE).  Capacity, buffers, the expert FFN and the shared
+ * expert are those of the top-1 layer.
+ *   Top-K token choice: each token's K highest logits (ties to the lower
+ *   index), gate_tj = p[t, e_tj] (SWITCH_RENORM: divided by the token's K-gate
+ *   sum).  C = min(T, max(1, ceil(capacity_factor * K * T / N))) unless
+ *   desc.C is set.  The K T assignments are ranked inside each expert as one
+ *   list ordered j * T + t (every first choice before every second choice;
+ *   SWITCH_GATE_DESC: by descending gate, ties in that order).  Outputs:
+ *   expert_id, gate and slot hold [T, K] (choice j of token t at t * K + j);
+ *   routed_count counts all K T assignments, f_i = routed_count_i / (K T),
+ *   P and l_aux as for top-1; n_dropped counts dropped assignments.
+ *   y_t = sum over the token's kept assignments of (gate-scale ? gate : 1) *
+ *   E(x_t) (+ x_t with SWITCH_RESIDUAL_ALL); a token with no kept assignment
+ *   passes through (y_t = x_t).
+ *   Expert choice: C = max(1, ceil(capacity_factor * T / N)) unless desc.C
+ *   is set (min(C, T) <= 8192); expert i takes the min(C, T) tokens with the
+ *   highest p[t, i] (ties to the lower token) into slots by descending p.
+ *   y_t = sum over the experts that took t of (gate-scale ? p[t, i] : 1) *
+ *   E_i(x_t) (+ x_t with SWITCH_RESIDUAL_ALL); a token no expert took passes
+ *   through.  Outputs: expert_id, gate, routed_count, f, P, l_aux are the
+ *   argmax (top-1) statistics of the same router; kept_count[i] = min(C, T);
+ *   slot[t] = the number of experts that took token t; n_dropped = the
+ *   number of tokens no expert took.
+ * The training entry points below support top-1 only (SWITCH_E_UNSUPPORTED
+ * otherwise). */
 
 /* switch_moe_forward with its stage boundaries recorded on `stream`, for
    timing the stages of the very launches a caller measures.  stage_events

@@ -201,12 +201,14 @@ switch_status validate_combine(const void* expert_out, const void* x, const void
 // ---------------------------------------------------------------------------
 struct FwdLayout {
   int32_t C;
-  bool fused;  // token order: slots from the router's tiles, dispatch folded into GEMM 1
+  int K;       // token choice: experts per token
+  bool ec;     // expert choice
+  bool fused;  // top-1 token order: slots from the router's tiles, dispatch folded into GEMM 1
   RoutePlan route;
   AssignPlan assign;
   FfnPlan ffn, sffn;
   size_t off_route, off_assign, off_rank, off_toff, off_tos, off_active, off_nact, off_xin, off_xout, off_ffn;
-  size_t off_dense, off_sffn, off_sout, bytes;
+  size_t off_dense, off_sffn, off_sout, off_ev, off_gv, off_slotv, off_probs_t, off_pick, bytes;
 };
 
 // The fused path needs token order, the token matrix addressable through
@@ -218,9 +220,11 @@ FwdLayout fwd_layout(const switch_moe_desc& d, int32_t C) {
   FwdLayout L{};
   L.C = C;
   const size_t esz = d.dtype == SWITCH_BF16 ? 2 : 4;
+  L.K = d.top_k < 1 ? 1 : d.top_k;
+  L.ec = d.routing == SWITCH_EXPERT_CHOICE;
   L.route = route_plan(d.T, d.d_model, d.N, d.dtype);
-  L.fused = d.priority == SWITCH_TOKEN_ORDER && (int64_t)d.T * d.d_model * (int64_t)esz < ((int64_t)1 << 31) &&
-            L.route.nblk <= kFusedMaxTiles;
+  L.fused = !L.ec && L.K == 1 && d.priority == SWITCH_TOKEN_ORDER &&
+            (int64_t)d.T * d.d_model * (int64_t)esz < ((int64_t)1 << 31) && L.route.nblk <= kFusedMaxTiles;
   L.ffn = ffn_plan(d.N, C, d.d_model, d.d_ff, d.dtype);
   size_t off = 0;
   L.off_route = off;
@@ -230,10 +234,24 @@ FwdLayout fwd_layout(const switch_moe_desc& d, int32_t C) {
     off = align_up(off + (size_t)d.T * 4);
     L.off_toff = off;
     off = align_up(off + (size_t)L.route.nblk * d.N * 4);
-  } else {
-    L.assign = assign_plan(d.T, d.N, C, d.priority);
+  } else if (!L.ec) {
+    const int64_t TV = (int64_t)L.K * d.T;  // assignments ("virtual tokens")
+    L.assign = assign_plan(TV, d.N, C, d.priority);
     L.off_assign = off;
     off = align_up(off + L.assign.bytes);
+    if (L.K > 1) {
+      L.off_ev = off;
+      off = align_up(off + (size_t)TV * 4);
+      L.off_gv = off;
+      off = align_up(off + (size_t)TV * 4);
+      L.off_slotv = off;
+      off = align_up(off + (size_t)TV * 4);
+    }
+  } else {
+    L.off_probs_t = off;
+    off = align_up(off + (size_t)d.T * d.N * 4);
+    L.off_pick = off;
+    off = align_up(off + (size_t)d.T * d.N * 4);
   }
   L.off_tos = off;
   off = align_up(off + (size_t)d.N * C * 4);
@@ -273,14 +291,25 @@ switch_status validate_desc(const switch_moe_desc* d, int32_t* C) {
     return fail(SWITCH_E_SHAPE, "d_model * d_ff (or d_ff_shared) exceeds 2^30");
   if (d->priority != SWITCH_TOKEN_ORDER && d->priority != SWITCH_GATE_DESC)
     return fail(SWITCH_E_UNSUPPORTED, "priority %d is not supported", d->priority);
-  if (d->flags & ~(SWITCH_GATE_SCALE | SWITCH_RESIDUAL_ALL))
+  if (d->flags & ~(SWITCH_GATE_SCALE | SWITCH_RESIDUAL_ALL | SWITCH_RENORM))
     return fail(SWITCH_E_UNSUPPORTED, "unknown flag bits 0x%x", d->flags);
+  if (d->routing != SWITCH_TOKEN_CHOICE && d->routing != SWITCH_EXPERT_CHOICE)
+    return fail(SWITCH_E_UNSUPPORTED, "routing %d is not supported", d->routing);
+  const int K = d->top_k < 1 ? 1 : d->top_k;
+  if (K > kMaxTopK || K > d->N) return fail(SWITCH_E_SHAPE, "top_k=%d outside [1, min(N, %d)]", K, kMaxTopK);
+  if (d->routing == SWITCH_EXPERT_CHOICE && K != 1)
+    return fail(SWITCH_E_UNSUPPORTED, "expert choice takes no top_k (top_k=%d)", d->top_k);
+  if (K > 1 && (int64_t)K * d->T > kMaxTokens)
+    return fail(SWITCH_E_SHAPE, "top_k * T = %lld exceeds 2^30", (long long)K * d->T);
   int32_t c = d->C;
   if (c == 0) {
-    c = switch_capacity(d->T, d->N, d->capacity_factor);
+    c = switch_capacity(K * d->T, d->N, d->capacity_factor);  // K assignments per token
     if (c < 1) return fail(SWITCH_E_SHAPE, "capacity_factor=%g gives no capacity", d->capacity_factor);
+    if (c > d->T) c = (int32_t)d->T;  // an expert receives each token at most once
   }
   if (c < 1 || c > d->T) return fail(SWITCH_E_SHAPE, "C=%d outside [1, T=%lld]", c, (long long)d->T);
+  if (d->routing == SWITCH_EXPERT_CHOICE && c > kMaxExpertChoiceK)
+    return fail(SWITCH_E_UNSUPPORTED, "expert choice with min(C, T) = %d beyond %d", c, kMaxExpertChoiceK);
   if ((int64_t)d->N * c > ((int64_t)1 << 31) - 1) return fail(SWITCH_E_SHAPE, "N*C exceeds 2^31-1");
   *C = c;
   return SWITCH_OK;
@@ -467,7 +496,11 @@ static switch_status moe_forward(const switch_moe_desc* desc, const switch_moe_i
     REQUIRE_ALIGN(in->ws1, 16);
     REQUIRE_ALIGN(in->ws2, 16);
   }
-  if (sv != nullptr) TRY(validate_saved(d, sv));
+  if (sv != nullptr) {
+    if (d.top_k > 1 || d.routing != SWITCH_TOKEN_CHOICE)
+      return fail(SWITCH_E_UNSUPPORTED, "the training forward supports top-1 routing only");
+    TRY(validate_saved(d, sv));
+  }
   const FwdLayout L = fwd_layout(d, C);
   TRY(check_ws(ws, ws_bytes, L.bytes));
   char* w = static_cast<char*>(ws);
@@ -475,7 +508,15 @@ static switch_status moe_forward(const switch_moe_desc* desc, const switch_moe_i
   int32_t* tos = sv != nullptr ? sv->token_of_slot : reinterpret_cast<int32_t*>(w + L.off_tos);
   int32_t* active = sv != nullptr ? sv->active : reinterpret_cast<int32_t*>(w + L.off_active);
   int32_t* nact = sv != nullptr ? sv->n_active : reinterpret_cast<int32_t*>(w + L.off_nact);
-  float* probs = sv != nullptr ? sv->probs : nullptr;
+  RouteExtra rex;
+  rex.probs = sv != nullptr ? sv->probs : nullptr;
+  rex.K = L.K;
+  rex.renorm = (d.flags & SWITCH_RENORM) != 0;
+  if (L.K > 1) {
+    rex.ev_cm = reinterpret_cast<int32_t*>(w + L.off_ev);
+    rex.gv_cm = reinterpret_cast<float*>(w + L.off_gv);
+  }
+  if (L.ec) rex.probs_t = reinterpret_cast<float*>(w + L.off_probs_t);
   void* h_save = sv != nullptr ? sv->h : nullptr;
   void* xin = w + L.off_xin;
   void* xout = w + L.off_xout;
@@ -487,7 +528,7 @@ static switch_status moe_forward(const switch_moe_desc* desc, const switch_moe_i
   if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
   int32_t* rank = L.fused ? reinterpret_cast<int32_t*>(w + L.off_rank) : nullptr;
   e = launch_route(L.route, in->x, in->w_gate, in->bias, d.T, d.d_model, d.N, d.dtype, out->expert_id, out->gate,
-                   out->routed_count, out->f, out->P, out->l_aux, w + L.off_route, st, rank, probs);
+                   out->routed_count, out->f, out->P, out->l_aux, w + L.off_route, st, rank, rex);
   if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/route");
   if ((e = mark(1)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
   if (L.fused) {
@@ -503,8 +544,19 @@ static switch_status moe_forward(const switch_moe_desc* desc, const switch_moe_i
     e = launch_ffn(L.ffn, in->x, in->w1, in->w2, d.dtype, d.N, C, d.d_model, d.d_ff, out->kept_count, active, nact,
                    xout, w + L.off_ffn, st, tos, d.T, h_save);
   } else {
-    e = launch_assign(L.assign, out->expert_id, out->gate, d.T, d.N, C, d.priority, out->slot, tos, out->kept_count,
-                      out->n_dropped, active, nact, w + L.off_assign, st);
+    if (L.ec) {
+      e = launch_ec_select(rex.probs_t, d.T, d.N, C, tos, reinterpret_cast<int32_t*>(w + L.off_pick),
+                           out->kept_count, active, nact, out->n_dropped, st);
+    } else if (L.K > 1) {
+      // rank the K T assignments as one list, then back to token rows and [T, K] slots
+      int32_t* slot_v = reinterpret_cast<int32_t*>(w + L.off_slotv);
+      e = launch_assign(L.assign, rex.ev_cm, rex.gv_cm, (int64_t)L.K * d.T, d.N, C, d.priority, slot_v, tos,
+                        out->kept_count, out->n_dropped, active, nact, w + L.off_assign, st);
+      if (e == hipSuccess) e = launch_topk_fixup(slot_v, d.T, L.K, tos, (int64_t)d.N * C, out->slot, st);
+    } else {
+      e = launch_assign(L.assign, out->expert_id, out->gate, d.T, d.N, C, d.priority, out->slot, tos,
+                        out->kept_count, out->n_dropped, active, nact, w + L.off_assign, st);
+    }
     if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/assign");
     if ((e = mark(2)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
     e = launch_dispatch(in->x, d.dtype, d.T, d.d_model, tos, out->kept_count, d.N, C, xin, st);
@@ -526,8 +578,16 @@ static switch_status moe_forward(const switch_moe_desc* desc, const switch_moe_i
     if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/shared_ffn");
   }
   if ((e = mark(5)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
-  e = launch_combine(xout, in->x, sout, d.dtype, d.T, d.d_model, out->expert_id, out->slot, out->gate, d.N, C,
-                     d.flags, out->y, st);
+  if (L.ec)
+    e = launch_combine_picks(1, xout, in->x, sout, d.dtype, d.T, d.d_model, 1, nullptr, nullptr, nullptr,
+                             reinterpret_cast<const int32_t*>(w + L.off_pick), rex.probs_t, d.N, C, d.flags,
+                             out->slot, out->n_dropped, out->y, st);
+  else if (L.K > 1)
+    e = launch_combine_picks(0, xout, in->x, sout, d.dtype, d.T, d.d_model, L.K, out->expert_id, out->slot,
+                             out->gate, nullptr, nullptr, d.N, C, d.flags, nullptr, nullptr, out->y, st);
+  else
+    e = launch_combine(xout, in->x, sout, d.dtype, d.T, d.d_model, out->expert_id, out->slot, out->gate, d.N, C,
+                       d.flags, out->y, st);
   if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/combine");
   if ((e = mark(6)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
   return ok();
@@ -574,6 +634,8 @@ static switch_status moe_backward(const switch_moe_desc* desc, const switch_moe_
   if (saved == nullptr) return fail(SWITCH_E_NULL, "saved is NULL");
   if (grads == nullptr) return fail(SWITCH_E_NULL, "grads is NULL");
   const switch_moe_desc& d = *desc;
+  if (d.top_k > 1 || d.routing != SWITCH_TOKEN_CHOICE)
+    return fail(SWITCH_E_UNSUPPORTED, "the backward supports top-1 routing only");
   const bool gate_scale = (d.flags & SWITCH_GATE_SCALE) != 0;
   REQUIRE_PTR(in->x);
   REQUIRE_PTR(in->w_gate);

@@ -21,11 +21,26 @@ RoutePlan route_plan(int64_t T, int d, int N, int dtype);
 // local_rank == NULL: statistics (routed_count, f, P, l_aux) by a final reduction
 // kernel; else every token's rank inside its tile is written and the statistics
 // are left to launch_route_assign_token
-// probs != NULL: the softmax of every token is written too ([T, N] fp32)
+// Router options beyond top-1:
+//   probs != NULL: the softmax of every token is written too ([T, N] fp32);
+//   K > 1: top-K choices, expert_id / gate are [T, K] (t * K + j), routed_count
+//          counts all K T assignments and f_i = count_i / (K T); renorm divides
+//          each token's K gates by their sum;
+//   ev_cm / gv_cm != NULL: the choices and gates also in choice-major order
+//          ([K, T]: j * T + t), the "virtual token" list the slot assignment ranks.
+constexpr int kMaxTopK = 8;
+struct RouteExtra {
+  float* probs = nullptr;
+  float* probs_t = nullptr;  // the softmax transposed, [N, T] (expert choice)
+  int K = 1;
+  int renorm = 0;
+  int32_t* ev_cm = nullptr;
+  float* gv_cm = nullptr;
+};
 hipError_t launch_route(const RoutePlan& pl, const void* x, const void* wg, const float* bias, int64_t T, int d, int N,
                         int dtype, int32_t* expert_id, float* gate, int32_t* routed_count, float* f, float* P,
                         float* l_aux, char* ws, hipStream_t st, int32_t* local_rank = nullptr,
-                        float* probs = nullptr);
+                        const RouteExtra& ex = RouteExtra{});
 // token-order slots from the router's tiles (after launch_route with local_rank);
 // off: int32 [nblk x N] scratch
 hipError_t launch_route_assign_token(const RoutePlan& pl, int64_t T, int N, int C, const int32_t* expert_id,
@@ -138,6 +153,25 @@ hipError_t launch_router_bwd_mfma(const RouterBwdPlan& p, const float* dlogit, c
                                   const int32_t* slot, int64_t T, int d, int N, int C, int residual_all,
                                   uint16_t* hi, uint16_t* lo, float* partial, float* dw_gate, void* dx,
                                   hipStream_t st);
+
+// ---------------- routing variants ----------------
+// top-K: slots [T, K] from the ranks of the virtual-token list; token_of_slot
+// virtual indices -> token rows (in place)
+hipError_t launch_topk_fixup(const int32_t* slot_v, int64_t T, int K, int32_t* tos, int64_t NC, int32_t* slot,
+                             hipStream_t st);
+// expert choice: each expert's min(C, T) highest-probability tokens from the
+// transposed softmax; pick [T, N] (slot or -1), n_dropped zeroed for the combine
+constexpr int kMaxExpertChoiceK = 8192;
+hipError_t launch_ec_select(const float* probs_t, int64_t T, int N, int C, int32_t* tos, int32_t* pick,
+                            int32_t* kept_count, int32_t* active, int32_t* n_active, int32_t* n_dropped,
+                            hipStream_t st);
+// combine over each token's picks: mode 0 top-K ([T, K] ids, slots, gates),
+// mode 1 expert choice (pick [T, N], gates from probs_t; writes npick [T] and
+// counts unpicked tokens into n_dropped)
+hipError_t launch_combine_picks(int mode, const void* expert_out, const void* x, const void* shared_out, int dtype,
+                                int64_t T, int d, int K, const int32_t* eid, const int32_t* slot, const float* gate,
+                                const int32_t* pick, const float* probs_t, int N, int C, uint32_t flags,
+                                int32_t* npick, int32_t* n_dropped, void* y, hipStream_t st);
 
 inline size_t align_up(size_t v, size_t a = 256) { return (v + a - 1) / a * a; }
 

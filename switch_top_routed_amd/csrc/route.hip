@@ -39,7 +39,7 @@ template <int J>
 __device__ void route_epilogue(float* lg, int ldl, int rows, int64_t t0, int64_t T, int N,
                                const float* __restrict__ bias, int32_t* __restrict__ expert_id,
                                float* __restrict__ gate, float* __restrict__ part_p, int32_t* __restrict__ part_cnt,
-                               int32_t* __restrict__ local_rank, int64_t blk, float* __restrict__ probs) {
+                               int32_t* __restrict__ local_rank, int64_t blk, const RouteExtra& ex) {
   __shared__ int tile_e[64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   float bs[J], ps[J];
@@ -67,6 +67,9 @@ __device__ void route_epilogue(float* lg, int ldl, int rows, int64_t t0, int64_t
       }
     }
     wave_argmax(best, bi);
+    float lv[J];  // logits, kept for the further choices of top-K
+#pragma unroll
+    for (int j = 0; j < J; ++j) lv[j] = v[j];
     float s = 0.f;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
@@ -81,12 +84,65 @@ __device__ void route_epilogue(float* lg, int ldl, int rows, int64_t t0, int64_t
       const int n = lane + 64 * j;
       ps[j] += v[j] * inv;
       cn[j] += (n == bi) ? 1 : 0;
-      if (probs != nullptr && n < N) probs[t * N + n] = v[j] * inv;
+      if (ex.probs != nullptr && n < N) ex.probs[t * N + n] = v[j] * inv;
+      if (ex.probs_t != nullptr && n < N) ex.probs_t[(int64_t)n * T + t] = v[j] * inv;
     }
-    if (lane == 0) {
-      expert_id[t] = bi;
-      gate[t] = inv;
-      tile_e[m] = bi;
+    if (ex.K <= 1) {
+      if (lane == 0) {
+        expert_id[t] = bi;
+        gate[t] = inv;
+        tile_e[m] = bi;
+        if (ex.ev_cm != nullptr) {
+          ex.ev_cm[t] = bi;
+          ex.gv_cm[t] = inv;
+        }
+      }
+    } else {
+      // top-K: choice r is the largest logit not chosen yet (ties to the lower
+      // index); its gate is p at that expert
+      int ek[kMaxTopK];
+      float gk[kMaxTopK];
+      ek[0] = bi;
+      gk[0] = inv;
+      float gsum = inv;
+      for (int r = 1; r < ex.K; ++r) {
+        float bv = -INFINITY;
+        int bx = 0x7fffffff;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+          const int n = lane + 64 * j;
+          bool taken = n >= N;
+          for (int q = 0; q < r; ++q) taken = taken || (ek[q] == n);
+          if (!taken && lv[j] > bv) {
+            bv = lv[j];
+            bx = n;
+          }
+        }
+        wave_argmax(bv, bx);
+        // p of the chosen expert, from the lane that holds it
+        float mine = 0.f;
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+          if (lane + 64 * j == bx) mine = v[j] * inv;
+        const float pr = __shfl(mine, bx & 63, 64);
+#pragma unroll
+        for (int j = 0; j < J; ++j) cn[j] += (lane + 64 * j == bx) ? 1 : 0;
+        ek[r] = bx;
+        gk[r] = pr;
+        gsum += pr;
+      }
+      if (lane == 0) {
+        const float rn = ex.renorm ? 1.0f / gsum : 1.0f;
+        for (int r = 0; r < ex.K; ++r) {
+          const float g = ex.renorm ? gk[r] * rn : gk[r];
+          expert_id[t * ex.K + r] = ek[r];
+          gate[t * ex.K + r] = g;
+          if (ex.ev_cm != nullptr) {
+            ex.ev_cm[(int64_t)r * T + t] = ek[r];
+            ex.gv_cm[(int64_t)r * T + t] = g;
+          }
+        }
+      }
     }
   }
   __syncthreads();  // every wave is done reading the logits; tile_e is complete
@@ -122,7 +178,7 @@ template <int TM, int NG, int J>
 __global__ __launch_bounds__(kRouteThreads) void route_fused_bf16(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg, const float* __restrict__ bias, int64_t T, int d,
     int N, int32_t* __restrict__ expert_id, float* __restrict__ gate, float* __restrict__ part_p,
-    int32_t* __restrict__ part_cnt, int32_t* __restrict__ local_rank, float* __restrict__ probs) {
+    int32_t* __restrict__ part_cnt, int32_t* __restrict__ local_rank, RouteExtra ex) {
   extern __shared__ float smem[];
   const int NT = (N + 15) >> 4;
   const int ldl = NT * 16;
@@ -198,7 +254,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_fused_bf16(
       }
   }
   __syncthreads();
-  route_epilogue<J>(lg, ldl, TM * 16, t0, T, N, bias, expert_id, gate, part_p, part_cnt, local_rank, blockIdx.x, probs);
+  route_epilogue<J>(lg, ldl, TM * 16, t0, T, N, bias, expert_id, gate, part_p, part_cnt, local_rank, blockIdx.x, ex);
 }
 
 // ----------------------------------------------------------------------------
@@ -260,7 +316,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_softmax_split(const float
                                                                      float* __restrict__ gate,
                                                                      float* __restrict__ part_p,
                                                                      int32_t* __restrict__ part_cnt,
-                                                                     int32_t* __restrict__ local_rank, float* __restrict__ probs) {
+                                                                     int32_t* __restrict__ local_rank, RouteExtra ex) {
   // one token per workgroup: its N logits are sums over the S k-chunks, in
   // chunk order, with 8 independent loads in flight per expert
   extern __shared__ float smem[];
@@ -282,7 +338,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_softmax_split(const float
     lg[n] = v;
   }
   __syncthreads();
-  route_epilogue<J>(lg, N, 1, t, T, N, bias, expert_id, gate, part_p, part_cnt, local_rank, blockIdx.x, probs);
+  route_epilogue<J>(lg, N, 1, t, T, N, bias, expert_id, gate, part_p, part_cnt, local_rank, blockIdx.x, ex);
 }
 
 // ----------------------------------------------------------------------------
@@ -294,7 +350,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_f32(const float* __restri
                                                            int32_t* __restrict__ expert_id, float* __restrict__ gate,
                                                            float* __restrict__ part_p,
                                                            int32_t* __restrict__ part_cnt,
-                                                           int32_t* __restrict__ local_rank, float* __restrict__ probs) {
+                                                           int32_t* __restrict__ local_rank, RouteExtra ex) {
   extern __shared__ float smem[];
   const int ldl = N;
   float* lg = smem;
@@ -311,7 +367,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_f32(const float* __restri
     lg[m * ldl + n] = acc;
   }
   __syncthreads();
-  route_epilogue<J>(lg, ldl, 16, t0, T, N, bias, expert_id, gate, part_p, part_cnt, local_rank, blockIdx.x, probs);
+  route_epilogue<J>(lg, ldl, 16, t0, T, N, bias, expert_id, gate, part_p, part_cnt, local_rank, blockIdx.x, ex);
 }
 
 // ----------------------------------------------------------------------------
@@ -332,7 +388,7 @@ __device__ __forceinline__ void finalize_partials(const float* __restrict__ part
                                                   const int32_t* __restrict__ part_cnt, int64_t nblk, int64_t T,
                                                   int N, int NP, int32_t* __restrict__ routed_count,
                                                   float* __restrict__ f, float* __restrict__ P,
-                                                  float* __restrict__ l_aux, int* cnt_out) {
+                                                  float* __restrict__ l_aux, int* cnt_out, int K = 1) {
   __shared__ double sp[1024];
   __shared__ double sl[1024];
   const int tid = threadIdx.x;
@@ -370,7 +426,7 @@ __device__ __forceinline__ void finalize_partials(const float* __restrict__ part
       s += sp[i * NP + tid];
       cnum += cnt_out[i * NP + tid];
     }
-    const double fn = (double)cnum / (double)T;
+    const double fn = (double)cnum / ((double)K * (double)T);  // K assignments per token
     const double pn = s / (double)T;
     routed_count[tid] = (int32_t)cnum;
     f[tid] = (float)fn;
@@ -390,9 +446,9 @@ __global__ __launch_bounds__(1024) void route_finalize(const float* __restrict__
                                                        const int32_t* __restrict__ part_cnt, int64_t nblk, int64_t T,
                                                        int N, int NP, int32_t* __restrict__ routed_count,
                                                        float* __restrict__ f, float* __restrict__ P,
-                                                       float* __restrict__ l_aux) {
+                                                       float* __restrict__ l_aux, int K) {
   __shared__ int cnt[1024];
-  finalize_partials(part_p, part_cnt, nblk, T, N, NP, routed_count, f, P, l_aux, cnt);
+  finalize_partials(part_p, part_cnt, nblk, T, N, NP, routed_count, f, P, l_aux, cnt, K);
 }
 
 // Token-order capacity and slots straight from the router's tiles (one
@@ -527,7 +583,8 @@ RoutePlan route_plan(int64_t T, int d, int N, int dtype) {
 template <int J>
 static hipError_t launch_route_j(const RoutePlan& pl, const void* x, const void* wg, const float* bias, int64_t T,
                                  int d, int N, int dtype, int32_t* expert_id, float* gate, float* part_p,
-                                 int32_t* part_cnt, int32_t* local_rank, char* ws, hipStream_t st, float* probs) {
+                                 int32_t* part_cnt, int32_t* local_rank, char* ws, hipStream_t st,
+                                 const RouteExtra& ex) {
   if (dtype == 1 && pl.split == 0) {
     const int NT = (N + 15) / 16;
     const size_t lds = (size_t)pl.tm * 16 * NT * 16 * 4;
@@ -536,13 +593,13 @@ static hipError_t launch_route_j(const RoutePlan& pl, const void* x, const void*
     auto* wb = static_cast<const uint16_t*>(wg);
     if (pl.tm == 4)
       hipLaunchKernelGGL((route_fused_bf16<4, 2, J>), grid, dim3(kRouteThreads), lds, st, xb, wb, bias, T, d, N,
-                         expert_id, gate, part_p, part_cnt, local_rank, probs);
+                         expert_id, gate, part_p, part_cnt, local_rank, ex);
     else if (pl.tm == 2)
       hipLaunchKernelGGL((route_fused_bf16<2, 2, J>), grid, dim3(kRouteThreads), lds, st, xb, wb, bias, T, d, N,
-                         expert_id, gate, part_p, part_cnt, local_rank, probs);
+                         expert_id, gate, part_p, part_cnt, local_rank, ex);
     else
       hipLaunchKernelGGL((route_fused_bf16<1, 2, J>), grid, dim3(kRouteThreads), lds, st, xb, wb, bias, T, d, N,
-                         expert_id, gate, part_p, part_cnt, local_rank, probs);
+                         expert_id, gate, part_p, part_cnt, local_rank, ex);
   } else if (dtype == 1) {
     float* plog = reinterpret_cast<float*>(ws + pl.off_logits);
     hipLaunchKernelGGL((route_logits_split_bf16<2>), dim3((unsigned)((T + 15) / 16), (unsigned)pl.split), dim3(kRouteThreads),
@@ -552,33 +609,33 @@ static hipError_t launch_route_j(const RoutePlan& pl, const void* x, const void*
     if (e != hipSuccess) return e;
     const size_t lds = (size_t)8 * N * 4;  // the epilogue reuses it for the cross-wave partials
     hipLaunchKernelGGL(route_softmax_split<J>, dim3((unsigned)pl.nblk), dim3(kRouteThreads), lds, st, plog, pl.split,
-                       T, N, bias, expert_id, gate, part_p, part_cnt, local_rank, probs);
+                       T, N, bias, expert_id, gate, part_p, part_cnt, local_rank, ex);
   } else {
     const size_t lds = (size_t)16 * N * 4;
     hipLaunchKernelGGL(route_f32<J>, dim3((unsigned)pl.nblk), dim3(kRouteThreads), lds, st,
                        static_cast<const float*>(x), static_cast<const float*>(wg), bias, T, d, N, expert_id, gate,
-                       part_p, part_cnt, local_rank, probs);
+                       part_p, part_cnt, local_rank, ex);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_route(const RoutePlan& pl, const void* x, const void* wg, const float* bias, int64_t T, int d, int N,
                         int dtype, int32_t* expert_id, float* gate, int32_t* routed_count, float* f, float* P,
-                        float* l_aux, char* ws, hipStream_t st, int32_t* local_rank, float* probs) {
+                        float* l_aux, char* ws, hipStream_t st, int32_t* local_rank, const RouteExtra& ex) {
   float* part_p = reinterpret_cast<float*>(ws + pl.off_part_p);
   int32_t* part_cnt = reinterpret_cast<int32_t*>(ws + pl.off_part_cnt);
   hipError_t e;
   if (N <= 128)
-    e = launch_route_j<2>(pl, x, wg, bias, T, d, N, dtype, expert_id, gate, part_p, part_cnt, local_rank, ws, st, probs);
+    e = launch_route_j<2>(pl, x, wg, bias, T, d, N, dtype, expert_id, gate, part_p, part_cnt, local_rank, ws, st, ex);
   else if (N <= 512)
-    e = launch_route_j<8>(pl, x, wg, bias, T, d, N, dtype, expert_id, gate, part_p, part_cnt, local_rank, ws, st, probs);
+    e = launch_route_j<8>(pl, x, wg, bias, T, d, N, dtype, expert_id, gate, part_p, part_cnt, local_rank, ws, st, ex);
   else
-    e = launch_route_j<16>(pl, x, wg, bias, T, d, N, dtype, expert_id, gate, part_p, part_cnt, local_rank, ws, st, probs);
+    e = launch_route_j<16>(pl, x, wg, bias, T, d, N, dtype, expert_id, gate, part_p, part_cnt, local_rank, ws, st, ex);
   if (e != hipSuccess) return e;
   if (local_rank != nullptr) return hipSuccess;  // the statistics come from launch_route_assign_token
   const int NP = (N + 63) / 64 * 64;
   hipLaunchKernelGGL(route_finalize, dim3(1), dim3(1024), 0, st, part_p, part_cnt, pl.nblk, T, N, NP, routed_count, f,
-                     P, l_aux);
+                     P, l_aux, ex.K < 1 ? 1 : ex.K);
   return hipGetLastError();
 }
 

@@ -21,7 +21,9 @@ HEADER = os.path.join(os.path.dirname(_PKG), "include", "switch_moe.h")
 
 F32, BF16 = 0, 1
 TOKEN_ORDER, GATE_DESC = 0, 1
-GATE_SCALE, RESIDUAL_ALL = 1, 2
+GATE_SCALE, RESIDUAL_ALL, RENORM = 1, 2, 4
+TOKEN_CHOICE, EXPERT_CHOICE = 0, 1
+_ROUTING = {"token": TOKEN_CHOICE, "expert": EXPERT_CHOICE, TOKEN_CHOICE: TOKEN_CHOICE, EXPERT_CHOICE: EXPERT_CHOICE}
 _DT = {torch.float32: F32, torch.bfloat16: BF16}
 _PRIO = {"token": TOKEN_ORDER, "gate": GATE_DESC, TOKEN_ORDER: TOKEN_ORDER, GATE_DESC: GATE_DESC}
 
@@ -32,7 +34,7 @@ _i32, _i64, _u32, _f64, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, c
 class SwitchMoeDesc(ctypes.Structure):
     _fields_ = [("T", _i64), ("d_model", _i32), ("d_ff", _i32), ("N", _i32), ("C", _i32),
                 ("capacity_factor", _f64), ("dtype", _i32), ("priority", _i32), ("flags", _u32),
-                ("d_ff_shared", _i32)]
+                ("d_ff_shared", _i32), ("top_k", _i32), ("routing", _i32)]
 
 
 class SwitchMoeInputs(ctypes.Structure):
@@ -296,21 +298,27 @@ class SwitchMoE:
     """The whole layer with its outputs and workspace preallocated (one call = switch_moe_forward)."""
 
     def __init__(self, T, d_model, d_ff, N, *, dtype=torch.bfloat16, capacity_factor=1.0, C=0, priority="token",
-                 gate_scale=True, residual_all=False, d_ff_shared=0, device="cuda", train=False):
+                 gate_scale=True, residual_all=False, d_ff_shared=0, device="cuda", train=False, top_k=1,
+                 routing="token", renorm=False):
+        """top_k > 1: top-K token choice; routing="expert": expert choice (see include/switch_moe.h).
+        With top-K, out["expert_id"], out["gate"] and out["slot"] are [T, K]."""
         self.desc = SwitchMoeDesc(T=T, d_model=d_model, d_ff=d_ff, N=N, C=C, capacity_factor=capacity_factor,
                                   dtype=_DT[dtype], priority=_PRIO[priority],
-                                  flags=(GATE_SCALE if gate_scale else 0) | (RESIDUAL_ALL if residual_all else 0),
-                                  d_ff_shared=d_ff_shared)
+                                  flags=(GATE_SCALE if gate_scale else 0) | (RESIDUAL_ALL if residual_all else 0)
+                                  | (RENORM if renorm else 0),
+                                  d_ff_shared=d_ff_shared, top_k=top_k, routing=_ROUTING[routing])
+        K = max(1, top_k)
         L = lib()
         nb = L.switch_moe_workspace_bytes(ctypes.byref(self.desc))
         if nb == 0:
             raise ValueError("invalid layer description (switch_moe_workspace_bytes returned 0): "
                              + L.switch_last_error().decode())
-        self.C = C if C else switch_capacity(T, N, capacity_factor)
+        self.C = C if C else min(T, switch_capacity(K * T, N, capacity_factor))
         dev = torch.device(device)
         self.ws = torch.empty(nb, dtype=torch.uint8, device=dev)
-        self.out = dict(y=_empty((T, d_model), dtype, dev), expert_id=_empty(T, torch.int32, dev),
-                        gate=_empty(T, torch.float32, dev), slot=_empty(T, torch.int32, dev),
+        tk = (T, K) if K > 1 else (T,)
+        self.out = dict(y=_empty((T, d_model), dtype, dev), expert_id=_empty(tk, torch.int32, dev),
+                        gate=_empty(tk, torch.float32, dev), slot=_empty(tk, torch.int32, dev),
                         routed_count=_empty(N, torch.int32, dev), kept_count=_empty(N, torch.int32, dev),
                         n_dropped=_empty(1, torch.int32, dev), f=_empty(N, torch.float32, dev),
                         P=_empty(N, torch.float32, dev), l_aux=_empty(1, torch.float32, dev))

@@ -52,3 +52,53 @@ def conditioned_inputs(wl, *, weights=True, gate_order_cmax=None, threads=8):
     """Inputs with the margin rule (and the gate-gap rule if gate_order_cmax is set)."""
     pred = margin_bad_rows if gate_order_cmax is None else gate_gap_bad_rows(gate_order_cmax)
     return workloads.make_inputs(wl, weights=weights, bad_rows=pred, threads=threads)
+
+
+# ---------------------------------------------------------------------------
+# routing variants (top-K token choice, expert choice)
+# ---------------------------------------------------------------------------
+def topk_margin_bad_rows(K):
+    """Rows whose top K + 1 logits are not 1e-3 apart (the K choices and their order)."""
+    def bad(inp):
+        l, _, _, _ = stored_router(inp)
+        top = -np.sort(-l, axis=1)[:, : min(K + 1, l.shape[1])]
+        return np.nonzero((top[:, :-1] - top[:, 1:] < MARGIN).any(axis=1))[0]
+    return bad
+
+
+def topk_gate_gap_bad_rows(K, c_max, gap=GATE_GAP):
+    """Also, for gate-descending slots: inside each expert's assignment list, the
+    c_max + 1 highest gates must be a relative `gap` apart."""
+    from oracle import routing as orr
+    margin = topk_margin_bad_rows(K)
+
+    def bad(inp):
+        rows = set(margin(inp).tolist())
+        dt = inp.wl.dtype
+        _, _, e, g = orr.route_topk(oracle.widen(inp.x, dt), oracle.widen(inp.w_gate, dt), inp.bias, K)
+        T = e.shape[0]
+        ev, gv = e.T.ravel(), g.T.ravel()
+        for i in np.unique(ev):
+            vs = np.nonzero(ev == i)[0]
+            vs = vs[np.lexsort((vs, -gv[vs]))][: c_max + 1]
+            gg = gv[vs]
+            close = (gg[:-1] - gg[1:]) < gap * gg[:-1]
+            rows.update((vs[1:][close] % T).tolist())
+        return np.array(sorted(rows), dtype=np.int64)
+    return bad
+
+
+def expert_choice_bad_rows(C, gap=GATE_GAP):
+    """Expert choice: for every expert, its C + 1 highest probabilities must be a
+    relative `gap` apart (which tokens it takes, and their slot order)."""
+    def bad(inp):
+        rows = set(margin_bad_rows(inp).tolist())
+        _, p, _, _ = stored_router(inp)
+        T = p.shape[0]
+        for i in range(p.shape[1]):
+            ts = np.lexsort((np.arange(T), -p[:, i]))[: C + 1]
+            pp = p[ts, i]
+            close = (pp[:-1] - pp[1:]) < gap * pp[:-1]
+            rows.update(ts[1:][close].tolist())
+        return np.array(sorted(rows), dtype=np.int64)
+    return bad

@@ -1,0 +1,202 @@
+"""GPU parity of the routing variants (top-K token choice, expert choice)
+through switch_moe_forward against the fp64 oracle on the same seeded inputs.
+
+Bars as for top-1: integer results (choices, slots, token_of_slot through
+kept_count, counts, n_dropped) bit-exact; gates and P relative 1e-5; f exact;
+outputs per token max_k |y - y_ref| / max_k |y_ref| <= 1e-4 (fp32) or 2e-2
+(bf16); tokens without a kept pick bit-identical to x.  Inputs are
+conditioned so that every choice, selection and slot order is decided by
+margins far above fp32 rounding (tests/inputs_util.py).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from oracle import routing as orr
+from tests import inputs_util
+from tests.gpu_util import TOL_OUT, TOL_P, dev, host, host_bits, row_rel
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from switch_top_routed_amd import native
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _custom(name, T, d, dff, N, cf, dtype="bf16", seed=0, **kw):
+    return workloads.Workload(name, T, d, dff, N, cf, dtype, 1.0 / math.sqrt(d), seed=30_000 + seed, **kw)
+
+
+def _devs(inp, dt):
+    return dict(x=dev(inp.x, dt), w_gate=dev(inp.w_gate, dt), w1=dev(inp.w1, dt), w2=dev(inp.w2, dt),
+                bias=None if inp.bias is None else torch.from_numpy(inp.bias).cuda(), ws1=dev(inp.ws1, dt),
+                ws2=dev(inp.ws2, dt))
+
+
+def _run(wl, d, **kw):
+    layer = native.SwitchMoE(wl.T, wl.d_model, wl.d_ff, wl.N,
+                             dtype=torch.bfloat16 if wl.dtype == "bf16" else torch.float32,
+                             capacity_factor=wl.capacity_factor, priority=wl.priority, gate_scale=wl.gate_scale,
+                             residual_all=wl.residual_all, d_ff_shared=wl.d_ff_shared, **kw)
+    out = layer(d["x"], d["w_gate"], d["w1"], d["w2"], bias=d["bias"], ws1=d["ws1"], ws2=d["ws2"])
+    torch.cuda.synchronize()
+    return layer, out
+
+
+def _widened(inp):
+    dt = inp.wl.dtype
+    ws1 = oracle.widen(inp.ws1, dt) if inp.ws1 is not None else None
+    ws2 = oracle.widen(inp.ws2, dt) if inp.ws2 is not None else None
+    return (oracle.widen(inp.x, dt), oracle.widen(inp.w_gate, dt), lambda e: oracle.widen(inp.w1[e], dt),
+            lambda e: oracle.widen(inp.w2[e], dt), ws1, ws2)
+
+
+def _check_y(y_dev, ref_y, x_stored, passed, dtype, shared):
+    y = host(y_dev)
+    tol = TOL_OUT[dtype]
+    idx = np.arange(len(passed))
+    live = idx[~passed]
+    if live.size:
+        r = row_rel(y[live], ref_y[live])
+        assert r.max() <= tol, f"max row rel err {r.max():.3g} > {tol} (token {live[r.argmax()]})"
+    if passed.any():
+        if shared:
+            r = row_rel(y[passed], ref_y[passed])
+            assert r.max() <= tol
+        else:
+            xs = x_stored.view(np.uint32) if x_stored.dtype == np.float32 else x_stored
+            np.testing.assert_array_equal(host_bits(y_dev)[passed], xs[passed])
+    return float(row_rel(y, ref_y).max())
+
+
+# ---------------------------------------------------------------------------
+# top-K token choice
+# ---------------------------------------------------------------------------
+def _topk_case(wl, K, renorm=False):
+    _say(f"top-{K} {wl.name} T={wl.T} N={wl.N} cf={wl.capacity_factor} {wl.priority} gs={wl.gate_scale} "
+         f"res={wl.residual_all} renorm={renorm} shared={wl.d_ff_shared}")
+    C = min(wl.T, orr.capacity_topk(wl.T, wl.N, K, wl.capacity_factor))
+    pred = (inputs_util.topk_gate_gap_bad_rows(K, C) if wl.priority == "gate"
+            else inputs_util.topk_margin_bad_rows(K))
+    inp = workloads.make_inputs(wl, bad_rows=pred)
+    d = _devs(inp, wl.dtype)
+    layer, out = _run(wl, d, top_k=K, renorm=renorm)
+    x, wg, w1_of, w2_of, ws1, ws2 = _widened(inp)
+    ref = orr.moe_forward_topk(x, wg, inp.bias, w1_of, w2_of, wl.N, K=K, C=C, priority=wl.priority,
+                               gate_scale=wl.gate_scale, residual_all=wl.residual_all, renorm=renorm, ws1=ws1,
+                               ws2=ws2)
+    assert layer.C == C
+    np.testing.assert_array_equal(host(out["expert_id"]), ref["expert_ids"])
+    np.testing.assert_allclose(host(out["gate"]), ref["gates"], rtol=1e-5)
+    np.testing.assert_array_equal(host(out["routed_count"]), ref["routed_count"])
+    np.testing.assert_array_equal(host(out["f"]), ref["f"].astype(np.float32).astype(np.float64))
+    np.testing.assert_allclose(host(out["P"]), ref["P"], rtol=TOL_P, atol=1e-9)
+    assert abs(float(host(out["l_aux"])[0]) - ref["l_aux"]) <= 1e-5 * abs(ref["l_aux"])
+    np.testing.assert_array_equal(host(out["slot"]), ref["slot"])
+    np.testing.assert_array_equal(host(out["kept_count"]), ref["kept_count"])
+    assert int(host(out["n_dropped"])[0]) == ref["n_dropped"]
+    passed = (ref["slot"] < 0).all(axis=1)
+    err = _check_y(out["y"], ref["y"], inp.x, passed, wl.dtype, wl.d_ff_shared > 0)
+    _say(f"  C={C} dropped assignments {ref['n_dropped']} passed-through tokens {int(passed.sum())} y err {err:.2e}")
+
+
+def test_top2_tiny_fp32():
+    _topk_case(workloads.WORKLOADS["switch-tiny-fp32"], 2)
+
+
+def test_top2_base():
+    _topk_case(workloads.WORKLOADS["switch-base-uniform"], 2)
+
+
+@pytest.mark.parametrize("cf,priority,gate_scale,renorm", [(0.5, "token", True, False), (1.0, "gate", True, True),
+                                                           (2.0, "gate", False, False), (1.0, "token", True, True)])
+def test_top2_skewed(cf, priority, gate_scale, renorm):
+    wl = workloads.WORKLOADS["switch-base-zipf"].with_(capacity_factor=cf, priority=priority, gate_scale=gate_scale)
+    _topk_case(wl, 2, renorm)
+
+
+TOPK_EDGE = [
+    (_custom("k3-ragged", 1000, 256, 384, 12, 0.8, seed=1, bias_scale=1.0), 3),
+    (_custom("k2-n19", 700, 128, 128, 19, 1.1, seed=2), 2),
+    (_custom("k2-residual", 512, 256, 256, 8, 0.6, seed=3, residual_all=True), 2),
+    (_custom("k2-shared", 384, 256, 512, 8, 1.0, seed=4, d_ff_shared=256), 2),
+    (_custom("k4-f32-odd", 301, 20, 36, 7, 1.3, dtype="f32", seed=5), 4),
+    (_custom("k8-all-experts", 256, 128, 128, 8, 2.0, seed=6), 8),
+    (_custom("k2-t1", 1, 128, 256, 4, 1.0, seed=7), 2),
+]
+
+
+@pytest.mark.parametrize("wl,K", TOPK_EDGE, ids=[f"{w.name}" for w, _ in TOPK_EDGE])
+def test_topk_edge(wl, K):
+    _topk_case(wl, K)
+
+
+def test_top1_through_topk_field_matches_top1():
+    """top_k = 1 is the Switch layer: bit-identical outputs."""
+    wl = workloads.WORKLOADS["switch-base-uniform"]
+    inp = inputs_util.conditioned_inputs(wl)
+    d = _devs(inp, wl.dtype)
+    _, a = _run(wl, d, top_k=1)
+    a = {k: v.clone() for k, v in a.items()}
+    _, b = _run(wl, d)
+    for k in a:
+        np.testing.assert_array_equal(host_bits(a[k]), host_bits(b[k]), err_msg=k)
+
+
+# ---------------------------------------------------------------------------
+# expert choice
+# ---------------------------------------------------------------------------
+def _ec_case(wl):
+    _say(f"expert choice {wl.name} T={wl.T} N={wl.N} cf={wl.capacity_factor} gs={wl.gate_scale} "
+         f"res={wl.residual_all} shared={wl.d_ff_shared}")
+    C = oracle.capacity(wl.T, wl.N, wl.capacity_factor)
+    inp = workloads.make_inputs(wl, bad_rows=inputs_util.expert_choice_bad_rows(min(C, wl.T)))
+    d = _devs(inp, wl.dtype)
+    layer, out = _run(wl, d, routing="expert")
+    x, wg, w1_of, w2_of, ws1, ws2 = _widened(inp)
+    ref = orr.moe_forward_expert_choice(x, wg, inp.bias, w1_of, w2_of, wl.N, C=C, gate_scale=wl.gate_scale,
+                                        residual_all=wl.residual_all, ws1=ws1, ws2=ws2)
+    top1 = oracle.route(x, wg, inp.bias)
+    np.testing.assert_array_equal(host(out["expert_id"]), top1[2])
+    np.testing.assert_array_equal(host(out["kept_count"]), ref["kept_count"])
+    npick = (ref["pick"] >= 0).sum(axis=1)
+    np.testing.assert_array_equal(host(out["slot"]), npick)
+    assert int(host(out["n_dropped"])[0]) == int((npick == 0).sum())
+    # token_of_slot is internal here; the slot order shows in which rows y mixes, and
+    # the oracle's selection is checked through y and the pick counts
+    passed = npick == 0
+    err = _check_y(out["y"], ref["y"], inp.x, passed, wl.dtype, wl.d_ff_shared > 0)
+    _say(f"  C={C} tokens taken by no expert {int(passed.sum())}, max picks {int(npick.max())}, y err {err:.2e}")
+
+
+def test_expert_choice_tiny_fp32():
+    _ec_case(workloads.WORKLOADS["switch-tiny-fp32"])
+
+
+def test_expert_choice_base():
+    _ec_case(workloads.WORKLOADS["switch-base-uniform"])
+
+
+@pytest.mark.parametrize("cf,gate_scale", [(0.5, True), (2.0, False)])
+def test_expert_choice_skewed(cf, gate_scale):
+    _ec_case(workloads.WORKLOADS["switch-base-zipf"].with_(capacity_factor=cf, gate_scale=gate_scale))
+
+
+EC_EDGE = [
+    _custom("ec-ragged", 1000, 256, 384, 12, 1.1, seed=11, bias_scale=1.0),
+    _custom("ec-residual-shared", 384, 256, 512, 8, 0.7, seed=12, residual_all=True, d_ff_shared=256),
+    _custom("ec-f32-odd", 301, 20, 36, 7, 1.3, dtype="f32", seed=13),
+    _custom("ec-c-exceeds-t", 40, 128, 128, 4, 8.0, seed=14),
+]
+
+
+@pytest.mark.parametrize("wl", EC_EDGE, ids=[w.name for w in EC_EDGE])
+def test_expert_choice_edge(wl):
+    _ec_case(wl)
