@@ -92,6 +92,9 @@ def parse():
     ap.add_argument("--capacity-factor", type=float, default=None, help="override the workload's capacity factor")
     ap.add_argument("--priority", choices=("token", "gate"), default=None, help="override the overflow priority")
     ap.add_argument("--no-gate-scale", action="store_true", help="combine without the gate multiplier")
+    ap.add_argument("--top-k", type=int, default=1, help="token choice with K experts per token")
+    ap.add_argument("--routing", choices=("token", "expert"), default="token", help="token choice or expert choice")
+    ap.add_argument("--renorm", action="store_true", help="top-K: divide each token's gates by their sum")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the layer backward measurement")
     ap.add_argument("--backward-steps", type=int, default=None,
@@ -171,9 +174,13 @@ def main():
     else:
         w1, w2, ws1, ws2 = dev(inp.w1), dev(inp.w2), dev(inp.ws1), dev(inp.ws2)
     bias = None if inp.bias is None else torch.from_numpy(inp.bias).cuda()
+    variant = args.top_k > 1 or args.routing != "token"
+    if variant:
+        over["top_k"] = args.top_k
+        over["routing"] = args.routing
     layer = sw.SwitchMoE(wl.T, wl.d_model, wl.d_ff, wl.N, dtype=dt, capacity_factor=wl.capacity_factor,
                          priority=wl.priority, gate_scale=wl.gate_scale, residual_all=wl.residual_all,
-                         d_ff_shared=wl.d_ff_shared)
+                         d_ff_shared=wl.d_ff_shared, top_k=args.top_k, routing=args.routing, renorm=args.renorm)
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -206,13 +213,15 @@ def main():
     n_active = int((out["kept_count"] > 0).sum().item())
     T, d, F, N, C = wl.T, wl.d_model, wl.d_ff, wl.N, layer.C
     dropped = T - kept
-    # the library's token-order forward folds the dispatch into GEMM 1 (same rule as its workspace layout)
-    gathered = wl.priority == "token" and T * d * esz < 2 ** 31
+    # the library's top-1 token-order forward folds the dispatch into GEMM 1 (same rule as its workspace layout)
+    gathered = not variant and wl.priority == "token" and T * d * esz < 2 ** 31
     route_bytes = T * d * esz + N * d * esz + T * 8 + N * 16
     disp_bytes = 2 * kept * d * esz + 4 * kept
     # combine: one row read per token (expert output if kept, x if dropped), one row written,
     # plus the shared-expert row when there is one, and expert id, slot and gate per token
     comb_bytes = 2 * T * d * esz + (T * d * esz if wl.d_ff_shared else 0) + T * 12
+    if variant:  # every kept pick's expert row, every x row, every y row
+        comb_bytes = (kept + 2 * T) * d * esz + (T * d * esz if wl.d_ff_shared else 0)
     ffn_launch_bytes = n_active * d * F * esz + kept * (d + F) * esz  # one GEMM launch
     ffn_flops = 4.0 * kept * d * F
 
@@ -258,10 +267,10 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline and not on_device:
-        cpu = cpu_baseline(inp, args.cpu_seconds)
+        cpu = cpu_baseline(inp, args.cpu_seconds, args.top_k, args.routing, args.renorm)
 
     backward = None
-    if not args.no_backward:
+    if not args.no_backward and not variant:  # the backward is built for top-1 routing
         backward = measure_backward(args, wl, inp, layer.C, x, wg, w1, w2, bias, ws1, ws2, stream, on_device)
 
     line = {
@@ -270,7 +279,8 @@ def main():
         "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic (seeded Gaussian tokens and weights)",
         "config": {"workload": wl.name, "T": T, "d_model": d, "d_ff": F, "N": N,
                    "capacity_factor": wl.capacity_factor, "C": C, "priority": wl.priority,
-                   "gate_scale": wl.gate_scale, "d_ff_shared": wl.d_ff_shared, "parallelism": "single GPU"},
+                   "gate_scale": wl.gate_scale, "d_ff_shared": wl.d_ff_shared, "parallelism": "single GPU",
+                   "routing": "expert choice" if args.routing == "expert" else f"top-{max(1, args.top_k)}"},
         "roofline": roofline, "stages": stages, "cpu_baseline": cpu, "backward": backward,
     }
     print(json.dumps(line), flush=True)
@@ -407,10 +417,29 @@ def traffic_bytes(workload):
     return sum(per) / len(per)
 
 
-def cpu_baseline(inp, seconds):
-    """The fp64 oracle, as it stands, on the same workload: whole layer passes
-    over the batch, repeated until `seconds` have elapsed (at most 30 passes)."""
+def cpu_baseline(inp, seconds, top_k=1, routing="token", renorm=False):
+    """The fp64 oracle, as it stands, on the same workload (and routing): whole
+    layer passes over the batch, repeated until `seconds` have elapsed (at most
+    30 passes)."""
     import oracle
+    from oracle import routing as orr
+
+    def one_pass():
+        if top_k <= 1 and routing == "token":
+            return oracle.moe_forward_stored(inp)
+        wl, dt = inp.wl, inp.wl.dtype
+        x, wg = oracle.widen(inp.x, dt), oracle.widen(inp.w_gate, dt)
+        w1_of, w2_of = (lambda e: oracle.widen(inp.w1[e], dt)), (lambda e: oracle.widen(inp.w2[e], dt))
+        ws1 = oracle.widen(inp.ws1, dt) if inp.ws1 is not None else None
+        ws2 = oracle.widen(inp.ws2, dt) if inp.ws2 is not None else None
+        if routing == "expert":
+            return orr.moe_forward_expert_choice(x, wg, inp.bias, w1_of, w2_of, wl.N, wl.capacity_factor,
+                                                 gate_scale=wl.gate_scale, residual_all=wl.residual_all,
+                                                 ws1=ws1, ws2=ws2)
+        C = min(wl.T, orr.capacity_topk(wl.T, wl.N, top_k, wl.capacity_factor))
+        return orr.moe_forward_topk(x, wg, inp.bias, w1_of, w2_of, wl.N, K=top_k, C=C, priority=wl.priority,
+                                    gate_scale=wl.gate_scale, residual_all=wl.residual_all, renorm=renorm,
+                                    ws1=ws1, ws2=ws2)
     try:
         from threadpoolctl import threadpool_info
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
@@ -419,14 +448,15 @@ def cpu_baseline(inp, seconds):
     passes = 0
     t0 = time.perf_counter()
     while True:
-        oracle.moe_forward_stored(inp)
+        one_pass()
         passes += 1
         el = time.perf_counter() - t0
         if el >= seconds or passes >= 30:
             break
     return {"value": inp.wl.T * passes / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "seconds": el, "sample": f"{passes} full fp64 layer passes over the {inp.wl.name} batch "
-                                     f"(T={inp.wl.T} tokens each)"}
+                                     f"(T={inp.wl.T} tokens each, "
+                                     f"{'expert choice' if routing == 'expert' else f'top-{max(1, top_k)}'})"}
 
 
 if __name__ == "__main__":
