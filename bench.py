@@ -95,6 +95,8 @@ def parse():
     ap.add_argument("--top-k", type=int, default=1, help="token choice with K experts per token")
     ap.add_argument("--routing", choices=("token", "expert"), default="token", help="token choice or expert choice")
     ap.add_argument("--renorm", action="store_true", help="top-K: divide each token's gates by their sum")
+    ap.add_argument("--weights", choices=("native", "mxfp4"), default="native",
+                    help="expert weights in the layer dtype, or MXFP4 (quantized on the device before timing)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the layer backward measurement")
     ap.add_argument("--backward-steps", type=int, default=None,
@@ -178,13 +180,22 @@ def main():
     if variant:
         over["top_k"] = args.top_k
         over["routing"] = args.routing
+    mxw = args.weights == "mxfp4"
+    w1s = w2s = None
+    if mxw:
+        over["weights"] = "mxfp4"
+        w1, w1s = sw.switch_quantize_mxfp4(w1)
+        w2, w2s = sw.switch_quantize_mxfp4(w2)
+        torch.cuda.synchronize()
     layer = sw.SwitchMoE(wl.T, wl.d_model, wl.d_ff, wl.N, dtype=dt, capacity_factor=wl.capacity_factor,
                          priority=wl.priority, gate_scale=wl.gate_scale, residual_all=wl.residual_all,
-                         d_ff_shared=wl.d_ff_shared, top_k=args.top_k, routing=args.routing, renorm=args.renorm)
+                         d_ff_shared=wl.d_ff_shared, top_k=args.top_k, routing=args.routing, renorm=args.renorm,
+                         weight_format=args.weights)
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
-        layer(x, wg, w1, w2, bias=bias, ws1=ws1, ws2=ws2, stream=stream, stage_events=ev)
+        layer(x, wg, w1, w2, bias=bias, ws1=ws1, ws2=ws2, stream=stream, stage_events=ev, w1_scale=w1s,
+              w2_scale=w2s)
 
     for _ in range(args.warmup):
         step()
@@ -222,7 +233,8 @@ def main():
     comb_bytes = 2 * T * d * esz + (T * d * esz if wl.d_ff_shared else 0) + T * 12
     if variant:  # every kept pick's expert row, every x row, every y row
         comb_bytes = (kept + 2 * T) * d * esz + (T * d * esz if wl.d_ff_shared else 0)
-    ffn_launch_bytes = n_active * d * F * esz + kept * (d + F) * esz  # one GEMM launch
+    wbytes_per = (0.5 + 1.0 / 32) if mxw else esz  # bytes per weight: MXFP4 codes + E8M0 scales
+    ffn_launch_bytes = n_active * d * F * wbytes_per + kept * (d + F) * esz  # one GEMM launch
     ffn_flops = 4.0 * kept * d * F
 
     def gbs(b, t):
@@ -257,6 +269,8 @@ def main():
     achieved = gbs(ffn_launch_bytes, launch_s)
     if wl.dtype != "bf16":
         kernel = "ffn_gemm_f32"
+    elif mxw:
+        kernel = "ffn_mx_stream"
     else:
         kernel = "ffn_tile_dma" if C > 64 and d % 256 == 0 and F % 256 == 0 else "ffn_gemm_bf16"
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -267,10 +281,10 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline and not on_device:
-        cpu = cpu_baseline(inp, args.cpu_seconds, args.top_k, args.routing, args.renorm)
+        cpu = cpu_baseline(inp, args.cpu_seconds, args.top_k, args.routing, args.renorm, args.weights)
 
     backward = None
-    if not args.no_backward and not variant:  # the backward is built for top-1 routing
+    if not args.no_backward and not variant and not mxw:  # the backward: top-1 routing, native weights
         backward = measure_backward(args, wl, inp, layer.C, x, wg, w1, w2, bias, ws1, ws2, stream, on_device)
 
     line = {
@@ -280,7 +294,8 @@ def main():
         "config": {"workload": wl.name, "T": T, "d_model": d, "d_ff": F, "N": N,
                    "capacity_factor": wl.capacity_factor, "C": C, "priority": wl.priority,
                    "gate_scale": wl.gate_scale, "d_ff_shared": wl.d_ff_shared, "parallelism": "single GPU",
-                   "routing": "expert choice" if args.routing == "expert" else f"top-{max(1, args.top_k)}"},
+                   "routing": "expert choice" if args.routing == "expert" else f"top-{max(1, args.top_k)}",
+                   "expert_weights": "MXFP4 (E2M1 + E8M0 per 32)" if mxw else wl.dtype},
         "roofline": roofline, "stages": stages, "cpu_baseline": cpu, "backward": backward,
     }
     print(json.dumps(line), flush=True)
@@ -417,19 +432,28 @@ def traffic_bytes(workload):
     return sum(per) / len(per)
 
 
-def cpu_baseline(inp, seconds, top_k=1, routing="token", renorm=False):
+def cpu_baseline(inp, seconds, top_k=1, routing="token", renorm=False, weights="native"):
     """The fp64 oracle, as it stands, on the same workload (and routing): whole
     layer passes over the batch, repeated until `seconds` have elapsed (at most
     30 passes)."""
     import oracle
     from oracle import routing as orr
 
+    from oracle import mxfp4 as mx
+
     def one_pass():
-        if top_k <= 1 and routing == "token":
+        if top_k <= 1 and routing == "token" and weights == "native":
             return oracle.moe_forward_stored(inp)
         wl, dt = inp.wl, inp.wl.dtype
         x, wg = oracle.widen(inp.x, dt), oracle.widen(inp.w_gate, dt)
         w1_of, w2_of = (lambda e: oracle.widen(inp.w1[e], dt)), (lambda e: oracle.widen(inp.w2[e], dt))
+        if weights == "mxfp4":  # the oracle's own MXFP4 encoding of each expert, decoded exactly
+            w1_of = lambda e: mx.dequantize(*mx.quantize(oracle.widen(inp.w1[e:e + 1], dt)))[0]  # noqa: E731
+            w2_of = lambda e: mx.dequantize(*mx.quantize(oracle.widen(inp.w2[e:e + 1], dt)))[0]  # noqa: E731
+            if top_k <= 1 and routing == "token":
+                return oracle.moe_forward(x, wg, inp.bias, w1_of, w2_of, wl.N, wl.capacity_factor,
+                                          priority=wl.priority, gate_scale=wl.gate_scale,
+                                          residual_all=wl.residual_all)
         ws1 = oracle.widen(inp.ws1, dt) if inp.ws1 is not None else None
         ws2 = oracle.widen(inp.ws2, dt) if inp.ws2 is not None else None
         if routing == "expert":
@@ -456,7 +480,8 @@ def cpu_baseline(inp, seconds, top_k=1, routing="token", renorm=False):
     return {"value": inp.wl.T * passes / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "seconds": el, "sample": f"{passes} full fp64 layer passes over the {inp.wl.name} batch "
                                      f"(T={inp.wl.T} tokens each, "
-                                     f"{'expert choice' if routing == 'expert' else f'top-{max(1, top_k)}'})"}
+                                     f"{'expert choice' if routing == 'expert' else f'top-{max(1, top_k)}'}"
+                                     f"{', MXFP4 experts' if weights == 'mxfp4' else ''})"}
 
 
 if __name__ == "__main__":

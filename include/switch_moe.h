@@ -181,6 +181,29 @@ switch_status switch_combine(const void* expert_out, const void* x, const void* 
                              int32_t N, int32_t C, uint32_t flags, void* y, void* stream);
 
 /* ------------------------------------------------------------------------
+ * MXFP4 expert weights (the open-MoE routing comparison page: gpt-oss ships
+ * its MoE weights in MXFP4 to fit one GPU; format: OCP Microscaling v1.0).
+ * Blocks of 32 consecutive elements along the GEMM's reduction dimension share
+ * one E8M0 scale byte (2^(byte - 127)); elements are FP4 E2M1 codes, two per
+ * byte, the lower index in the low nibble.  Quantization: E = clamp(floor(
+ * log2(max |v|)) - 2, -127, 127) (-127 for an all-zero block); each v / 2^E
+ * rounds to the nearest E2M1 value (0, 0.5, 1, 1.5, 2, 3, 4, 6), ties to the
+ * even mantissa, saturating at 6; the sign bit is the sign of v.
+ * ---------------------------------------------------------------------- */
+typedef enum switch_weight_format {
+  SWITCH_WEIGHTS_NATIVE = 0, /* w1 / w2 in the layer dtype */
+  SWITCH_WEIGHTS_MXFP4 = 1   /* w1 / w2 MXFP4 codes + scales; bf16 layers with C <= 64, forward only */
+} switch_weight_format;
+
+/* Quantize w [batches, K, Ncols] (dtype) along K:
+ *   codes [batches, Ncols, K/2] (bytes), scales [batches, Ncols, K/32].
+ * K must be a multiple of 128 and at most 2^21.  For the experts: w1 with
+ * K = d_model, Ncols = d_ff; w2 with K = d_ff, Ncols = d_model.  Bit-exact and
+ * deterministic. */
+switch_status switch_quantize_mxfp4(const void* w, int32_t dtype, int64_t batches, int32_t K, int32_t Ncols,
+                                    uint8_t* codes, uint8_t* scales, void* stream);
+
+/* ------------------------------------------------------------------------
  * The whole layer: route -> capacity/slots -> dispatch -> expert FFN ->
  * (shared FFN) -> combine, enqueued on one stream.  Results equal those of
  * the per-stage entry points above, bit for bit.  With token-order priority
@@ -205,16 +228,19 @@ typedef struct switch_moe_desc {
   int32_t top_k;            /* token choice: experts per token, 0 or 1 = top-1,
                                at most 8 and at most N */
   int32_t routing;          /* switch_routing */
+  int32_t weight_format;    /* switch_weight_format of w1 / w2 */
 } switch_moe_desc;
 
 typedef struct switch_moe_inputs {
   const void* x;
   const void* w_gate;
   const float* bias; /* NULL: no router bias */
-  const void* w1;
-  const void* w2;
-  const void* ws1;   /* shared expert, only if d_ff_shared > 0 */
+  const void* w1;    /* dtype [N, d_model, d_ff]; MXFP4: codes [N, d_ff, d_model/2] */
+  const void* w2;    /* dtype [N, d_ff, d_model]; MXFP4: codes [N, d_model, d_ff/2] */
+  const void* ws1;   /* shared expert, only if d_ff_shared > 0 (always dtype) */
   const void* ws2;
+  const uint8_t* w1_scale; /* MXFP4 only: E8M0 [N, d_ff, d_model/32] */
+  const uint8_t* w2_scale; /* MXFP4 only: E8M0 [N, d_model, d_ff/32] */
 } switch_moe_inputs;
 
 typedef struct switch_moe_outputs {

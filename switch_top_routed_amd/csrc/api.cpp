@@ -310,6 +310,10 @@ switch_status validate_desc(const switch_moe_desc* d, int32_t* C) {
   if (c < 1 || c > d->T) return fail(SWITCH_E_SHAPE, "C=%d outside [1, T=%lld]", c, (long long)d->T);
   if (d->routing == SWITCH_EXPERT_CHOICE && c > kMaxExpertChoiceK)
     return fail(SWITCH_E_UNSUPPORTED, "expert choice with min(C, T) = %d beyond %d", c, kMaxExpertChoiceK);
+  if (d->weight_format != SWITCH_WEIGHTS_NATIVE && d->weight_format != SWITCH_WEIGHTS_MXFP4)
+    return fail(SWITCH_E_UNSUPPORTED, "weight_format %d is not supported", d->weight_format);
+  if (d->weight_format == SWITCH_WEIGHTS_MXFP4 && (d->dtype != SWITCH_BF16 || !mx_ffn_applies(c, d->d_model, d->d_ff)))
+    return fail(SWITCH_E_UNSUPPORTED, "MXFP4 expert weights need a bf16 layer with C <= 64 (C=%d)", c);
   if ((int64_t)d->N * c > ((int64_t)1 << 31) - 1) return fail(SWITCH_E_SHAPE, "N*C exceeds 2^31-1");
   *C = c;
   return SWITCH_OK;
@@ -462,6 +466,21 @@ switch_status switch_combine(const void* expert_out, const void* x, const void* 
   return ok();
 }
 
+switch_status switch_quantize_mxfp4(const void* w, int32_t dtype, int64_t batches, int32_t K, int32_t Ncols,
+                                    uint8_t* codes, uint8_t* scales, void* stream) {
+  TRY(check_dtype(dtype));
+  if (batches < 1 || batches > 65535) return fail(SWITCH_E_SHAPE, "batches=%lld outside [1, 65535]", (long long)batches);
+  if (K < 128 || K % 128 != 0 || K > (1 << 21)) return fail(SWITCH_E_SHAPE, "K=%d: a multiple of 128 up to 2^21", K);
+  if (Ncols < 1) return fail(SWITCH_E_SHAPE, "Ncols=%d must be >= 1", Ncols);
+  REQUIRE_PTR(w);
+  REQUIRE_PTR(codes);
+  REQUIRE_PTR(scales);
+  REQUIRE_ALIGN(codes, 16);
+  hipError_t e = launch_mx_quantize(w, dtype, batches, K, Ncols, codes, scales, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "switch_quantize_mxfp4");
+  return ok();
+}
+
 size_t switch_moe_workspace_bytes(const switch_moe_desc* desc) {
   int32_t C = 0;
   if (validate_desc(desc, &C) != SWITCH_OK) return 0;
@@ -485,6 +504,13 @@ static switch_status moe_forward(const switch_moe_desc* desc, const switch_moe_i
   REQUIRE_PTR(in->w2);
   REQUIRE_ALIGN(in->w1, 16);
   REQUIRE_ALIGN(in->w2, 16);
+  const bool mxw = d.weight_format == SWITCH_WEIGHTS_MXFP4;
+  if (mxw) {
+    REQUIRE_PTR(in->w1_scale);
+    REQUIRE_PTR(in->w2_scale);
+    REQUIRE_ALIGN(in->w1_scale, 4);
+    REQUIRE_ALIGN(in->w2_scale, 4);
+  }
   REQUIRE_PTR(out->y);
   REQUIRE_ALIGN(out->y, 16);
   REQUIRE_PTR(out->slot);
@@ -497,8 +523,8 @@ static switch_status moe_forward(const switch_moe_desc* desc, const switch_moe_i
     REQUIRE_ALIGN(in->ws2, 16);
   }
   if (sv != nullptr) {
-    if (d.top_k > 1 || d.routing != SWITCH_TOKEN_CHOICE)
-      return fail(SWITCH_E_UNSUPPORTED, "the training forward supports top-1 routing only");
+    if (d.top_k > 1 || d.routing != SWITCH_TOKEN_CHOICE || d.weight_format != SWITCH_WEIGHTS_NATIVE)
+      return fail(SWITCH_E_UNSUPPORTED, "the training forward supports top-1 routing with native weights only");
     TRY(validate_saved(d, sv));
   }
   const FwdLayout L = fwd_layout(d, C);
@@ -518,6 +544,9 @@ static switch_status moe_forward(const switch_moe_desc* desc, const switch_moe_i
   }
   if (L.ec) rex.probs_t = reinterpret_cast<float*>(w + L.off_probs_t);
   void* h_save = sv != nullptr ? sv->h : nullptr;
+  const MxWeights mxs{static_cast<const uint8_t*>(in->w1), in->w1_scale, static_cast<const uint8_t*>(in->w2),
+                      in->w2_scale};
+  const MxWeights* mxp = mxw ? &mxs : nullptr;
   void* xin = w + L.off_xin;
   void* xout = w + L.off_xout;
   auto mark = [&](int i) -> hipError_t {
@@ -542,7 +571,7 @@ static switch_status moe_forward(const switch_moe_desc* desc, const switch_moe_i
     if ((e = mark(2)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
     if ((e = mark(3)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
     e = launch_ffn(L.ffn, in->x, in->w1, in->w2, d.dtype, d.N, C, d.d_model, d.d_ff, out->kept_count, active, nact,
-                   xout, w + L.off_ffn, st, tos, d.T, h_save);
+                   xout, w + L.off_ffn, st, tos, d.T, h_save, mxp);
   } else {
     if (L.ec) {
       e = launch_ec_select(rex.probs_t, d.T, d.N, C, tos, reinterpret_cast<int32_t*>(w + L.off_pick),
@@ -563,7 +592,7 @@ static switch_status moe_forward(const switch_moe_desc* desc, const switch_moe_i
     if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/dispatch");
     if ((e = mark(3)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
     e = launch_ffn(L.ffn, xin, in->w1, in->w2, d.dtype, d.N, C, d.d_model, d.d_ff, out->kept_count, active, nact,
-                   xout, w + L.off_ffn, st, nullptr, 0, h_save);
+                   xout, w + L.off_ffn, st, nullptr, 0, h_save, mxp);
   }
   if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/expert_ffn");
   if ((e = mark(4)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
@@ -634,8 +663,8 @@ static switch_status moe_backward(const switch_moe_desc* desc, const switch_moe_
   if (saved == nullptr) return fail(SWITCH_E_NULL, "saved is NULL");
   if (grads == nullptr) return fail(SWITCH_E_NULL, "grads is NULL");
   const switch_moe_desc& d = *desc;
-  if (d.top_k > 1 || d.routing != SWITCH_TOKEN_CHOICE)
-    return fail(SWITCH_E_UNSUPPORTED, "the backward supports top-1 routing only");
+  if (d.top_k > 1 || d.routing != SWITCH_TOKEN_CHOICE || d.weight_format != SWITCH_WEIGHTS_NATIVE)
+    return fail(SWITCH_E_UNSUPPORTED, "the backward supports top-1 routing with native weights only");
   const bool gate_scale = (d.flags & SWITCH_GATE_SCALE) != 0;
   REQUIRE_PTR(in->x);
   REQUIRE_PTR(in->w_gate);

@@ -472,8 +472,11 @@ static hipError_t gemm_bf16(const FfnPlan& pl, const void* A, const void* W, voi
 
 hipError_t launch_ffn(const FfnPlan& pl, const void* xin, const void* w1, const void* w2, int dtype, int N, int C, int d,
                       int dff, const int32_t* kept_count, const int32_t* active, const int32_t* n_active, void* xout,
-                      char* ws, hipStream_t st, const int32_t* gather, int64_t a_rows, void* h_out) {
+                      char* ws, hipStream_t st, const int32_t* gather, int64_t a_rows, void* h_out,
+                      const MxWeights* mx) {
   void* h = h_out != nullptr ? h_out : static_cast<void*>(ws + pl.off_h);
+  if (mx != nullptr)  // MXFP4 weights (bf16 activations; the caller checked mx_ffn_applies)
+    return launch_ffn_mx(xin, *mx, N, C, d, dff, kept_count, active, n_active, xout, h, st, gather, a_rows);
   if (dtype == 0) {
     hipLaunchKernelGGL(ffn_gemm_f32, dim3((unsigned)C, (unsigned)N), dim3(256), 0, st, static_cast<const float*>(xin),
                        static_cast<const float*>(w1), static_cast<float*>(h), kept_count, active, n_active, N, C, d,

@@ -67,6 +67,11 @@ hipError_t launch_combine(const void* expert_out, const void* x, const void* sha
                           uint32_t flags, void* y, hipStream_t st);
 
 // ---------------- expert FFN ----------------
+// MXFP4 expert weights (codes [N][Ncols][K/2], E8M0 scales [N][Ncols][K/32] for
+// W1 (K = d, Ncols = d_ff) and W2 (K = d_ff, Ncols = d)); bf16 activations
+struct MxWeights {
+  const uint8_t *w1_codes, *w1_scales, *w2_codes, *w2_scales;
+};
 struct FfnPlan {
   int mt;    // 16-row tiles per work item (bf16 path)
   int mch;   // m-chunks per expert
@@ -82,7 +87,13 @@ FfnPlan ffn_plan(int N, int C, int d, int dff, int dtype);
 hipError_t launch_ffn(const FfnPlan& pl, const void* xin, const void* w1, const void* w2, int dtype, int N, int C, int d,
                       int dff, const int32_t* kept_count, const int32_t* active, const int32_t* n_active, void* xout,
                       char* ws, hipStream_t st, const int32_t* gather = nullptr, int64_t a_rows = 0,
-                      void* h_out = nullptr);
+                      void* h_out = nullptr, const MxWeights* mx = nullptr);
+bool mx_ffn_applies(int C, int d, int dff);
+hipError_t launch_ffn_mx(const void* xin, const MxWeights& mw, int N, int C, int d, int dff,
+                         const int32_t* kept_count, const int32_t* active, const int32_t* n_active, void* xout,
+                         void* h, hipStream_t st, const int32_t* gather, int64_t a_rows);
+hipError_t launch_mx_quantize(const void* w, int dtype, int64_t batches, int K, int Ncols, uint8_t* codes,
+                              uint8_t* scales, hipStream_t st);
 // writes {M}, {0}, {1} for the dense (shared-expert) FFN
 // LDS-tiled MFMA GEMM (direct global-to-LDS loads, transposing LDS reads) for
 // experts with more than 64 rows and the dense shared FFN

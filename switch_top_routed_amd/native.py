@@ -34,11 +34,12 @@ _i32, _i64, _u32, _f64, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, c
 class SwitchMoeDesc(ctypes.Structure):
     _fields_ = [("T", _i64), ("d_model", _i32), ("d_ff", _i32), ("N", _i32), ("C", _i32),
                 ("capacity_factor", _f64), ("dtype", _i32), ("priority", _i32), ("flags", _u32),
-                ("d_ff_shared", _i32), ("top_k", _i32), ("routing", _i32)]
+                ("d_ff_shared", _i32), ("top_k", _i32), ("routing", _i32), ("weight_format", _i32)]
 
 
 class SwitchMoeInputs(ctypes.Structure):
-    _fields_ = [("x", _vp), ("w_gate", _vp), ("bias", _vp), ("w1", _vp), ("w2", _vp), ("ws1", _vp), ("ws2", _vp)]
+    _fields_ = [("x", _vp), ("w_gate", _vp), ("bias", _vp), ("w1", _vp), ("w2", _vp), ("ws1", _vp), ("ws2", _vp),
+                ("w1_scale", _vp), ("w2_scale", _vp)]
 
 
 class SwitchMoeOutputs(ctypes.Structure):
@@ -81,6 +82,7 @@ _SIGS = {
     "switch_moe_backward_timed": (_i32, [ctypes.POINTER(SwitchMoeDesc), ctypes.POINTER(SwitchMoeInputs),
                                          ctypes.POINTER(SwitchMoeOutputs), ctypes.POINTER(SwitchMoeSaved), _vp, _vp,
                                          ctypes.POINTER(SwitchMoeGrads), _vp, _sz, _vp, ctypes.POINTER(_vp)]),
+    "switch_quantize_mxfp4": (_i32, [_vp, _i32, _i64, _i32, _i32, _vp, _vp, _vp]),
     "switch_status_str": (ctypes.c_char_p, [_i32]),
     "switch_last_error": (ctypes.c_char_p, []),
 }
@@ -299,14 +301,15 @@ class SwitchMoE:
 
     def __init__(self, T, d_model, d_ff, N, *, dtype=torch.bfloat16, capacity_factor=1.0, C=0, priority="token",
                  gate_scale=True, residual_all=False, d_ff_shared=0, device="cuda", train=False, top_k=1,
-                 routing="token", renorm=False):
+                 routing="token", renorm=False, weight_format="native"):
         """top_k > 1: top-K token choice; routing="expert": expert choice (see include/switch_moe.h).
         With top-K, out["expert_id"], out["gate"] and out["slot"] are [T, K]."""
         self.desc = SwitchMoeDesc(T=T, d_model=d_model, d_ff=d_ff, N=N, C=C, capacity_factor=capacity_factor,
                                   dtype=_DT[dtype], priority=_PRIO[priority],
                                   flags=(GATE_SCALE if gate_scale else 0) | (RESIDUAL_ALL if residual_all else 0)
                                   | (RENORM if renorm else 0),
-                                  d_ff_shared=d_ff_shared, top_k=top_k, routing=_ROUTING[routing])
+                                  d_ff_shared=d_ff_shared, top_k=top_k, routing=_ROUTING[routing],
+                                  weight_format={"native": 0, "mxfp4": 1}[weight_format])
         K = max(1, top_k)
         L = lib()
         nb = L.switch_moe_workspace_bytes(ctypes.byref(self.desc))
@@ -346,12 +349,16 @@ class SwitchMoE:
                               dws1=_empty((d_model, d_ff_shared), wdt, dev) if d_ff_shared else None,
                               dws2=_empty((d_ff_shared, d_model), wdt, dev) if d_ff_shared else None)
 
-    def __call__(self, x, w_gate, w1, w2, bias=None, ws1=None, ws2=None, stream=None, stage_events=None):
+    def __call__(self, x, w_gate, w1, w2, bias=None, ws1=None, ws2=None, stream=None, stage_events=None,
+                 w1_scale=None, w2_scale=None):
         """One layer forward.  stage_events: optional StageEvents (7 HIP events) recorded at the stage
-        boundaries (switch_moe_forward_timed)."""
+        boundaries (switch_moe_forward_timed).  MXFP4 weights: w1 / w2 are the codes and
+        w1_scale / w2_scale the E8M0 scales (switch_quantize_mxfp4)."""
         ins = SwitchMoeInputs(x.data_ptr(), w_gate.data_ptr(), None if bias is None else bias.data_ptr(),
                               w1.data_ptr(), w2.data_ptr(), None if ws1 is None else ws1.data_ptr(),
-                              None if ws2 is None else ws2.data_ptr())
+                              None if ws2 is None else ws2.data_ptr(),
+                              None if w1_scale is None else w1_scale.data_ptr(),
+                              None if w2_scale is None else w2_scale.data_ptr())
         if stage_events is None:
             _check("switch_moe_forward", lib().switch_moe_forward(ctypes.byref(self.desc), ctypes.byref(ins),
                                                                   ctypes.byref(self._outs), _p(self.ws),
@@ -408,6 +415,18 @@ class SwitchMoE:
         if bias is None:
             out["dbias"] = None
         return out
+
+
+def switch_quantize_mxfp4(w, *, stream=None):
+    """MXFP4 along K of w [B, K, Ncols] (bf16 or fp32): returns (codes [B, Ncols, K/2] uint8,
+    scales [B, Ncols, K/32] uint8)."""
+    _need(w, "w")
+    B, K, Nc = w.shape
+    codes = torch.empty((B, Nc, K // 2), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((B, Nc, K // 32), dtype=torch.uint8, device=w.device)
+    _check("switch_quantize_mxfp4", lib().switch_quantize_mxfp4(_p(w), _dtype(w), B, K, Nc, _p(codes), _p(scales),
+                                                                _stream(stream)))
+    return codes, scales
 
 
 def switch_moe_forward_train(layer: "SwitchMoE", x, w_gate, w1, w2, **kw):
