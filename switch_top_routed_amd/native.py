@@ -94,7 +94,7 @@ def header_functions():
     """Names of the functions declared in include/switch_moe.h."""
     with open(HEADER) as fh:
         text = fh.read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(switch_[a-z_]+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(switch_[a-z0-9_]+)\s*\(", text, re.M)))
 
 
 def lib():
