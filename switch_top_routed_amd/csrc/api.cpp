@@ -373,7 +373,8 @@ BwdLayout bwd_layout(const switch_moe_desc& d, int32_t C) {
   }
   if (d.d_ff_shared > 0) {
     take(L.off_dense, 3 * 4);
-    take(L.off_us, (size_t)d.T * d.d_ff_shared * 4);
+    if (!(d.dtype == SWITCH_BF16 && dense_bwd_applies(d.T, d.d_model, d.d_ff_shared)))
+      take(L.off_us, (size_t)d.T * d.d_ff_shared * 4);  // the generic path's fp32 U
     take(L.off_dzs, (size_t)d.T * d.d_ff_shared * esz);
     take(L.off_dxs, (size_t)d.T * d.d_model * 4);
   }
@@ -784,6 +785,11 @@ static switch_status moe_backward(const switch_moe_desc* desc, const switch_moe_
     float* Us = reinterpret_cast<float*>(w + L.off_us);
     void* dZs = w + L.off_dzs;
     dxs = reinterpret_cast<float*>(w + L.off_dxs);
+    if (dt == SWITCH_BF16 && dense_bwd_applies(T, dm, dfs)) {
+      BWD_TRY(launch_shared_bwd_dense(in->x, dy, in->ws1, in->ws2, saved->h_shared, dZs, dxs, grads->dws1,
+                                      grads->dws2, T, dm, dfs, st),
+              "switch_moe_backward/shared_dense");
+    } else {
     BWD_TRY(launch_dense_plan(dk, dk + 1, dk + 2, (int32_t)T, st), "switch_moe_backward/shared_plan");
     BWD_TRY(launch_gemm_generic(GemmOperand{dy, dm, 0, nullptr, nullptr, 0}, 0,
                                 GemmOperand{in->ws2, dm, 0, nullptr, nullptr, 1}, GemmOut{Us, dfs, 0}, 1, dt, 1,
@@ -803,6 +809,7 @@ static switch_status moe_backward(const switch_moe_desc* desc, const switch_moe_
                                 GemmOperand{in->ws1, dfs, 0, nullptr, nullptr, 1}, GemmOut{dxs, dm, 0}, 1, dt, 1,
                                 (int)T, dm, dfs, (int)T, nullptr, 0, st),
             "switch_moe_backward/shared_dX");
+    }
   }
   BWD_TRY(mark(4), "switch_moe_backward/event");
   // router: softmax gradient, dW_g = dlogit^T x, db, and dx

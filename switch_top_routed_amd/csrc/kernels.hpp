@@ -184,6 +184,13 @@ hipError_t launch_combine_picks(int mode, const void* expert_out, const void* x,
                                 const int32_t* pick, const float* probs_t, int N, int C, uint32_t flags,
                                 int32_t* npick, int32_t* n_dropped, void* y, hipStream_t st);
 
+// shared dense expert backward on LDS-tiled MFMA (bf16): dZs = (dY Ws2^T) *
+// [Hs > 0], dWs2 = Hs^T dY, dWs1 = x^T dZs, dXs = dZs Ws1^T (fp32)
+bool dense_bwd_applies(int64_t T, int d, int dffs);
+hipError_t launch_shared_bwd_dense(const void* x, const void* dy, const void* ws1, const void* ws2, const void* hs,
+                                   void* dzs, float* dxs, void* dws1, void* dws2, int64_t T, int d, int dffs,
+                                   hipStream_t st);
+
 inline size_t align_up(size_t v, size_t a = 256) { return (v + a - 1) / a * a; }
 
 }  // namespace swm

@@ -182,6 +182,8 @@ EDGE = [
     _custom("f32-odd", 301, 20, 36, 7, 1.3, dtype="f32", seed=5),
     _custom("residual", 512, 256, 256, 8, 0.8, seed=6, residual_all=True),
     _custom("shared", 384, 256, 512, 8, 1.0, seed=7, d_ff_shared=256),
+    _custom("shared-dense-tiles", 640, 512, 256, 8, 1.0, seed=14, d_ff_shared=768),
+    _custom("shared-generic", 300, 256, 256, 8, 1.0, seed=15, d_ff_shared=256),
     _custom("tiled-c150", 1200, 256, 512, 8, 1.0, seed=13, bias_scale=0.5),
 ]
 
