@@ -34,7 +34,8 @@ with its reason in the design notes):
 
 The backward pass of the layer lives in oracle/backward.py; the routing
 variants next to top-1 (top-K token choice, expert choice) in
-oracle/routing.py; MXFP4 expert weights in oracle/mxfp4.py.
+oracle/routing.py; MXFP4 expert weights in oracle/mxfp4.py; Expanded Drop
+(re-routing of overflow tokens at inference) in oracle/expanded.py.
 
 Parity status: every function here is pinned by the CPU tests
 (brute-force evaluation, closed forms, invariants, a hand-worked example);

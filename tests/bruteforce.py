@@ -209,3 +209,53 @@ def brute_forward_expert_choice(x, wg, bias, w1, w2, C, gate_scale=True, residua
                 row[k] += x[t][k]
         y.append(row)
     return dict(p=probs, pick=pick, y=y)
+
+
+def brute_forward_expanded(x, wg, bias, w1, w2, M, C, priority="token", gate_scale=True, residual_all=False):
+    """Expanded Drop as a sequential slot-filling simulation: per round, the
+    tokens still without a slot are visited one at a time in the priority
+    order (ascending t, or descending p at the expert they apply to, ties to the
+    lower t) and each takes the next free slot of its candidate for that round
+    if there is one.  Candidates by repeated selection of the largest remaining
+    logit."""
+    T, N, d = len(x), len(wg), len(x[0])
+    probs, chosen = [], []
+    for t in range(T):
+        l = [_dot(wg[i], x[t]) + (bias[i] if bias is not None else 0.0) for i in range(N)]
+        probs.append(_softmax_row(l))
+        c = []
+        for _ in range(M):
+            best = None
+            for i in range(N):
+                if i not in c and (best is None or l[i] > l[best]):
+                    best = i
+            c.append(best)
+        chosen.append(c)
+    fill = [0] * N
+    slot = [-1] * T
+    served = [c[0] for c in chosen]
+    gate = [probs[t][chosen[t][0]] for t in range(T)]
+    rnd = [-1] * T
+    for r in range(M):
+        waiting = [t for t in range(T) if slot[t] < 0]
+        if priority == "gate":
+            waiting.sort(key=lambda t: (-probs[t][chosen[t][r]], t))
+        for t in waiting:
+            e = chosen[t][r]
+            if fill[e] < C:
+                slot[t], served[t], gate[t], rnd[t] = fill[e], e, probs[t][e], r
+                fill[e] += 1
+    y = []
+    for t in range(T):
+        if slot[t] < 0:
+            y.append(list(x[t]))
+            continue
+        o = _expert(x[t], w1[served[t]], w2[served[t]])
+        s = gate[t] if gate_scale else 1.0
+        y.append([s * o[k] + (x[t][k] if residual_all else 0.0) for k in range(d)])
+    count = [sum(1 for t in range(T) if chosen[t][0] == i) for i in range(N)]  # first choices
+    f = [c / T for c in count]
+    P = [math.fsum(probs[t][i] for t in range(T)) / T for i in range(N)]
+    return dict(candidates=chosen, p=probs, expert_id=served, gate=gate, slot=slot, round=rnd, y=y,
+                kept_count=fill, n_dropped=T - sum(fill), routed_count=count, f=f, P=P,
+                l_aux=N * math.fsum(f[i] * P[i] for i in range(N)))
