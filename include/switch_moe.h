@@ -12,7 +12,7 @@
  *          passage, selective-precision passage.
  *   [CAP]  "MoE expert capacity factor and token dropping" (wiblog.cn):
  *          Where capacity comes from, After overflow, training-step
- *          flowchart.
+ *          flowchart, inference section (Expanded Drop).
  *
  * Conventions shared by every entry point:
  *   - Tensor pointers are DEVICE pointers; the descriptor structs and scalar
@@ -229,6 +229,9 @@ typedef struct switch_moe_desc {
                                at most 8 and at most N */
   int32_t routing;          /* switch_routing */
   int32_t weight_format;    /* switch_weight_format of w1 / w2 */
+  int32_t expand_choices;   /* Expanded Drop: 0 or 1 = off; M in [2, min(N, 8)]
+                               = re-route overflow tokens over their M
+                               highest-logit experts (top-1 token choice only) */
 } switch_moe_desc;
 
 typedef struct switch_moe_inputs {
@@ -284,6 +287,22 @@ switch_status switch_moe_forward(const switch_moe_desc* desc, const switch_moe_i
  *   argmax (top-1) statistics of the same router; kept_count[i] = min(C, T);
  *   slot[t] = the number of experts that took token t; n_dropped = the
  *   number of tokens no expert took.
+ *   Expanded Drop (desc.expand_choices = M >= 2; [CAP] inference section:
+ *   overflow tokens of full experts consider further experts of their
+ *   candidate set, so that lightly loaded experts' spare capacity is used).
+ *   Top-1 token choice with capacity C = max(1, ceil(capacity_factor * T /
+ *   N)) unless desc.C is set (C <= 8192).  A token's candidates are its M
+ *   highest logits (ties to the lower index).  Round 0 is the top-1
+ *   assignment; in round r = 1 .. M-1 every token still without a slot
+ *   applies to its candidate r, and expert i fills its C - kept_i free slots
+ *   with that round's applicants in the priority order (token order: by
+ *   token index; SWITCH_GATE_DESC: by descending p[t, i], ties to the lower
+ *   token), after the slots already taken.  Outputs: expert_id, gate and slot
+ *   name the expert holding the token, p at that expert and the slot (a
+ *   token no candidate took keeps its first choice with slot -1 and passes
+ *   through); kept_count, n_dropped as after the last round; routed_count, f,
+ *   P, l_aux are the first-choice (top-1) statistics.  SWITCH_RENORM is not
+ *   accepted.
  * The training entry points below support top-1 only (SWITCH_E_UNSUPPORTED
  * otherwise). */
 
@@ -362,7 +381,10 @@ typedef struct switch_moe_grads {
    fp32 [1], or NULL for 0.  Every gradient is overwritten (not accumulated).
    Accumulation is fp32 everywhere; bf16 gradients are rounded once, except
    that dO = s dy and dZ are rounded to bf16 as GEMM operands.  Shape rules
-   and errors are those of switch_moe_forward; deterministic. */
+   and errors are those of switch_moe_forward; deterministic.
+   switch_moe_backward_workspace_bytes returns 0 for a description that the
+   forward rejects or that training does not support (top_k > 1, expert
+   choice, Expanded Drop, MXFP4 weights). */
 size_t switch_moe_backward_workspace_bytes(const switch_moe_desc* desc);
 switch_status switch_moe_backward(const switch_moe_desc* desc, const switch_moe_inputs* in,
                                   const switch_moe_outputs* fwd, const switch_moe_saved* saved, const void* dy,

@@ -202,13 +202,14 @@ switch_status validate_combine(const void* expert_out, const void* x, const void
 struct FwdLayout {
   int32_t C;
   int K;       // token choice: experts per token
+  int M;       // Expanded Drop candidates (1: off)
   bool ec;     // expert choice
   bool fused;  // top-1 token order: slots from the router's tiles, dispatch folded into GEMM 1
   RoutePlan route;
   AssignPlan assign;
   FfnPlan ffn, sffn;
   size_t off_route, off_assign, off_rank, off_toff, off_tos, off_active, off_nact, off_xin, off_xout, off_ffn;
-  size_t off_dense, off_sffn, off_sout, off_ev, off_gv, off_slotv, off_probs_t, off_pick, bytes;
+  size_t off_dense, off_sffn, off_sout, off_ev, off_gv, off_slotv, off_probs_t, off_pick, off_list, bytes;
 };
 
 // The fused path needs token order, the token matrix addressable through
@@ -221,6 +222,7 @@ FwdLayout fwd_layout(const switch_moe_desc& d, int32_t C) {
   L.C = C;
   const size_t esz = d.dtype == SWITCH_BF16 ? 2 : 4;
   L.K = d.top_k < 1 ? 1 : d.top_k;
+  L.M = d.expand_choices < 1 ? 1 : d.expand_choices;
   L.ec = d.routing == SWITCH_EXPERT_CHOICE;
   L.route = route_plan(d.T, d.d_model, d.N, d.dtype);
   L.fused = !L.ec && L.K == 1 && d.priority == SWITCH_TOKEN_ORDER &&
@@ -252,6 +254,14 @@ FwdLayout fwd_layout(const switch_moe_desc& d, int32_t C) {
     off = align_up(off + (size_t)d.T * d.N * 4);
     L.off_pick = off;
     off = align_up(off + (size_t)d.T * d.N * 4);
+  }
+  if (L.M > 1) {  // candidate lists [M, T] and one applicant list per expert
+    L.off_ev = off;
+    off = align_up(off + (size_t)L.M * d.T * 4);
+    L.off_gv = off;
+    off = align_up(off + (size_t)L.M * d.T * 4);
+    L.off_list = off;
+    off = align_up(off + (size_t)d.N * d.T * 4);
   }
   L.off_tos = off;
   off = align_up(off + (size_t)d.N * C * 4);
@@ -301,6 +311,16 @@ switch_status validate_desc(const switch_moe_desc* d, int32_t* C) {
     return fail(SWITCH_E_UNSUPPORTED, "expert choice takes no top_k (top_k=%d)", d->top_k);
   if (K > 1 && (int64_t)K * d->T > kMaxTokens)
     return fail(SWITCH_E_SHAPE, "top_k * T = %lld exceeds 2^30", (long long)K * d->T);
+  const int M = d->expand_choices < 1 ? 1 : d->expand_choices;
+  if (M > 1) {
+    if (K != 1 || d->routing != SWITCH_TOKEN_CHOICE)
+      return fail(SWITCH_E_UNSUPPORTED, "Expanded Drop re-routes top-1 token choice only");
+    if (M > kMaxTopK || M > d->N)
+      return fail(SWITCH_E_SHAPE, "expand_choices=%d outside [2, min(N, %d)]", M, kMaxTopK);
+    if (d->flags & SWITCH_RENORM) return fail(SWITCH_E_UNSUPPORTED, "SWITCH_RENORM applies to top-K only");
+    if ((int64_t)M * d->T > kMaxTokens || (int64_t)d->N * d->T > ((int64_t)1 << 31) - 1)
+      return fail(SWITCH_E_SHAPE, "Expanded Drop lists (M T, N T) exceed their index range");
+  }
   int32_t c = d->C;
   if (c == 0) {
     c = switch_capacity(K * d->T, d->N, d->capacity_factor);  // K assignments per token
@@ -310,12 +330,22 @@ switch_status validate_desc(const switch_moe_desc* d, int32_t* C) {
   if (c < 1 || c > d->T) return fail(SWITCH_E_SHAPE, "C=%d outside [1, T=%lld]", c, (long long)d->T);
   if (d->routing == SWITCH_EXPERT_CHOICE && c > kMaxExpertChoiceK)
     return fail(SWITCH_E_UNSUPPORTED, "expert choice with min(C, T) = %d beyond %d", c, kMaxExpertChoiceK);
+  if (M > 1 && c > kMaxExpertChoiceK)
+    return fail(SWITCH_E_UNSUPPORTED, "Expanded Drop with C = %d beyond %d", c, kMaxExpertChoiceK);
   if (d->weight_format != SWITCH_WEIGHTS_NATIVE && d->weight_format != SWITCH_WEIGHTS_MXFP4)
     return fail(SWITCH_E_UNSUPPORTED, "weight_format %d is not supported", d->weight_format);
   if (d->weight_format == SWITCH_WEIGHTS_MXFP4 && (d->dtype != SWITCH_BF16 || !mx_ffn_applies(c, d->d_model, d->d_ff)))
     return fail(SWITCH_E_UNSUPPORTED, "MXFP4 expert weights need a bf16 layer with C <= 64 (C=%d)", c);
   if ((int64_t)d->N * c > ((int64_t)1 << 31) - 1) return fail(SWITCH_E_SHAPE, "N*C exceeds 2^31-1");
   *C = c;
+  return SWITCH_OK;
+}
+
+// training (the saved forward and the backward): the top-1 layer with native weights
+switch_status check_trainable(const switch_moe_desc& d) {
+  if (d.top_k > 1 || d.routing != SWITCH_TOKEN_CHOICE || d.weight_format != SWITCH_WEIGHTS_NATIVE ||
+      d.expand_choices > 1)
+    return fail(SWITCH_E_UNSUPPORTED, "training supports top-1 routing with native weights only");
   return SWITCH_OK;
 }
 
@@ -524,8 +554,7 @@ static switch_status moe_forward(const switch_moe_desc* desc, const switch_moe_i
     REQUIRE_ALIGN(in->ws2, 16);
   }
   if (sv != nullptr) {
-    if (d.top_k > 1 || d.routing != SWITCH_TOKEN_CHOICE || d.weight_format != SWITCH_WEIGHTS_NATIVE)
-      return fail(SWITCH_E_UNSUPPORTED, "the training forward supports top-1 routing with native weights only");
+    TRY(check_trainable(d));
     TRY(validate_saved(d, sv));
   }
   const FwdLayout L = fwd_layout(d, C);
@@ -539,9 +568,13 @@ static switch_status moe_forward(const switch_moe_desc* desc, const switch_moe_i
   rex.probs = sv != nullptr ? sv->probs : nullptr;
   rex.K = L.K;
   rex.renorm = (d.flags & SWITCH_RENORM) != 0;
-  if (L.K > 1) {
+  if (L.K > 1 || L.M > 1) {
     rex.ev_cm = reinterpret_cast<int32_t*>(w + L.off_ev);
     rex.gv_cm = reinterpret_cast<float*>(w + L.off_gv);
+  }
+  if (L.M > 1) {
+    rex.K = L.M;
+    rex.expand = 1;
   }
   if (L.ec) rex.probs_t = reinterpret_cast<float*>(w + L.off_probs_t);
   void* h_save = sv != nullptr ? sv->h : nullptr;
@@ -568,6 +601,9 @@ static switch_status moe_forward(const switch_moe_desc* desc, const switch_moe_i
                                   reinterpret_cast<int32_t*>(w + L.off_toff), out->routed_count, out->f, out->P,
                                   out->l_aux, out->slot, tos, out->kept_count, out->n_dropped, active, nact,
                                   w + L.off_route, st);
+    if (e == hipSuccess && L.M > 1)
+      e = launch_expand(rex.ev_cm, rex.gv_cm, d.T, d.N, C, L.M, 0, out->slot, out->expert_id, out->gate, tos,
+                        out->kept_count, active, nact, out->n_dropped, reinterpret_cast<int32_t*>(w + L.off_list), st);
     if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/assign");
     if ((e = mark(2)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
     if ((e = mark(3)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
@@ -586,6 +622,10 @@ static switch_status moe_forward(const switch_moe_desc* desc, const switch_moe_i
     } else {
       e = launch_assign(L.assign, out->expert_id, out->gate, d.T, d.N, C, d.priority, out->slot, tos,
                         out->kept_count, out->n_dropped, active, nact, w + L.off_assign, st);
+      if (e == hipSuccess && L.M > 1)
+        e = launch_expand(rex.ev_cm, rex.gv_cm, d.T, d.N, C, L.M, d.priority == SWITCH_GATE_DESC ? 1 : 0, out->slot,
+                          out->expert_id, out->gate, tos, out->kept_count, active, nact, out->n_dropped,
+                          reinterpret_cast<int32_t*>(w + L.off_list), st);
     }
     if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/assign");
     if ((e = mark(2)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
@@ -646,7 +686,7 @@ switch_status switch_moe_forward_train(const switch_moe_desc* desc, const switch
 
 size_t switch_moe_backward_workspace_bytes(const switch_moe_desc* desc) {
   int32_t C = 0;
-  if (validate_desc(desc, &C) != SWITCH_OK) return 0;
+  if (validate_desc(desc, &C) != SWITCH_OK || check_trainable(*desc) != SWITCH_OK) return 0;
   return bwd_layout(*desc, C).bytes;
 }
 
@@ -664,8 +704,7 @@ static switch_status moe_backward(const switch_moe_desc* desc, const switch_moe_
   if (saved == nullptr) return fail(SWITCH_E_NULL, "saved is NULL");
   if (grads == nullptr) return fail(SWITCH_E_NULL, "grads is NULL");
   const switch_moe_desc& d = *desc;
-  if (d.top_k > 1 || d.routing != SWITCH_TOKEN_CHOICE || d.weight_format != SWITCH_WEIGHTS_NATIVE)
-    return fail(SWITCH_E_UNSUPPORTED, "the backward supports top-1 routing with native weights only");
+  TRY(check_trainable(d));
   const bool gate_scale = (d.flags & SWITCH_GATE_SCALE) != 0;
   REQUIRE_PTR(in->x);
   REQUIRE_PTR(in->w_gate);

@@ -1,0 +1,232 @@
+// Expanded Drop: capacity-aware re-routing of overflow tokens at inference
+// ("MoE expert capacity factor and token dropping" page, inference section:
+// tokens dropped by a full expert consider further experts of their candidate
+// set, so that the spare capacity of lightly loaded experts is used).
+//
+// Round 0 is the top-1 capacity assignment.  In round r every token still
+// without a slot applies to its candidate r (the router's r-th highest logit),
+// and each expert fills its free slots with that round's applicants in the
+// layer's priority order, after the slots already taken.  One launch per round:
+//   expand_round    - one workgroup (1024 threads) per expert: the applicants
+//                     in ascending token order (ballots per wave, one LDS scan
+//                     per 16K tokens) into a list of their own, then the
+//                     first min(applicants, free) by priority: token order takes
+//                     the head of the list; gate order finds the threshold key
+//                     with a 4-pass 8-bit radix select on the fp32 bit patterns
+//                     of p (ties go to the lower token, which is list order),
+//                     gathers the taken tokens by an ordered scan and ranks
+//                     them by counting.  Integer LDS atomics only count.
+//   expand_finalize - the active list, n_active and n_dropped from the final
+//                     kept counts.
+// Only workgroup i writes expert i's slots, kept count and the rows of its
+// applicants (an applicant's candidate r is one expert), so one round's
+// workgroups never touch the same data.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace swm {
+
+namespace {
+constexpr int kXdThreads = 1024;
+constexpr int kXdWaves = kXdThreads / 64;
+constexpr int kXdSub = 16;  // 1024-token chunks per list-building step
+}  // namespace
+
+// ev, gv: candidate r of every token and p there (rows r*T of the router's
+// choice-major candidate lists).  list: this expert's scratch row [T].
+__global__ __launch_bounds__(kXdThreads) void expand_round(const int32_t* __restrict__ ev,
+                                                           const float* __restrict__ gv, int64_t T, int C,
+                                                           int gate_order, int32_t* __restrict__ slot,
+                                                           int32_t* __restrict__ expert_id, float* __restrict__ gate,
+                                                           int32_t* __restrict__ tos,
+                                                           int32_t* __restrict__ kept_count,
+                                                           int32_t* __restrict__ list_all) {
+  extern __shared__ uint32_t xd_lds[];  // sel_key[free], sel_tok[free]
+  __shared__ int woff[kXdSub * kXdWaves];
+  __shared__ int hist[256];
+  __shared__ int wsum[16];
+  __shared__ int s_total;
+  __shared__ uint32_t s_prefix, s_mask;
+  __shared__ int s_need, s_base, s_eqbase;
+  const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int kept0 = kept_count[e];
+  const int room = C - kept0;
+  if (room <= 0) return;  // uniform over the workgroup
+  int32_t* list = list_all + (int64_t)e * T;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+  // ---- applicants of this round, ascending token order ----
+  int n_app = 0;
+  for (int64_t c0 = 0; c0 < T; c0 += (int64_t)kXdSub * kXdThreads) {
+    bool f[kXdSub];
+    uint64_t m[kXdSub];
+#pragma unroll
+    for (int j = 0; j < kXdSub; ++j) {
+      const int64_t t = c0 + (int64_t)j * kXdThreads + tid;
+      f[j] = t < T && ev[t] == e;
+    }
+#pragma unroll
+    for (int j = 0; j < kXdSub; ++j) {
+      const int64_t t = c0 + (int64_t)j * kXdThreads + tid;
+      f[j] = f[j] && slot[t] < 0;
+      m[j] = __ballot(f[j]);
+      if (lane == 0) woff[j * kXdWaves + w] = __popcll(m[j]);
+    }
+    __syncthreads();
+    if (w == 0) {  // exclusive scan of the 256 counts, chunk-major then wave
+      int v[4], s = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[q] = woff[lane * 4 + q];
+        s += v[q];
+      }
+      int incl = s;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += u;
+      }
+      int run = incl - s;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        woff[lane * 4 + q] = run;
+        run += v[q];
+      }
+      if (lane == 63) s_total = incl;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kXdSub; ++j) {
+      if (f[j]) {
+        const int64_t t = c0 + (int64_t)j * kXdThreads + tid;
+        list[n_app + woff[j * kXdWaves + w] + __popcll(m[j] & below)] = (int32_t)t;
+      }
+    }
+    n_app += s_total;
+    __syncthreads();  // woff and s_total are rewritten by the next step
+  }
+  const int take = n_app < room ? n_app : room;
+  if (take == 0) return;
+  __threadfence_block();  // the list is read back by other threads of this workgroup
+  __syncthreads();
+
+  // ---- the threshold: keys > thr are taken, and the first eq_take keys == thr ----
+  // token order: every key is 0, so the head of the list is taken
+  uint32_t thr = 0u;
+  int eq_take = take;
+  if (gate_order && take < n_app) {
+    if (tid == 0) {
+      s_prefix = 0u;
+      s_mask = 0u;
+      s_need = take;
+    }
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      for (int b = tid; b < 256; b += kXdThreads) hist[b] = 0;
+      __syncthreads();
+      const uint32_t prefix = s_prefix, mask = s_mask;
+      for (int a = tid; a < n_app; a += kXdThreads) {
+        const uint32_t v = __float_as_uint(gv[list[a]]);
+        if ((v & mask) == prefix) atomicAdd(&hist[(v >> shift) & 255], 1);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        int need = s_need, b = 255;
+        for (; b > 0; --b) {
+          if (hist[b] >= need) break;
+          need -= hist[b];
+        }
+        s_need = need;
+        s_prefix = prefix | ((uint32_t)b << shift);
+        s_mask = mask | (255u << shift);
+      }
+      __syncthreads();
+    }
+    thr = s_prefix;
+    eq_take = s_need;
+  }
+
+  // ---- ordered gather of the taken applicants ----
+  uint32_t* sel_key = xd_lds;
+  int* sel_tok = reinterpret_cast<int*>(xd_lds + room);
+  if (tid == 0) {
+    s_base = 0;
+    s_eqbase = 0;
+  }
+  __syncthreads();
+  for (int a0 = 0; a0 < n_app; a0 += kXdThreads) {
+    const int a = a0 + tid;
+    const int t = a < n_app ? list[a] : 0;
+    const uint32_t v = (a < n_app && gate_order) ? __float_as_uint(gv[t]) : 0u;
+    const int is_eq = (a < n_app && v == thr) ? 1 : 0;
+    int tot_eq;
+    const int eq_rank = s_eqbase + block_exclusive_scan(is_eq, wsum, &tot_eq);
+    const int tk = (a < n_app && (v > thr || (is_eq && eq_rank < eq_take))) ? 1 : 0;
+    int tot;
+    const int pos = s_base + block_exclusive_scan(tk, wsum, &tot);
+    if (tk) {
+      sel_key[pos] = v;
+      sel_tok[pos] = t;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      s_base += tot;
+      s_eqbase += tot_eq;
+    }
+    __syncthreads();
+  }
+
+  // ---- slots: rank by (key descending, token ascending); the gather kept token order ----
+  for (int a = tid; a < take; a += kXdThreads) {
+    const uint32_t ka = sel_key[a];
+    const int ta = sel_tok[a];
+    int r = a;
+    if (gate_order) {
+      r = 0;
+      for (int b = 0; b < take; ++b) {
+        const uint32_t kb = sel_key[b];
+        r += (kb > ka || (kb == ka && sel_tok[b] < ta)) ? 1 : 0;
+      }
+    }
+    const int s = kept0 + r;
+    slot[ta] = s;
+    tos[(int64_t)e * C + s] = ta;
+    expert_id[ta] = e;
+    gate[ta] = gv[ta];
+  }
+  if (tid == 0) kept_count[e] = kept0 + take;
+}
+
+__global__ __launch_bounds__(1024) void expand_finalize(const int32_t* __restrict__ kept_count, int N, int64_t T,
+                                                        int32_t* __restrict__ active, int32_t* __restrict__ n_active,
+                                                        int32_t* __restrict__ n_dropped) {
+  __shared__ int wsum[16];
+  const int n = threadIdx.x;
+  const int kept = n < N ? kept_count[n] : 0;
+  int tot_active, tot_kept;
+  const int pos = block_exclusive_scan(kept > 0 ? 1 : 0, wsum, &tot_active);
+  block_exclusive_scan(kept, wsum, &tot_kept);
+  if (n < N && kept > 0) active[pos] = n;
+  if (n == 0) {
+    n_active[0] = tot_active;
+    n_dropped[0] = (int32_t)(T - tot_kept);
+  }
+}
+
+// ----------------------------------------------------------------------------
+size_t expand_lds_bytes(int C) { return (size_t)C * 8; }
+
+hipError_t launch_expand(const int32_t* ev_cm, const float* gv_cm, int64_t T, int N, int C, int M, int gate_order,
+                         int32_t* slot, int32_t* expert_id, float* gate, int32_t* tos, int32_t* kept_count,
+                         int32_t* active, int32_t* n_active, int32_t* n_dropped, int32_t* list, hipStream_t st) {
+  for (int r = 1; r < M; ++r) {
+    hipLaunchKernelGGL(expand_round, dim3((unsigned)N), dim3(kXdThreads), expand_lds_bytes(C), st, ev_cm + r * T,
+                       gv_cm + r * T, T, C, gate_order, slot, expert_id, gate, tos, kept_count, list);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(expand_finalize, dim3(1), dim3(1024), 0, st, kept_count, N, T, active, n_active, n_dropped);
+  return hipGetLastError();
+}
+
+}  // namespace swm

@@ -36,6 +36,7 @@ struct RouteExtra {
   int renorm = 0;
   int32_t* ev_cm = nullptr;
   float* gv_cm = nullptr;
+  int expand = 0;  // K choices are Expanded Drop candidates: stats, expert_id and gate stay top-1
 };
 hipError_t launch_route(const RoutePlan& pl, const void* x, const void* wg, const float* bias, int64_t T, int d, int N,
                         int dtype, int32_t* expert_id, float* gate, int32_t* routed_count, float* f, float* P,
@@ -183,6 +184,14 @@ hipError_t launch_combine_picks(int mode, const void* expert_out, const void* x,
                                 int64_t T, int d, int K, const int32_t* eid, const int32_t* slot, const float* gate,
                                 const int32_t* pick, const float* probs_t, int N, int C, uint32_t flags,
                                 int32_t* npick, int32_t* n_dropped, void* y, hipStream_t st);
+
+// Expanded Drop: rounds 1 .. M-1 over the candidates ev_cm / gv_cm [M, T]
+// after the top-1 assignment (slot, token_of_slot, kept_count in place;
+// expert_id / gate rewritten for re-routed tokens), then active, n_active and
+// n_dropped.  list: workspace [N, T] int32.  C <= kMaxExpertChoiceK.
+hipError_t launch_expand(const int32_t* ev_cm, const float* gv_cm, int64_t T, int N, int C, int M, int gate_order,
+                         int32_t* slot, int32_t* expert_id, float* gate, int32_t* tos, int32_t* kept_count,
+                         int32_t* active, int32_t* n_active, int32_t* n_dropped, int32_t* list, hipStream_t st);
 
 // shared dense expert backward on LDS-tiled MFMA (bf16): dZs = (dY Ws2^T) *
 // [Hs > 0], dWs2 = Hs^T dY, dWs1 = x^T dZs, dXs = dZs Ws1^T (fp32)

@@ -87,7 +87,7 @@ __device__ void route_epilogue(float* lg, int ldl, int rows, int64_t t0, int64_t
       if (ex.probs != nullptr && n < N) ex.probs[t * N + n] = v[j] * inv;
       if (ex.probs_t != nullptr && n < N) ex.probs_t[(int64_t)n * T + t] = v[j] * inv;
     }
-    if (ex.K <= 1) {
+    if (ex.K <= 1 || ex.expand) {
       if (lane == 0) {
         expert_id[t] = bi;
         gate[t] = inv;
@@ -97,9 +97,12 @@ __device__ void route_epilogue(float* lg, int ldl, int rows, int64_t t0, int64_t
           ex.gv_cm[t] = inv;
         }
       }
-    } else {
+    }
+    if (ex.K > 1) {
       // top-K: choice r is the largest logit not chosen yet (ties to the lower
-      // index); its gate is p at that expert
+      // index); its gate is p at that expert.  With ex.expand the further
+      // choices are only candidates: they are neither counted nor written to
+      // expert_id / gate
       int ek[kMaxTopK];
       float gk[kMaxTopK];
       ek[0] = bi;
@@ -125,13 +128,20 @@ __device__ void route_epilogue(float* lg, int ldl, int rows, int64_t t0, int64_t
         for (int j = 0; j < J; ++j)
           if (lane + 64 * j == bx) mine = v[j] * inv;
         const float pr = __shfl(mine, bx & 63, 64);
+        if (!ex.expand) {
 #pragma unroll
-        for (int j = 0; j < J; ++j) cn[j] += (lane + 64 * j == bx) ? 1 : 0;
+          for (int j = 0; j < J; ++j) cn[j] += (lane + 64 * j == bx) ? 1 : 0;
+        }
         ek[r] = bx;
         gk[r] = pr;
         gsum += pr;
       }
-      if (lane == 0) {
+      if (lane == 0 && ex.expand) {
+        for (int r = 1; r < ex.K; ++r) {
+          ex.ev_cm[(int64_t)r * T + t] = ek[r];
+          ex.gv_cm[(int64_t)r * T + t] = gk[r];
+        }
+      } else if (lane == 0) {
         const float rn = ex.renorm ? 1.0f / gsum : 1.0f;
         for (int r = 0; r < ex.K; ++r) {
           const float g = ex.renorm ? gk[r] * rn : gk[r];
@@ -635,7 +645,7 @@ hipError_t launch_route(const RoutePlan& pl, const void* x, const void* wg, cons
   if (local_rank != nullptr) return hipSuccess;  // the statistics come from launch_route_assign_token
   const int NP = (N + 63) / 64 * 64;
   hipLaunchKernelGGL(route_finalize, dim3(1), dim3(1024), 0, st, part_p, part_cnt, pl.nblk, T, N, NP, routed_count, f,
-                     P, l_aux, ex.K < 1 ? 1 : ex.K);
+                     P, l_aux, (ex.K < 1 || ex.expand) ? 1 : ex.K);
   return hipGetLastError();
 }
 

@@ -34,7 +34,8 @@ _i32, _i64, _u32, _f64, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, c
 class SwitchMoeDesc(ctypes.Structure):
     _fields_ = [("T", _i64), ("d_model", _i32), ("d_ff", _i32), ("N", _i32), ("C", _i32),
                 ("capacity_factor", _f64), ("dtype", _i32), ("priority", _i32), ("flags", _u32),
-                ("d_ff_shared", _i32), ("top_k", _i32), ("routing", _i32), ("weight_format", _i32)]
+                ("d_ff_shared", _i32), ("top_k", _i32), ("routing", _i32), ("weight_format", _i32),
+                ("expand_choices", _i32)]
 
 
 class SwitchMoeInputs(ctypes.Structure):
@@ -301,15 +302,17 @@ class SwitchMoE:
 
     def __init__(self, T, d_model, d_ff, N, *, dtype=torch.bfloat16, capacity_factor=1.0, C=0, priority="token",
                  gate_scale=True, residual_all=False, d_ff_shared=0, device="cuda", train=False, top_k=1,
-                 routing="token", renorm=False, weight_format="native"):
-        """top_k > 1: top-K token choice; routing="expert": expert choice (see include/switch_moe.h).
+                 routing="token", renorm=False, weight_format="native", expand=1):
+        """top_k > 1: top-K token choice; routing="expert": expert choice; expand = M >= 2: Expanded
+        Drop over each token's M highest-logit experts (see include/switch_moe.h).
         With top-K, out["expert_id"], out["gate"] and out["slot"] are [T, K]."""
         self.desc = SwitchMoeDesc(T=T, d_model=d_model, d_ff=d_ff, N=N, C=C, capacity_factor=capacity_factor,
                                   dtype=_DT[dtype], priority=_PRIO[priority],
                                   flags=(GATE_SCALE if gate_scale else 0) | (RESIDUAL_ALL if residual_all else 0)
                                   | (RENORM if renorm else 0),
                                   d_ff_shared=d_ff_shared, top_k=top_k, routing=_ROUTING[routing],
-                                  weight_format={"native": 0, "mxfp4": 1}[weight_format])
+                                  weight_format={"native": 0, "mxfp4": 1}[weight_format],
+                                  expand_choices=expand)
         K = max(1, top_k)
         L = lib()
         nb = L.switch_moe_workspace_bytes(ctypes.byref(self.desc))

@@ -102,3 +102,31 @@ def expert_choice_bad_rows(C, gap=GATE_GAP):
             rows.update(ts[1:][close].tolist())
         return np.array(sorted(rows), dtype=np.int64)
     return bad
+
+
+def expanded_bad_rows(M, C, gate_order, gap=GATE_GAP):
+    """Expanded Drop: the top-(M+1) logit margins decide every candidate list
+    (topk_margin_bad_rows(M)); with gate order also the first-choice gate gaps of
+    the top-1 layer (gate_gap_bad_rows(C)) and, for every expert i and round r >= 1,
+    a relative `gap` between all gates p[t, i] of the tokens whose candidate r is i
+    (the round's applicants are a subset of them)."""
+    from oracle import expanded as ox
+    margin = topk_margin_bad_rows(M)
+    top1 = gate_gap_bad_rows(C, gap) if gate_order else None
+
+    def bad(inp):
+        rows = set(margin(inp).tolist())
+        if not gate_order:
+            return np.array(sorted(rows), dtype=np.int64)
+        rows.update(top1(inp).tolist())
+        l, p, _, _ = stored_router(inp)
+        cand = ox.candidates(l, M)
+        for r in range(1, M):
+            for i in np.unique(cand[:, r]):
+                ts = np.nonzero(cand[:, r] == i)[0]
+                ts = ts[np.lexsort((ts, -p[ts, i]))]
+                pp = p[ts, i]
+                close = (pp[:-1] - pp[1:]) < gap * pp[:-1]
+                rows.update(ts[1:][close].tolist())
+        return np.array(sorted(rows), dtype=np.int64)
+    return bad

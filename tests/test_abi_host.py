@@ -178,3 +178,30 @@ def test_train_forward_and_backward_validation(L):
     d.flags = 16
     assert bwd(*args()) == E_UNSUP
     assert L.switch_moe_backward_workspace_bytes(ctypes.byref(d)) == 0
+
+
+def test_expanded_drop_validation(L):
+    """Expanded Drop: top-1 token choice only, M in [2, min(N, 8)], no RENORM, C <= 8192, inference only."""
+    def ws(**kw):
+        base = dict(T=1024, d_model=128, d_ff=128, N=8, C=0, capacity_factor=1.0, dtype=1, priority=0, flags=1,
+                    d_ff_shared=0, expand_choices=2)
+        base.update(kw)
+        return L.switch_moe_workspace_bytes(ctypes.byref(native.SwitchMoeDesc(**base)))
+    assert ws() > ws(expand_choices=0) == ws(expand_choices=1) > 0
+    assert ws(expand_choices=8) > ws(expand_choices=2)
+    assert ws(priority=1, expand_choices=4) > 0
+    assert ws(expand_choices=9) == 0 and b"expand_choices" in L.switch_last_error()
+    assert ws(N=4, expand_choices=5) == 0
+    assert ws(top_k=2) == 0 and b"top-1" in L.switch_last_error()
+    assert ws(routing=1) == 0
+    assert ws(flags=1 | 4) == 0 and b"RENORM" in L.switch_last_error()
+    assert ws(T=20000, N=2, C=9000) == 0 and b"Expanded Drop" in L.switch_last_error()
+    assert ws(T=20000, N=2, C=8192) > 0
+    d = native.SwitchMoeDesc(T=64, d_model=128, d_ff=128, N=8, C=0, capacity_factor=1.0, dtype=1, priority=0,
+                             flags=1, d_ff_shared=0, expand_choices=2)
+    ins = native.SwitchMoeInputs(1 << 20, 1 << 20, None, 1 << 20, 1 << 20, None, None)
+    outs = native.SwitchMoeOutputs(*([1 << 20] * 10))
+    sv = native.SwitchMoeSaved(1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, None)
+    assert L.switch_moe_forward_train(ctypes.byref(d), ctypes.byref(ins), ctypes.byref(outs), ctypes.byref(sv),
+                                      FAKE, 1 << 30, None) == E_UNSUP
+    assert L.switch_moe_backward_workspace_bytes(ctypes.byref(d)) == 0
