@@ -95,6 +95,8 @@ def parse():
     ap.add_argument("--top-k", type=int, default=1, help="token choice with K experts per token")
     ap.add_argument("--routing", choices=("token", "expert"), default="token", help="token choice or expert choice")
     ap.add_argument("--renorm", action="store_true", help="top-K: divide each token's gates by their sum")
+    ap.add_argument("--expand", type=int, default=1, metavar="M",
+                    help="Expanded Drop: re-route overflow tokens over their M highest-logit experts (M >= 2)")
     ap.add_argument("--weights", choices=("native", "mxfp4"), default="native",
                     help="expert weights in the layer dtype, or MXFP4 (quantized on the device before timing)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -180,6 +182,9 @@ def main():
     if variant:
         over["top_k"] = args.top_k
         over["routing"] = args.routing
+    xd = args.expand > 1
+    if xd:
+        over["expand"] = args.expand
     mxw = args.weights == "mxfp4"
     w1s = w2s = None
     if mxw:
@@ -190,7 +195,7 @@ def main():
     layer = sw.SwitchMoE(wl.T, wl.d_model, wl.d_ff, wl.N, dtype=dt, capacity_factor=wl.capacity_factor,
                          priority=wl.priority, gate_scale=wl.gate_scale, residual_all=wl.residual_all,
                          d_ff_shared=wl.d_ff_shared, top_k=args.top_k, routing=args.routing, renorm=args.renorm,
-                         weight_format=args.weights)
+                         weight_format=args.weights, expand=args.expand)
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -281,10 +286,11 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline and not on_device:
-        cpu = cpu_baseline(inp, args.cpu_seconds, args.top_k, args.routing, args.renorm, args.weights)
+        cpu = cpu_baseline(inp, args.cpu_seconds, args.top_k, args.routing, args.renorm, args.weights,
+                           args.expand)
 
     backward = None
-    if not args.no_backward and not variant and not mxw:  # the backward: top-1 routing, native weights
+    if not args.no_backward and not variant and not mxw and not xd:  # the backward: top-1, native weights
         backward = measure_backward(args, wl, inp, layer.C, x, wg, w1, w2, bias, ws1, ws2, stream, on_device)
 
     line = {
@@ -294,7 +300,9 @@ def main():
         "config": {"workload": wl.name, "T": T, "d_model": d, "d_ff": F, "N": N,
                    "capacity_factor": wl.capacity_factor, "C": C, "priority": wl.priority,
                    "gate_scale": wl.gate_scale, "d_ff_shared": wl.d_ff_shared, "parallelism": "single GPU",
-                   "routing": "expert choice" if args.routing == "expert" else f"top-{max(1, args.top_k)}",
+                   "routing": ("expert choice" if args.routing == "expert" else
+                               f"top-1 + Expanded Drop over {args.expand} candidates" if xd else
+                               f"top-{max(1, args.top_k)}"),
                    "expert_weights": "MXFP4 (E2M1 + E8M0 per 32)" if mxw else wl.dtype},
         "roofline": roofline, "stages": stages, "cpu_baseline": cpu, "backward": backward,
     }
@@ -432,17 +440,17 @@ def traffic_bytes(workload):
     return sum(per) / len(per)
 
 
-def cpu_baseline(inp, seconds, top_k=1, routing="token", renorm=False, weights="native"):
+def cpu_baseline(inp, seconds, top_k=1, routing="token", renorm=False, weights="native", expand=1):
     """The fp64 oracle, as it stands, on the same workload (and routing): whole
     layer passes over the batch, repeated until `seconds` have elapsed (at most
     30 passes)."""
     import oracle
+    from oracle import expanded as ox
+    from oracle import mxfp4 as mx
     from oracle import routing as orr
 
-    from oracle import mxfp4 as mx
-
     def one_pass():
-        if top_k <= 1 and routing == "token" and weights == "native":
+        if top_k <= 1 and routing == "token" and weights == "native" and expand <= 1:
             return oracle.moe_forward_stored(inp)
         wl, dt = inp.wl, inp.wl.dtype
         x, wg = oracle.widen(inp.x, dt), oracle.widen(inp.w_gate, dt)
@@ -450,12 +458,16 @@ def cpu_baseline(inp, seconds, top_k=1, routing="token", renorm=False, weights="
         if weights == "mxfp4":  # the oracle's own MXFP4 encoding of each expert, decoded exactly
             w1_of = lambda e: mx.dequantize(*mx.quantize(oracle.widen(inp.w1[e:e + 1], dt)))[0]  # noqa: E731
             w2_of = lambda e: mx.dequantize(*mx.quantize(oracle.widen(inp.w2[e:e + 1], dt)))[0]  # noqa: E731
-            if top_k <= 1 and routing == "token":
+            if top_k <= 1 and routing == "token" and expand <= 1:
                 return oracle.moe_forward(x, wg, inp.bias, w1_of, w2_of, wl.N, wl.capacity_factor,
                                           priority=wl.priority, gate_scale=wl.gate_scale,
                                           residual_all=wl.residual_all)
         ws1 = oracle.widen(inp.ws1, dt) if inp.ws1 is not None else None
         ws2 = oracle.widen(inp.ws2, dt) if inp.ws2 is not None else None
+        if expand > 1:
+            return ox.moe_forward_expanded(x, wg, inp.bias, w1_of, w2_of, wl.N, M=expand,
+                                           capacity_factor=wl.capacity_factor, priority=wl.priority,
+                                           gate_scale=wl.gate_scale, residual_all=wl.residual_all, ws1=ws1, ws2=ws2)
         if routing == "expert":
             return orr.moe_forward_expert_choice(x, wg, inp.bias, w1_of, w2_of, wl.N, wl.capacity_factor,
                                                  gate_scale=wl.gate_scale, residual_all=wl.residual_all,
@@ -481,6 +493,7 @@ def cpu_baseline(inp, seconds, top_k=1, routing="token", renorm=False, weights="
             "seconds": el, "sample": f"{passes} full fp64 layer passes over the {inp.wl.name} batch "
                                      f"(T={inp.wl.T} tokens each, "
                                      f"{'expert choice' if routing == 'expert' else f'top-{max(1, top_k)}'}"
+                                     f"{f', Expanded Drop over {expand} candidates' if expand > 1 else ''}"
                                      f"{', MXFP4 experts' if weights == 'mxfp4' else ''})"}
 
 

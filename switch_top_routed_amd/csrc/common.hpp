@@ -56,6 +56,58 @@ __device__ __forceinline__ void wave_argmax(float& v, int& idx) {
   }
 }
 
+// hist[digit] += 1 for every active lane (digit < 256); the lanes of a wave
+// with the same digit are counted together, one LDS atomic per distinct digit
+// and wave.  Every lane of the wave must call it.
+__device__ __forceinline__ void hist_add_wave(int* hist, uint32_t digit, bool active) {
+  const int lane = threadIdx.x & 63;
+  uint64_t same = __ballot(active);
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const bool bit = (digit >> b) & 1u;
+    const uint64_t m = __ballot(active && bit);
+    same &= bit ? m : ~m;
+  }
+  if (active && __ffsll((unsigned long long)same) - 1 == lane) atomicAdd(&hist[digit], __popcll(same));
+}
+
+// One step of a descending radix select over a 256-bin histogram in LDS, run
+// by all 64 lanes of one wave: the bin that holds the need-th largest key
+// (1-based, counting from bin 255 down) and need minus the keys in the bins
+// above it.  Bin 0 takes whatever remains.  The result is the same on every
+// lane.
+__device__ __forceinline__ void radix_pick_desc(const int* hist, int need, int* bin, int* rem) {
+  const int lane = threadIdx.x & 63;
+  int h[4], s = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {  // lane l holds bins 255 - 4l .. 252 - 4l
+    h[q] = hist[255 - 4 * lane - q];
+    s += h[q];
+  }
+  int incl = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += u;
+  }
+  int run = incl - s, b = 0, r = 0;
+  bool found = false;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int bq = 255 - 4 * lane - q;
+    if (!found && (bq == 0 || run + h[q] >= need)) {
+      b = bq;
+      r = need - run;
+      found = true;
+    }
+    if (!found) run += h[q];
+  }
+  const uint64_t ok = __ballot(incl >= need);
+  const int L = ok ? __ffsll((unsigned long long)ok) - 1 : 63;
+  *bin = __shfl(b, L, kWave);
+  *rem = __shfl(r, L, kWave);
+}
+
 // Exclusive prefix sum over a block of up to 1024 threads (blockDim.x multiple
 // of 64).  `wsum` is LDS scratch of >= 16 ints.  Returns the exclusive prefix;
 // *total receives the block total.

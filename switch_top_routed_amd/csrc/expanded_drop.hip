@@ -7,15 +7,17 @@
 // without a slot applies to its candidate r (the router's r-th highest logit),
 // and each expert fills its free slots with that round's applicants in the
 // layer's priority order, after the slots already taken.  One launch per round:
-//   expand_round    - one workgroup (1024 threads) per expert: the applicants
-//                     in ascending token order (ballots per wave, one LDS scan
-//                     per 16K tokens) into a list of their own, then the
-//                     first min(applicants, free) by priority: token order takes
-//                     the head of the list; gate order finds the threshold key
-//                     with a 4-pass 8-bit radix select on the fp32 bit patterns
-//                     of p (ties go to the lower token, which is list order),
-//                     gathers the taken tokens by an ordered scan and ranks
-//                     them by counting.  Integer LDS atomics only count.
+//   expand_round    - one workgroup (1024 threads) per expert finds its
+//                     applicants in ascending token order (ballots per wave,
+//                     one LDS scan per 16K tokens).  Token order: the first
+//                     `free` of them take the slots in that same pass.  Gate
+//                     order: the applicants (their keys and tokens in LDS up to
+//                     4096 of them, else a list in the workspace) go through a
+//                     4-pass 8-bit radix select of the threshold key on the fp32
+//                     bit patterns of p (ties go to the lower token, which is
+//                     list order; histogram atomics aggregated per wave and
+//                     digit), an ordered gather of the taken ones and ranks by
+//                     counting.  Integer LDS atomics only count.
 //   expand_finalize - the active list, n_active and n_dropped from the final
 //                     kept counts.
 // Only workgroup i writes expert i's slots, kept count and the rows of its
@@ -29,11 +31,13 @@ namespace swm {
 namespace {
 constexpr int kXdThreads = 1024;
 constexpr int kXdWaves = kXdThreads / 64;
-constexpr int kXdSub = 16;  // 1024-token chunks per list-building step
+constexpr int kXdSub = 16;     // 1024-token chunks per list-building step
+constexpr int kXdCache = 4096;  // gate order: applicants whose key and token stay in LDS
 }  // namespace
 
 // ev, gv: candidate r of every token and p there (rows r*T of the router's
-// choice-major candidate lists).  list: this expert's scratch row [T].
+// choice-major candidate lists).  list: this expert's scratch row [T] (gate
+// order only).
 __global__ __launch_bounds__(kXdThreads) void expand_round(const int32_t* __restrict__ ev,
                                                            const float* __restrict__ gv, int64_t T, int C,
                                                            int gate_order, int32_t* __restrict__ slot,
@@ -41,7 +45,8 @@ __global__ __launch_bounds__(kXdThreads) void expand_round(const int32_t* __rest
                                                            int32_t* __restrict__ tos,
                                                            int32_t* __restrict__ kept_count,
                                                            int32_t* __restrict__ list_all) {
-  extern __shared__ uint32_t xd_lds[];  // sel_key[free], sel_tok[free]
+  // gate order: akey[kXdCache], atok[kXdCache], then sel_key[room], sel_tok[room]
+  extern __shared__ uint32_t xd_lds[];
   __shared__ int woff[kXdSub * kXdWaves];
   __shared__ int hist[256];
   __shared__ int wsum[16];
@@ -53,9 +58,12 @@ __global__ __launch_bounds__(kXdThreads) void expand_round(const int32_t* __rest
   const int room = C - kept0;
   if (room <= 0) return;  // uniform over the workgroup
   int32_t* list = list_all + (int64_t)e * T;
+  uint32_t* akey = xd_lds;
+  int* atok = reinterpret_cast<int*>(xd_lds + kXdCache);
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
-  // ---- applicants of this round, ascending token order ----
+  // ---- applicants of this round in ascending token order; with token order
+  // the first `room` of them take the free slots right here ----
   int n_app = 0;
   for (int64_t c0 = 0; c0 < T; c0 += (int64_t)kXdSub * kXdThreads) {
     bool f[kXdSub];
@@ -99,22 +107,43 @@ __global__ __launch_bounds__(kXdThreads) void expand_round(const int32_t* __rest
     for (int j = 0; j < kXdSub; ++j) {
       if (f[j]) {
         const int64_t t = c0 + (int64_t)j * kXdThreads + tid;
-        list[n_app + woff[j * kXdWaves + w] + __popcll(m[j] & below)] = (int32_t)t;
+        const int pos = n_app + woff[j * kXdWaves + w] + __popcll(m[j] & below);
+        if (!gate_order) {
+          if (pos < room) {
+            const int s = kept0 + pos;
+            slot[t] = s;
+            tos[(int64_t)e * C + s] = (int32_t)t;
+            expert_id[t] = e;
+            gate[t] = gv[t];
+          }
+        } else {
+          list[pos] = (int32_t)t;
+          if (pos < kXdCache) {
+            akey[pos] = __float_as_uint(gv[t]);
+            atok[pos] = (int)t;
+          }
+        }
       }
     }
     n_app += s_total;
     __syncthreads();  // woff and s_total are rewritten by the next step
   }
   const int take = n_app < room ? n_app : room;
+  if (!gate_order) {
+    if (tid == 0) kept_count[e] = kept0 + take;
+    return;
+  }
   if (take == 0) return;
-  __threadfence_block();  // the list is read back by other threads of this workgroup
+  const bool cached = n_app <= kXdCache;
+  if (!cached) __threadfence_block();  // the list is read back by other threads of this workgroup
   __syncthreads();
+  auto key_at = [&](int a) -> uint32_t { return cached ? akey[a] : __float_as_uint(gv[list[a]]); };
+  auto tok_at = [&](int a) -> int { return cached ? atok[a] : list[a]; };
 
   // ---- the threshold: keys > thr are taken, and the first eq_take keys == thr ----
-  // token order: every key is 0, so the head of the list is taken
   uint32_t thr = 0u;
   int eq_take = take;
-  if (gate_order && take < n_app) {
+  if (take < n_app) {
     if (tid == 0) {
       s_prefix = 0u;
       s_mask = 0u;
@@ -125,20 +154,20 @@ __global__ __launch_bounds__(kXdThreads) void expand_round(const int32_t* __rest
       for (int b = tid; b < 256; b += kXdThreads) hist[b] = 0;
       __syncthreads();
       const uint32_t prefix = s_prefix, mask = s_mask;
-      for (int a = tid; a < n_app; a += kXdThreads) {
-        const uint32_t v = __float_as_uint(gv[list[a]]);
-        if ((v & mask) == prefix) atomicAdd(&hist[(v >> shift) & 255], 1);
+      for (int a0 = 0; a0 < n_app; a0 += kXdThreads) {  // the same trip count on every lane
+        const int a = a0 + tid;
+        const uint32_t v = a < n_app ? key_at(a) : 0u;
+        hist_add_wave(hist, (v >> shift) & 255u, a < n_app && (v & mask) == prefix);
       }
       __syncthreads();
-      if (tid == 0) {
-        int need = s_need, b = 255;
-        for (; b > 0; --b) {
-          if (hist[b] >= need) break;
-          need -= hist[b];
+      if (tid < 64) {
+        int b, need;
+        radix_pick_desc(hist, s_need, &b, &need);
+        if (tid == 0) {
+          s_need = need;
+          s_prefix = prefix | ((uint32_t)b << shift);
+          s_mask = mask | (255u << shift);
         }
-        s_need = need;
-        s_prefix = prefix | ((uint32_t)b << shift);
-        s_mask = mask | (255u << shift);
       }
       __syncthreads();
     }
@@ -147,8 +176,8 @@ __global__ __launch_bounds__(kXdThreads) void expand_round(const int32_t* __rest
   }
 
   // ---- ordered gather of the taken applicants ----
-  uint32_t* sel_key = xd_lds;
-  int* sel_tok = reinterpret_cast<int*>(xd_lds + room);
+  uint32_t* sel_key = xd_lds + 2 * kXdCache;
+  int* sel_tok = reinterpret_cast<int*>(sel_key + room);
   if (tid == 0) {
     s_base = 0;
     s_eqbase = 0;
@@ -156,8 +185,7 @@ __global__ __launch_bounds__(kXdThreads) void expand_round(const int32_t* __rest
   __syncthreads();
   for (int a0 = 0; a0 < n_app; a0 += kXdThreads) {
     const int a = a0 + tid;
-    const int t = a < n_app ? list[a] : 0;
-    const uint32_t v = (a < n_app && gate_order) ? __float_as_uint(gv[t]) : 0u;
+    const uint32_t v = a < n_app ? key_at(a) : 0u;
     const int is_eq = (a < n_app && v == thr) ? 1 : 0;
     int tot_eq;
     const int eq_rank = s_eqbase + block_exclusive_scan(is_eq, wsum, &tot_eq);
@@ -166,7 +194,7 @@ __global__ __launch_bounds__(kXdThreads) void expand_round(const int32_t* __rest
     const int pos = s_base + block_exclusive_scan(tk, wsum, &tot);
     if (tk) {
       sel_key[pos] = v;
-      sel_tok[pos] = t;
+      sel_tok[pos] = tok_at(a);
     }
     __syncthreads();
     if (tid == 0) {
@@ -176,17 +204,14 @@ __global__ __launch_bounds__(kXdThreads) void expand_round(const int32_t* __rest
     __syncthreads();
   }
 
-  // ---- slots: rank by (key descending, token ascending); the gather kept token order ----
+  // ---- slots: rank by (key descending, token ascending) ----
   for (int a = tid; a < take; a += kXdThreads) {
     const uint32_t ka = sel_key[a];
     const int ta = sel_tok[a];
-    int r = a;
-    if (gate_order) {
-      r = 0;
-      for (int b = 0; b < take; ++b) {
-        const uint32_t kb = sel_key[b];
-        r += (kb > ka || (kb == ka && sel_tok[b] < ta)) ? 1 : 0;
-      }
+    int r = 0;
+    for (int b = 0; b < take; ++b) {
+      const uint32_t kb = sel_key[b];
+      r += (kb > ka || (kb == ka && sel_tok[b] < ta)) ? 1 : 0;
     }
     const int s = kept0 + r;
     slot[ta] = s;
@@ -214,13 +239,13 @@ __global__ __launch_bounds__(1024) void expand_finalize(const int32_t* __restric
 }
 
 // ----------------------------------------------------------------------------
-size_t expand_lds_bytes(int C) { return (size_t)C * 8; }
+size_t expand_lds_bytes(int C, int gate_order) { return gate_order ? (size_t)kXdCache * 8 + (size_t)C * 8 : 0; }
 
 hipError_t launch_expand(const int32_t* ev_cm, const float* gv_cm, int64_t T, int N, int C, int M, int gate_order,
                          int32_t* slot, int32_t* expert_id, float* gate, int32_t* tos, int32_t* kept_count,
                          int32_t* active, int32_t* n_active, int32_t* n_dropped, int32_t* list, hipStream_t st) {
   for (int r = 1; r < M; ++r) {
-    hipLaunchKernelGGL(expand_round, dim3((unsigned)N), dim3(kXdThreads), expand_lds_bytes(C), st, ev_cm + r * T,
+    hipLaunchKernelGGL(expand_round, dim3((unsigned)N), dim3(kXdThreads), expand_lds_bytes(C, gate_order), st, ev_cm + r * T,
                        gv_cm + r * T, T, C, gate_order, slot, expert_id, gate, tos, kept_count, list);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

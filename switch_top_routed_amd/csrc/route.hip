@@ -103,10 +103,12 @@ __device__ void route_epilogue(float* lg, int ldl, int rows, int64_t t0, int64_t
       // index); its gate is p at that expert.  With ex.expand the further
       // choices are only candidates: they are neither counted nor written to
       // expert_id / gate
-      int ek[kMaxTopK];
-      float gk[kMaxTopK];
-      ek[0] = bi;
-      gk[0] = inv;
+      // tk bit j: expert lane + 64 j is chosen already; lane r < K keeps choice r
+      uint32_t tk = 0u;
+#pragma unroll
+      for (int j = 0; j < J; ++j) tk |= (lane + 64 * j == bi) ? (1u << j) : 0u;
+      int my_e = bi;
+      float my_g = inv;
       float gsum = inv;
       for (int r = 1; r < ex.K; ++r) {
         float bv = -INFINITY;
@@ -114,9 +116,7 @@ __device__ void route_epilogue(float* lg, int ldl, int rows, int64_t t0, int64_t
 #pragma unroll
         for (int j = 0; j < J; ++j) {
           const int n = lane + 64 * j;
-          bool taken = n >= N;
-          for (int q = 0; q < r; ++q) taken = taken || (ek[q] == n);
-          if (!taken && lv[j] > bv) {
+          if (n < N && !((tk >> j) & 1u) && lv[j] > bv) {
             bv = lv[j];
             bx = n;
           }
@@ -125,32 +125,32 @@ __device__ void route_epilogue(float* lg, int ldl, int rows, int64_t t0, int64_t
         // p of the chosen expert, from the lane that holds it
         float mine = 0.f;
 #pragma unroll
-        for (int j = 0; j < J; ++j)
-          if (lane + 64 * j == bx) mine = v[j] * inv;
-        const float pr = __shfl(mine, bx & 63, 64);
-        if (!ex.expand) {
-#pragma unroll
-          for (int j = 0; j < J; ++j) cn[j] += (lane + 64 * j == bx) ? 1 : 0;
+        for (int j = 0; j < J; ++j) {
+          if (lane + 64 * j == bx) {
+            mine = v[j] * inv;
+            tk |= 1u << j;
+            if (!ex.expand) cn[j] += 1;
+          }
         }
-        ek[r] = bx;
-        gk[r] = pr;
+        const float pr = __shfl(mine, bx & 63, 64);
+        if (lane == r) {
+          my_e = bx;
+          my_g = pr;
+        }
         gsum += pr;
       }
-      if (lane == 0 && ex.expand) {
-        for (int r = 1; r < ex.K; ++r) {
-          ex.ev_cm[(int64_t)r * T + t] = ek[r];
-          ex.gv_cm[(int64_t)r * T + t] = gk[r];
+      if (ex.expand) {
+        if (lane >= 1 && lane < ex.K) {
+          ex.ev_cm[(int64_t)lane * T + t] = my_e;
+          ex.gv_cm[(int64_t)lane * T + t] = my_g;
         }
-      } else if (lane == 0) {
-        const float rn = ex.renorm ? 1.0f / gsum : 1.0f;
-        for (int r = 0; r < ex.K; ++r) {
-          const float g = ex.renorm ? gk[r] * rn : gk[r];
-          expert_id[t * ex.K + r] = ek[r];
-          gate[t * ex.K + r] = g;
-          if (ex.ev_cm != nullptr) {
-            ex.ev_cm[(int64_t)r * T + t] = ek[r];
-            ex.gv_cm[(int64_t)r * T + t] = g;
-          }
+      } else if (lane < ex.K) {
+        const float g = ex.renorm ? my_g * (1.0f / gsum) : my_g;
+        expert_id[t * ex.K + lane] = my_e;
+        gate[t * ex.K + lane] = g;
+        if (ex.ev_cm != nullptr) {
+          ex.ev_cm[(int64_t)lane * T + t] = my_e;
+          ex.gv_cm[(int64_t)lane * T + t] = g;
         }
       }
     }

@@ -76,20 +76,20 @@ __global__ __launch_bounds__(1024) void ec_select(const float* __restrict__ prob
     for (int b = tid; b < 256; b += 1024) hist[b] = 0;
     __syncthreads();
     const uint32_t prefix = s_prefix, mask = s_mask;
-    for (int64_t t = tid; t < T; t += 1024) {
-      const uint32_t v = key[t];
-      if ((v & mask) == prefix) atomicAdd(&hist[(v >> shift) & 255], 1);
+    for (int64_t t0 = 0; t0 < T; t0 += 1024) {  // the same trip count on every lane
+      const int64_t t = t0 + tid;
+      const uint32_t v = t < T ? key[t] : 0u;
+      hist_add_wave(hist, (v >> shift) & 255u, t < T && (v & mask) == prefix);
     }
     __syncthreads();
-    if (tid == 0) {
-      int need = s_need, b = 255;
-      for (; b > 0; --b) {
-        if (hist[b] >= need) break;
-        need -= hist[b];
+    if (tid < 64) {
+      int b, need;
+      radix_pick_desc(hist, s_need, &b, &need);
+      if (tid == 0) {
+        s_need = need;
+        s_prefix = prefix | ((uint32_t)b << shift);
+        s_mask = mask | (255u << shift);
       }
-      s_need = need;
-      s_prefix = prefix | ((uint32_t)b << shift);
-      s_mask = mask | (255u << shift);
     }
     __syncthreads();
   }
