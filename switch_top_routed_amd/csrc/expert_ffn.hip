@@ -46,8 +46,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
 
+// cache policy of the weight stream: nt (non-temporal).  Every weight byte is
+// read once per launch, so it should not evict what is reused (the token rows,
+// the outputs).  Measured on the base layer: 125 -> 123 us per launch; decode
+// batch 49 -> 46 us.
 #ifndef SWM_W_CPOL
-#define SWM_W_CPOL 0
+#define SWM_W_CPOL 2
 #endif
 
 __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
@@ -230,14 +234,13 @@ __device__ __forceinline__ void ffn_stream(const uint16_t* __restrict__ A, const
       // The k-loop has no data-dependent branches (the waitcnt pass would drain
       // every load at each join).  The step count is padded to a multiple of
       // STAGES; prefetches past the last step re-read the last weight block (an L2
-      // hit) and padding steps multiply a zero A fragment.
+      // hit) and padding steps multiply a zero A fragment.  The zero is selected
+      // where the fragment is used: a select right after the load would make the
+      // load wait for itself, and with it for every load issued before it.
       auto load_a = [&](u32x4 (&dst)[MT], int step) {
         const int so = (step < nk ? step : nk - 1) * a_step;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const u32x4 v = buffer_load16(ares, a_voff[mt], so);
-          dst[mt] = step < nk ? v : zero;
-        }
+        for (int mt = 0; mt < MT; ++mt) dst[mt] = buffer_load16(ares, a_voff[mt], so);
       };
       typedef typename WRow<J>::type wrow_t;
       auto load_w = [&](wrow_t (&dst)[8], int step) {
@@ -245,31 +248,38 @@ __device__ __forceinline__ void ffn_stream(const uint16_t* __restrict__ A, const
 #pragma unroll
         for (int r = 0; r < 8; ++r) dst[r] = WRow<J>::load(wres, w_voff, so + r * w_row);
       };
-      u32x4 acur[MT];
-      load_a(acur, 0);  // oldest load: waiting for it never waits for the weights behind it
+      // A fragments and weight blocks share one ring: step s's loads are issued
+      // together STAGES - 1 steps ahead.  Loads retire in order, so an A load
+      // issued later than the weights (say one step ahead) would make the wait
+      // for it drain the weight ring as well.
+      u32x4 abuf[STAGES][MT];
       wrow_t buf[STAGES][8];
 #pragma unroll
-      for (int s = 0; s < STAGES - 1; ++s) load_w(buf[s], s);
+      for (int s = 0; s < STAGES - 1; ++s) {
+        load_w(buf[s], s);
+        load_a(abuf[s], s);
+      }
 
       const int nk_pad = (nk + STAGES - 1) / STAGES * STAGES;
       for (int it = 0; it < nk_pad; it += STAGES) {
 #pragma unroll
         for (int u = 0; u < STAGES; ++u) {
           const int cur = it + u;
-          u32x4 anext[MT];
-          load_a(anext, cur + 1);
           load_w(buf[(u + STAGES - 1) % STAGES], cur + STAGES - 1);
+          load_a(abuf[(u + STAGES - 1) % STAGES], cur + STAGES - 1);
           // keep the prefetches ahead of this step's math: the scheduler would sink
           // them below the MFMAs, and the next step would then wait for them
           __builtin_amdgcn_sched_barrier(0);
+          const bool live = cur < nk;
+          u32x4 af[MT];
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) af[mt] = live ? abuf[u][mt] : zero;
           u32x4 bt[J];
           WRow<J>::transpose(buf[u], bt);
 #pragma unroll
           for (int j = 0; j < J; ++j)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) acc[mt][j] = mfma_bf16_16x16x32(acur[mt], bt[j], acc[mt][j]);
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) acur[mt] = anext[mt];
+            for (int mt = 0; mt < MT; ++mt) acc[mt][j] = mfma_bf16_16x16x32(af[mt], bt[j], acc[mt][j]);
         }
       }
     }
