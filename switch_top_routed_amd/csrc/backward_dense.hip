@@ -226,26 +226,61 @@ __global__ __launch_bounds__(256, 2) void dense_tile_dma(const uint16_t* __restr
     }
   }
   SWM_DN_WAIT_VMCNT_LGKM0(0);  // no load may still be writing LDS when the workgroup exits
+  __syncthreads();              // every wave is done with the stages: they now stage the output
 
-  // lane: rows 4 kg + i of each 16-row tile, column c of each 16-column tile
+  // A lane holds rows 4 kg + i of each 16-row tile and column c of each
+  // 16-column tile.  Each 16-row slice of the wave's tile goes through an LDS
+  // region of its own (rows padded by 16 bytes so that the four kg row groups
+  // fall on different banks) and leaves as 16-byte non-temporal stores over
+  // whole 128-byte lines.  EPI 2 applies the mask to the staged chunk, from a
+  // 16-byte load of the same chunk of H.
+  constexpr int EB = EPI == 1 ? 4 : 2;        // output bytes per element
+  constexpr int ROWB = 16 * NJ * EB + 16;     // staged row: the wave's 16 NJ columns
+  constexpr int CH = 16 * NJ * EB / 16;       // 16-byte chunks per staged row
+  static_assert(2 * 16 * ROWB <= SB, "two waves' staging fits one LDS stage");
+  unsigned char* ost = (w < 2 ? st0 : st1) + (w & 1) * 16 * ROWB;
+  const int64_t col0 = (int64_t)n0 + wn * 16 * NJ;
 #pragma unroll
-  for (int mt = 0; mt < MTW; ++mt)
+  for (int mt = 0; mt < MTW; ++mt) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rl = wm * (BM / 2) + mt * 16 + kg * 4 + i;
-      if (rl >= rows) continue;
-      const int64_t row = (int64_t)(m0 + rl) * Ncols + n0 + wn * 16 * NJ + c;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        float v = acc[mt][j][i];
-        if (EPI == 1) {
-          static_cast<float*>(out)[row + 16 * j] = v;
-        } else {
-          if (EPI == 2) v = bf2f(H[row + 16 * j]) > 0.f ? v : 0.f;
-          static_cast<uint16_t*>(out)[row + 16 * j] = (uint16_t)f2bf(v);
+        unsigned char* p = ost + (kg * 4 + i) * ROWB + (16 * j + c) * EB;
+        if (EPI == 1)
+          *reinterpret_cast<float*>(p) = acc[mt][j][i];
+        else
+          *reinterpret_cast<uint16_t*>(p) = (uint16_t)f2bf(acc[mt][j][i]);
+      }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int q0 = 0; q0 < 16 * CH; q0 += 64) {
+      const int q = q0 + lane, r = q / CH, ch = q - r * CH;
+      const int rl = wm * (BM / 2) + mt * 16 + r;
+      u32x4 v = *reinterpret_cast<const u32x4*>(ost + r * ROWB + ch * 16);
+      if (rl < rows) {
+        const int64_t off = (int64_t)(m0 + rl) * Ncols + col0 + ch * (16 / EB);  // elements
+        if (EPI == 2) {  // keep where H > 0: bf16 bits in (0, 0x7f80] (positive, up to +inf)
+          const u32x4 h = *reinterpret_cast<const u32x4*>(H + off);
+#pragma unroll
+          for (int q2 = 0; q2 < 4; ++q2) {
+            const uint32_t lo = h[q2] & 0xffffu, hi = h[q2] >> 16;
+            const uint32_t keep = ((lo - 1u) < 0x7f80u ? 0x0000ffffu : 0u) | ((hi - 1u) < 0x7f80u ? 0xffff0000u : 0u);
+            v[q2] &= keep;
+          }
         }
+        if (EPI == 1)
+          __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(static_cast<float*>(out) + off));
+        else
+          __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + off));
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();  // the next slice overwrites the region
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
 }
 
 // ----------------------------------------------------------------------------

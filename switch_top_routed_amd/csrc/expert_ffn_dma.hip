@@ -233,23 +233,43 @@ __global__ __launch_bounds__(256, 2) void ffn_tile_dma(
 
   // no load may still be writing this workgroup's LDS when it exits
   SWM_WAIT_VMCNT_LGKM0(0);
+  __syncthreads();  // every wave is done with the stages: they now stage the output
 
-  // lane holds rows 4 kg + i of each 16-row tile and column c of each 16-column tile
+  // A lane holds rows 4 kg + i of each 16-row tile and column c of each
+  // 16-column tile, so direct stores would write 32 bytes per row and
+  // instruction.  Each 16-row slice of the wave's tile goes through its own LDS
+  // region instead (rows padded to 16 NJ * 2 + 16 bytes: the four kg row groups
+  // land on different banks) and leaves as 16-byte non-temporal stores that
+  // cover whole 128-byte lines (4 rows x 32 NJ bytes per instruction).
+  constexpr int ROWB = 32 * NJ + 16;
+  static_assert(4 * 16 * ROWB <= SB, "the output staging fits one LDS stage");
+  unsigned char* ost = st0 + w * 16 * ROWB;
+  constexpr int CH = 2 * NJ;  // 16-byte chunks per staged row
 #pragma unroll
   for (int mt = 0; mt < MTW; ++mt) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rl = wm * (BM / 2) + mt * 16 + kg * 4 + i;
-      if (rl < rows) {
-        uint16_t* dst = out + ((int64_t)e * C + m0 + rl) * Ncols + n0 + wn * 16 * NJ + c;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          float v = acc[mt][j][i];
-          if (relu) v = fmaxf(v, 0.f);
-          dst[16 * j] = (uint16_t)f2bf(v);
-        }
+      for (int j = 0; j < NJ; ++j) {
+        float v = acc[mt][j][i];
+        if (relu) v = fmaxf(v, 0.f);
+        *reinterpret_cast<uint16_t*>(ost + (kg * 4 + i) * ROWB + (16 * j + c) * 2) = (uint16_t)f2bf(v);
       }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int q0 = 0; q0 < 16 * CH; q0 += 64) {
+      const int q = q0 + lane, r = q / CH, ch = q - r * CH;
+      const int rl = wm * (BM / 2) + mt * 16 + r;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ost + r * ROWB + ch * 16);
+      if (rl < rows)
+        __builtin_nontemporal_store(
+            v, reinterpret_cast<u32x4*>(out + ((int64_t)e * C + m0 + rl) * Ncols + n0 + wn * 16 * NJ + ch * 8));
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();  // the next slice overwrites the region
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
 
