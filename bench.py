@@ -54,13 +54,13 @@ FFN_SOURCES = ("switch_top_routed_amd/csrc/expert_ffn.hip", "switch_top_routed_a
 # profiles/*_hbm_traffic.md.
 TRAFFIC = {
     "switch-base-uniform": {
-        "sources_sha256": "ce42edfacc82c46dbaa249026799b8f7e23a135b1a3cde1ec8754ab452708549",
-        "fetch_kib": [298400.0, 308566.0], "write_kib": [24108.0, 6027.0],
+        "sources_sha256": "c37c55f6f3d44f427e161a0c08d405f37d630fec7ba963b85faca058e5d7b0c0",
+        "fetch_kib": [306111.0, 315077.0], "write_kib": [25132.0, 7051.0],
         "fetch_scale": 2.0, "write_scale": 1.0,
     },
     "switch-large-shared": {
-        "sources_sha256": "ce42edfacc82c46dbaa249026799b8f7e23a135b1a3cde1ec8754ab452708549",
-        "fetch_kib": [5327956.0, 5510926.0], "write_kib": [262145.0, 163842.0],
+        "sources_sha256": "c37c55f6f3d44f427e161a0c08d405f37d630fec7ba963b85faca058e5d7b0c0",
+        "fetch_kib": [5329196.0, 5500907.0], "write_kib": [262233.0, 163840.0],
         "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
@@ -71,13 +71,13 @@ TRAFFIC = {
 BWD_SOURCES = ("switch_top_routed_amd/csrc/backward_fused.hip", "switch_top_routed_amd/csrc/common.hpp")
 BWD_TRAFFIC = {
     "switch-base-uniform": {
-        "sources_sha256": "89f4db8815d7f5ac6dd593a5c3008e48fd6153eb50998cb69c253a6570ef8b1c",
-        "fetch_kib": [322823.0, 313085.0], "write_kib": [614899.0, 601879.0],
+        "sources_sha256": "c6c269094b675f7b067d8f8b1bba07af0d3d0f9072471e1352637470ab7e43fc",
+        "fetch_kib": [322784.0, 313087.0], "write_kib": [614902.0, 601879.0],
         "fetch_scale": 2.0, "write_scale": 1.0,
     },
     "switch-large-shared": {
-        "sources_sha256": "89f4db8815d7f5ac6dd593a5c3008e48fd6153eb50998cb69c253a6570ef8b1c",
-        "fetch_kib": [5914936.0, 5783067.0], "write_kib": [10763009.0, 10813443.0],
+        "sources_sha256": "c6c269094b675f7b067d8f8b1bba07af0d3d0f9072471e1352637470ab7e43fc",
+        "fetch_kib": [5893690.0, 5795078.0], "write_kib": [10761174.0, 10813443.0],
         "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
