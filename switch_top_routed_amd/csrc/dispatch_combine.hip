@@ -55,61 +55,74 @@ __global__ __launch_bounds__(kRowThreads) void combine_rows(const u32x4* __restr
   const u32x4* orow = eo + ((int64_t)e * C + (kept ? s : 0)) * chunks;
   const u32x4* srow = sh ? sh + t * chunks : nullptr;
   u32x4* yr = y + t * chunks;
-  for (int c = lane; c < chunks; c += 64) {
-    const u32x4 xv = xr[c];
-    if (!kept && !sh) {
-      yr[c] = xv;  // dropped token: bit copy of its input
-      continue;
-    }
-    float v[BF16 ? 8 : 4];
-    if (BF16) {
+  const bool need_x = !kept || res;  // a kept token without the residual flag never reads x
+  constexpr int U = 4;               // chunks per lane in flight
+  for (int c0 = lane; c0 < chunks; c0 += 64 * U) {
+    u32x4 xv[U], ov[U], sv[U];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        v[2 * q] = bf2f(xv[q] & 0xffffu);
-        v[2 * q + 1] = bf2f(xv[q] >> 16);
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + 64 * u;
+      const bool in = c < chunks;
+      xv[u] = (in && need_x) ? xr[c] : u32x4{0u, 0u, 0u, 0u};
+      ov[u] = (in && kept) ? orow[c] : u32x4{0u, 0u, 0u, 0u};
+      sv[u] = (in && sh) ? srow[c] : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + 64 * u;
+      if (c >= chunks) break;
+      if (!kept && !sh) {
+        yr[c] = xv[u];  // dropped token: bit copy of its input
+        continue;
       }
-    } else {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) v[q] = __uint_as_float(xv[q]);
-    }
-    if (kept) {
-      const u32x4 ov = orow[c];
-      float o[BF16 ? 8 : 4];
+      float v[BF16 ? 8 : 4];
       if (BF16) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          o[2 * q] = bf2f(ov[q] & 0xffffu);
-          o[2 * q + 1] = bf2f(ov[q] >> 16);
+          v[2 * q] = bf2f(xv[u][q] & 0xffffu);
+          v[2 * q + 1] = bf2f(xv[u][q] >> 16);
         }
       } else {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) o[q] = __uint_as_float(ov[q]);
+        for (int q = 0; q < 4; ++q) v[q] = __uint_as_float(xv[u][q]);
       }
+      if (kept) {
+        float o[BF16 ? 8 : 4];
+        if (BF16) {
 #pragma unroll
-      for (int q = 0; q < (BF16 ? 8 : 4); ++q) v[q] = res ? v[q] + scale * o[q] : scale * o[q];
-    }
-    if (sh) {
-      const u32x4 sv = srow[c];
+          for (int q = 0; q < 4; ++q) {
+            o[2 * q] = bf2f(ov[u][q] & 0xffffu);
+            o[2 * q + 1] = bf2f(ov[u][q] >> 16);
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) o[q] = __uint_as_float(ov[u][q]);
+        }
+#pragma unroll
+        for (int q = 0; q < (BF16 ? 8 : 4); ++q) v[q] = res ? v[q] + scale * o[q] : scale * o[q];
+      }
+      if (sh) {
+        if (BF16) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            v[2 * q] += bf2f(sv[u][q] & 0xffffu);
+            v[2 * q + 1] += bf2f(sv[u][q] >> 16);
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] += __uint_as_float(sv[u][q]);
+        }
+      }
+      u32x4 out;
       if (BF16) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          v[2 * q] += bf2f(sv[q] & 0xffffu);
-          v[2 * q + 1] += bf2f(sv[q] >> 16);
-        }
+        for (int q = 0; q < 4; ++q) out[q] = pack_bf2(v[2 * q], v[2 * q + 1]);
       } else {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] += __uint_as_float(sv[q]);
+        for (int q = 0; q < 4; ++q) out[q] = __float_as_uint(v[q]);
       }
+      yr[c] = out;
     }
-    u32x4 out;
-    if (BF16) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) out[q] = pack_bf2(v[2 * q], v[2 * q + 1]);
-    } else {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) out[q] = __float_as_uint(v[q]);
-    }
-    yr[c] = out;
   }
 }
 

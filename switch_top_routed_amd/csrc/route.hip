@@ -400,7 +400,7 @@ __device__ __forceinline__ void finalize_partials(const float* __restrict__ part
                                                   float* __restrict__ f, float* __restrict__ P,
                                                   float* __restrict__ l_aux, int* cnt_out, int K = 1) {
   __shared__ double sp[1024];
-  __shared__ double sl[1024];
+  __shared__ double sl[16];
   const int tid = threadIdx.x;
   const int G = 1024 / NP;
   const int n = tid % NP, g = tid / NP;
@@ -443,13 +443,16 @@ __device__ __forceinline__ void finalize_partials(const float* __restrict__ part
     P[tid] = (float)pn;
     term = fn * pn;
   }
-  sl[tid] = term;
+  // L_aux: a fixed xor tree inside each wave, then the 16 wave sums in wave order
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) term += __shfl_xor(term, o, 64);
+  if ((tid & 63) == 0) sl[tid >> 6] = term;
   __syncthreads();
-  for (int o = 512; o > 0; o >>= 1) {
-    if (tid < o) sl[tid] += sl[tid + o];
-    __syncthreads();
+  if (tid == 0) {
+    double a = 0.0;
+    for (int i = 0; i < 16; ++i) a += sl[i];
+    l_aux[0] = (float)((double)N * a);
   }
-  if (tid == 0) l_aux[0] = (float)((double)N * sl[0]);
 }
 
 __global__ __launch_bounds__(1024) void route_finalize(const float* __restrict__ part_p,
