@@ -29,31 +29,59 @@ __device__ __forceinline__ f32x4 mfma_bf16_16x16x32(const u32x4& a, const u32x4&
                                                   0, 0);
 }
 
-// Butterfly all-reduce over the 64 lanes.  Every lane ends with the same bits
-// (each step adds a value to its partner's value, and fp addition commutes).
+// Wave reductions on DPP lane moves (no LDS traffic; a ds_bpermute shuffle
+// costs an LDS round trip per step): quad swaps (lane ^ 1, lane ^ 2), the half-
+// row and row mirrors (the 8- and 16-lane groups), then row broadcasts of lanes
+// 15 and 31 into the rows above.  Lane 63 ends with the whole wave's result,
+// which is read back as a wave-uniform value, so every lane returns the same
+// bits.  All 64 lanes must be active.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ int dpp_move(int old, int src) {
+  return __builtin_amdgcn_update_dpp(old, src, CTRL, ROW_MASK, 0xf, false);
+}
+constexpr int kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140,
+              kDppBcast15 = 0x142, kDppBcast31 = 0x143;
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += __int_as_float(dpp_move<kDppQuadXor1>(0, __float_as_int(v)));
+  v += __int_as_float(dpp_move<kDppQuadXor2>(0, __float_as_int(v)));
+  v += __int_as_float(dpp_move<kDppHalfMirror>(0, __float_as_int(v)));
+  v += __int_as_float(dpp_move<kDppMirror>(0, __float_as_int(v)));
+  v += __int_as_float(dpp_move<kDppBcast15, 0xa>(0, __float_as_int(v)));  // rows 1, 3 (+0 elsewhere)
+  v += __int_as_float(dpp_move<kDppBcast31, 0xc>(0, __float_as_int(v)));  // rows 2, 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 __device__ __forceinline__ int wave_sum_int(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += dpp_move<kDppQuadXor1>(0, v);
+  v += dpp_move<kDppQuadXor2>(0, v);
+  v += dpp_move<kDppHalfMirror>(0, v);
+  v += dpp_move<kDppMirror>(0, v);
+  v += dpp_move<kDppBcast15, 0xa>(0, v);
+  v += dpp_move<kDppBcast31, 0xc>(0, v);
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
 // (value, index) arg-max over the wave; equal values resolve to the lower index.
-__device__ __forceinline__ void wave_argmax(float& v, int& idx) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    float ov = __shfl_xor(v, o, kWave);
-    int oi = __shfl_xor(idx, o, kWave);
-    if (ov > v || (ov == v && oi < idx)) {
-      v = ov;
-      idx = oi;
-    }
+// Lanes a broadcast step does not write get their own pair back (no change).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void argmax_step(float& v, int& idx) {
+  const float ov = __int_as_float(dpp_move<CTRL, ROW_MASK>(__float_as_int(v), __float_as_int(v)));
+  const int oi = dpp_move<CTRL, ROW_MASK>(idx, idx);
+  if (ov > v || (ov == v && oi < idx)) {
+    v = ov;
+    idx = oi;
   }
+}
+__device__ __forceinline__ void wave_argmax(float& v, int& idx) {
+  argmax_step<kDppQuadXor1, 0xf>(v, idx);
+  argmax_step<kDppQuadXor2, 0xf>(v, idx);
+  argmax_step<kDppHalfMirror, 0xf>(v, idx);
+  argmax_step<kDppMirror, 0xf>(v, idx);
+  argmax_step<kDppBcast15, 0xa>(v, idx);
+  argmax_step<kDppBcast31, 0xc>(v, idx);
+  v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  idx = __builtin_amdgcn_readlane(idx, 63);
 }
 
 // hist[digit] += 1 for every active lane (digit < 256); the lanes of a wave
