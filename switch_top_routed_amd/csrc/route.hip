@@ -29,6 +29,16 @@
 namespace swm {
 
 constexpr int kRouteThreads = 256;
+constexpr size_t kRouteXlMax = 64 * 1024;  // token rows staged in LDS up to this many bytes per workgroup
+
+namespace {
+typedef __attribute__((address_space(3))) void lds_void_rt;
+// gfx950 builtin in a plain function (a kernel template naming it directly
+// loses its host launch stub): 16 bytes per lane, lane i lands at lds + 16 i
+__device__ __forceinline__ void rt_dma16(__amdgpu_buffer_rsrc_t r, unsigned char* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_rt*)lds, 16, voff, 0, 0, 0);
+}
+}  // namespace
 
 // logits for `rows` tokens live in LDS lg[m * ldl + n] (no bias yet)
 // lg must hold >= 8 * N floats; it is reused for the cross-wave partial sums.
@@ -184,7 +194,12 @@ __device__ void route_epilogue(float* lg, int ldl, int rows, int64_t t0, int64_t
 // selects 8 consecutive k.  A = x rows (k contiguous), B = W_g^T, whose
 // fragment is 8 consecutive k of one W_g row (also contiguous).
 // ----------------------------------------------------------------------------
-template <int TM, int NG, int J>
+// XL: the workgroup's token rows are copied to LDS once (direct global-to-LDS
+// loads, 16-byte chunks of each row XOR-swizzled by the row's low 4 bits so
+// that 16 rows read at one k fall on distinct banks) and the k-loop streams
+// only W_g.  Without it every wave streams the rows too, and because loads
+// retire in order each step also waits for its rows' first trip from HBM.
+template <int TM, int NG, int J, bool XL>
 __global__ __launch_bounds__(kRouteThreads) void route_fused_bf16(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg, const float* __restrict__ bias, int64_t T, int d,
     int N, int32_t* __restrict__ expert_id, float* __restrict__ gate, float* __restrict__ part_p,
@@ -202,13 +217,24 @@ __global__ __launch_bounds__(kRouteThreads) void route_fused_bf16(
   // Operands through buffer loads: rows past T or N get a lane offset beyond the
   // descriptor's extent and read zeros, so the k-loop needs no branches and the
   // loads of RP steps stay in flight ahead of the MFMAs (a register ring).
-  constexpr int RP = TM >= 4 ? 4 : 8;
+  constexpr int RP = TM >= 4 ? 4 : 8;  // a 12-deep ring with XL measured slower (16.7 against 15.5 us)
   const int64_t rows_here = (T - t0) < TM * 16 ? (T - t0) : TM * 16;
   const __amdgpu_buffer_rsrc_t xres =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x + t0 * d), (short)0, (int)(rows_here * d * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t wres =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(wg), (short)0, (int)((int64_t)N * d * 2), 0x00020000);
   const int kpad = (ksteps + RP - 1) / RP * RP;
+  const int cpr = d >> 3;  // 16-byte chunks per row (a multiple of 16: d % 128 == 0)
+  unsigned char* xt = reinterpret_cast<unsigned char*>(smem + TM * 16 * ldl);
+  if (XL) {
+    const int nb = TM * 16 * cpr / 64;  // 1 KB blocks of the tile
+    for (int b = w; b < nb; b += 4) {
+      const int q = b * 64 + lane, r = q / cpr, kc = (q - r * cpr) ^ (r & 15);
+      rt_dma16(xres, xt + b * 1024, r < rows_here ? (r * d + kc * 8) * 2 : 0x7ffffff0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // vmcnt, expcnt and lgkmcnt all zero
+    __syncthreads();
+  }
   for (int ntb = w * NG; ntb < NT; ntb += 4 * NG) {
     f32x4 acc[TM][NG];
 #pragma unroll
@@ -231,7 +257,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_fused_bf16(
       const int so = (ks < ksteps ? ks : ksteps - 1) * 64;  // past the end: re-read the last step
 #pragma unroll
       for (int mt = 0; mt < TM; ++mt)
-        ra[slot][mt] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, a_voff[mt], so, 0));
+        if (!XL)
+          ra[slot][mt] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, a_voff[mt], so, 0));
 #pragma unroll
       for (int g = 0; g < NG; ++g)
         rb[slot][g] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, b_voff[g], so, 0));
@@ -247,7 +274,14 @@ __global__ __launch_bounds__(kRouteThreads) void route_fused_bf16(
         const bool live = ks < ksteps;
 #pragma unroll
         for (int mt = 0; mt < TM; ++mt) {
-          const u32x4 a = live ? ra[u][mt] : zero;
+          u32x4 a;
+          if (XL) {
+            const int r = mt * 16 + c, kc = ((ks < ksteps ? ks : 0) * 4 + kg) ^ (r & 15);
+            a = *reinterpret_cast<const u32x4*>(xt + (r * cpr + kc) * 16);
+          } else {
+            a = ra[u][mt];
+          }
+          a = live ? a : zero;
 #pragma unroll
           for (int g = 0; g < NG; ++g) acc[mt][g] = mfma_bf16_16x16x32(a, rb[u][g], acc[mt][g]);
         }
@@ -601,17 +635,22 @@ static hipError_t launch_route_j(const RoutePlan& pl, const void* x, const void*
   if (dtype == 1 && pl.split == 0) {
     const int NT = (N + 15) / 16;
     const size_t lds = (size_t)pl.tm * 16 * NT * 16 * 4;
+    const size_t xl_bytes = (size_t)pl.tm * 16 * d * 2;  // the token rows of a workgroup
+    const bool xl = xl_bytes <= kRouteXlMax;
     dim3 grid((unsigned)pl.nblk);
     auto* xb = static_cast<const uint16_t*>(x);
     auto* wb = static_cast<const uint16_t*>(wg);
     if (pl.tm == 4)
-      hipLaunchKernelGGL((route_fused_bf16<4, 2, J>), grid, dim3(kRouteThreads), lds, st, xb, wb, bias, T, d, N,
+      hipLaunchKernelGGL((route_fused_bf16<4, 2, J, false>), grid, dim3(kRouteThreads), lds, st, xb, wb, bias, T, d, N,
                          expert_id, gate, part_p, part_cnt, local_rank, ex);
     else if (pl.tm == 2)
-      hipLaunchKernelGGL((route_fused_bf16<2, 2, J>), grid, dim3(kRouteThreads), lds, st, xb, wb, bias, T, d, N,
+      hipLaunchKernelGGL((route_fused_bf16<2, 2, J, false>), grid, dim3(kRouteThreads), lds, st, xb, wb, bias, T, d, N,
                          expert_id, gate, part_p, part_cnt, local_rank, ex);
+    else if (xl)
+      hipLaunchKernelGGL((route_fused_bf16<1, 2, J, true>), grid, dim3(kRouteThreads), lds + xl_bytes, st, xb, wb, bias,
+                         T, d, N, expert_id, gate, part_p, part_cnt, local_rank, ex);
     else
-      hipLaunchKernelGGL((route_fused_bf16<1, 2, J>), grid, dim3(kRouteThreads), lds, st, xb, wb, bias, T, d, N,
+      hipLaunchKernelGGL((route_fused_bf16<1, 2, J, false>), grid, dim3(kRouteThreads), lds, st, xb, wb, bias, T, d, N,
                          expert_id, gate, part_p, part_cnt, local_rank, ex);
   } else if (dtype == 1) {
     float* plog = reinterpret_cast<float*>(ws + pl.off_logits);
