@@ -54,13 +54,13 @@ FFN_SOURCES = ("switch_top_routed_amd/csrc/expert_ffn.hip", "switch_top_routed_a
 # profiles/*_hbm_traffic.md.
 TRAFFIC = {
     "switch-base-uniform": {
-        "sources_sha256": "c37c55f6f3d44f427e161a0c08d405f37d630fec7ba963b85faca058e5d7b0c0",
-        "fetch_kib": [306111.0, 315077.0], "write_kib": [25132.0, 7051.0],
+        "sources_sha256": "6b1b81e3f00ac42234e4f877f70a36fca106f02e337cb54ef31dc6a640417266",
+        "fetch_kib": [306078.0, 315040.0], "write_kib": [25132.0, 7051.0],
         "fetch_scale": 2.0, "write_scale": 1.0,
     },
     "switch-large-shared": {
-        "sources_sha256": "c37c55f6f3d44f427e161a0c08d405f37d630fec7ba963b85faca058e5d7b0c0",
-        "fetch_kib": [5329196.0, 5500907.0], "write_kib": [262233.0, 163840.0],
+        "sources_sha256": "6b1b81e3f00ac42234e4f877f70a36fca106f02e337cb54ef31dc6a640417266",
+        "fetch_kib": [5327476.0, 5499786.0], "write_kib": [262205.0, 163840.0],
         "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
@@ -71,13 +71,13 @@ TRAFFIC = {
 BWD_SOURCES = ("switch_top_routed_amd/csrc/backward_fused.hip", "switch_top_routed_amd/csrc/common.hpp")
 BWD_TRAFFIC = {
     "switch-base-uniform": {
-        "sources_sha256": "c6c269094b675f7b067d8f8b1bba07af0d3d0f9072471e1352637470ab7e43fc",
-        "fetch_kib": [322784.0, 313087.0], "write_kib": [614902.0, 601879.0],
+        "sources_sha256": "409d356bb35470314da9ef7f5376d0dd79ac1a74923680b28b0e5940205c76b4",
+        "fetch_kib": [322775.0, 313102.0], "write_kib": [614904.0, 601879.0],
         "fetch_scale": 2.0, "write_scale": 1.0,
     },
     "switch-large-shared": {
-        "sources_sha256": "c6c269094b675f7b067d8f8b1bba07af0d3d0f9072471e1352637470ab7e43fc",
-        "fetch_kib": [5893690.0, 5795078.0], "write_kib": [10761174.0, 10813443.0],
+        "sources_sha256": "409d356bb35470314da9ef7f5376d0dd79ac1a74923680b28b0e5940205c76b4",
+        "fetch_kib": [5884988.0, 5800569.0], "write_kib": [10761303.0, 10813442.0],
         "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
