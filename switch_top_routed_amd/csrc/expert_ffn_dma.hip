@@ -301,13 +301,18 @@ bool tiled_ffn_applies(int C, int d, int dff) { return C > 64 && d % 256 == 0 &&
 // 160 x 256 tiles with 2 stages for 128 < C <= 160 (one m-chunk per expert:
 // each weight panel is streamed once; measured on the 128-expert large layer,
 // GEMM 1 1.97 ms against 2.09 ms with 3 stages and 2.83 ms with 160 x 128
-// tiles); 128 x 256 tiles with 3 stages otherwise, including the shared dense
-// expert (1.21 ms per GEMM, against 1.27-1.45 ms for 160 x 256 or 2 stages).
+// tiles); 96 x 256 tiles with 2 stages for 64 < C <= 96 (top-2 on the base
+// layer, C = 80: 132 us per launch against 138 us with 128 x 256 x 3 and
+// 135-145 us for the other shapes tried); 128 x 256 tiles with 3 stages
+// otherwise, including the shared dense expert (1.21 ms per GEMM, against
+// 1.27-1.45 ms for 160 x 256 or 2 stages).
 hipError_t launch_tiled_dma(const void* A, const void* W, void* out, const int32_t* kept, const int32_t* active,
                             const int32_t* n_active, int N, int C, int K, int Ncols, int relu, hipStream_t st,
                             const int32_t* gather, int64_t a_rows) {
   if (C > 128 && C <= 160)
     return launch_dma<SWM_DMA_R>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st, gather, a_rows);
+  if (C > 64 && C <= 96)
+    return launch_dma<3, 8, 2>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st, gather, a_rows);
   return launch_dma<SWM_DMA_D>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st, gather, a_rows);
 }
 

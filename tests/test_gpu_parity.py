@@ -303,9 +303,10 @@ EDGE = [
     _custom("f32-odd", 77, 12, 20, 5, 0.8, dtype="f32", seed=6),
     _custom("ragged-gate", 1000, 256, 384, 16, 0.5, seed=7, priority="gate", gate_scale=False),
     _custom("residual", 700, 128, 256, 8, 1.0, seed=8, residual_all=True),
+    _custom("tiled-c90", 720, 256, 512, 8, 1.0, seed=15, bias_scale=0.4),      # C = 90: 96 x 256 tiles
     _custom("tiled-c128", 2048, 256, 512, 16, 1.0, seed=11, bias_scale=0.3),   # C > 64: LDS-tiled GEMM, 128 x 256 tiles
-    _custom("tiled-c150", 1200, 256, 512, 8, 1.0, seed=13, bias_scale=0.5),     # C = 150: 160 x 128 tiles
-    _custom("tiled-c180", 1440, 512, 256, 8, 1.0, seed=14, priority="gate"),    # C = 180: 192 x 256 tiles
+    _custom("tiled-c150", 1200, 256, 512, 8, 1.0, seed=13, bias_scale=0.5),     # C = 150: 160 x 256 tiles
+    _custom("tiled-c180", 1440, 512, 256, 8, 1.0, seed=14, priority="gate"),    # C = 180: two 128-row m-chunks
     _custom("tiled-c200", 1600, 512, 256, 8, 1.0, seed=12, priority="gate"),    # C = 200: two 128-row m-chunks
 ]
 
