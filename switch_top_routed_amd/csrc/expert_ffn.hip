@@ -22,7 +22,9 @@
 //  * A = token rows (k contiguous), 16 rows per MFMA tile, up to MT tiles per
 //    item.  Rows at or beyond kept_count are neither loaded (they read as zero
 //    through the buffer descriptor) nor stored, and items beyond kept_count are
-//    skipped, so empty capacity slots cost nothing.
+//    skipped, so empty capacity slots cost nothing.  The hidden matrix that the
+//    first GEMM writes for the second is fragment-blocked (see hblk_pos) unless
+//    the caller keeps it.
 //  * Work item = (active expert, 64-column block, m-chunk of MT*16 rows).  The
 //    KW waves that share an item (1, 2 or 4, chosen on the device from n_active
 //    so that every wave slot of the persistent grid is busy) take every KW-th
@@ -159,12 +161,26 @@ __device__ __forceinline__ void store_row<8>(uint16_t* p, const float (&v)[8], b
   __builtin_nontemporal_store(pack8(v, relu), reinterpret_cast<u32x4*>(p));
 }
 
+// Fragment-blocked hidden matrix.  Between the two GEMMs the hidden rows of an
+// expert are stored as 1 KB blocks, one per (32-deep k-step, 16-row tile):
+// block (s, t) of expert e starts at element (e * tiles * 16 * d_ff) +
+// (s * tiles + t) * 512 and holds the 16 rows x 32 k of that step and tile as
+// 16-byte chunks (row r, k-chunk q = k / 8 mod 4) at chunk position
+// hblk_pos(r, q).  The second GEMM's A load of a step is then one contiguous
+// 1 KB read per tile (lane (c, kg) reads chunk hblk_pos(c, kg)) instead of 16
+// row segments of 64 bytes 2 d_ff bytes apart, and the first GEMM's stores
+// (lane (c, g) holds rows 4g + i and chunk c mod 4) still cover whole 256-byte
+// runs per instruction: for a fixed i the 16 lanes of a block write positions
+// 16i .. 16i + 15.
+__device__ __forceinline__ int hblk_pos(int r, int q) { return (r & 3) * 16 + (r >> 2) * 4 + q; }
+
 template <int MT, int WAVES, int STAGES, int J>
 __device__ __forceinline__ void ffn_stream(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
                                            uint16_t* __restrict__ out, const int32_t* __restrict__ kept_count,
                                            const int32_t* __restrict__ active, int n_act, int N, int C, int K,
                                            int Ncols, int relu, int mch, float* red,
-                                           const int32_t* __restrict__ gather, int64_t a_rows) {
+                                           const int32_t* __restrict__ gather, int64_t a_rows, int a_tiles,
+                                           int o_tiles) {
   constexpr int COLS = 16 * J;  // output columns per item
   const int tid = threadIdx.x, lane = tid & 63, c = lane & 15, kg = lane >> 4;
   // wave index as a wave-uniform (scalar) value: everything derived from it -- item,
@@ -221,9 +237,13 @@ __device__ __forceinline__ void ffn_stream(const uint16_t* __restrict__ A, const
       const __amdgpu_buffer_rsrc_t wres = make_rsrc(W + (int64_t)e * K * Ncols, (int64_t)K * Ncols * 2);
       // gather != NULL: A is the token matrix [a_rows, K] and row r of the
       // expert's buffer is token gather[e * C + r] (the dispatch folded in)
+      // a_tiles > 0: A is the hidden matrix in the fragment-blocked layout, a_tiles
+      // 16-row tiles per expert
+      const int64_t a_rows_e = (int64_t)a_tiles * 16;
       const __amdgpu_buffer_rsrc_t ares =
-          gather != nullptr ? make_rsrc(A, a_rows * K * 2)
-                            : make_rsrc(A + ((int64_t)e * C + m0) * K, (int64_t)rows * K * 2);
+          a_tiles > 0 ? make_rsrc(A + (int64_t)e * a_rows_e * K, a_rows_e * K * 2)
+          : gather != nullptr ? make_rsrc(A, a_rows * K * 2)
+                              : make_rsrc(A + ((int64_t)e * C + m0) * K, (int64_t)rows * K * 2);
       const int w_voff = ((kw * 32 + kg * 8) * Ncols + cb * COLS + c * J) * 2;
       const int w_row = Ncols * 2;
       const int w_step = KW * 32 * Ncols * 2;
@@ -231,10 +251,14 @@ __device__ __forceinline__ void ffn_stream(const uint16_t* __restrict__ A, const
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int rr = mt * 16 + c;
-        const int64_t src = gather != nullptr && rr < rows ? gather[(int64_t)e * C + m0 + rr] : rr;
-        a_voff[mt] = rr < rows ? (int)((src * K + kw * 32 + kg * 8) * 2) : kOutOfRange;
+        if (a_tiles > 0) {  // block (k-step kw, tile m0/16 + mt): row c, k-chunk kg at hblk_pos(c, kg)
+          a_voff[mt] = rr < rows ? (kw * a_tiles + (m0 >> 4) + mt) * 1024 + hblk_pos(c, kg) * 16 : kOutOfRange;
+        } else {
+          const int64_t src = gather != nullptr && rr < rows ? gather[(int64_t)e * C + m0 + rr] : rr;
+          a_voff[mt] = rr < rows ? (int)((src * K + kw * 32 + kg * 8) * 2) : kOutOfRange;
+        }
       }
-      const int a_step = KW * 32 * 2;
+      const int a_step = a_tiles > 0 ? KW * a_tiles * 1024 : KW * 32 * 2;
 
       // The k-loop has no data-dependent branches (the waitcnt pass would drain
       // every load at each join).  The step count is padded to a multiple of
@@ -289,6 +313,16 @@ __device__ __forceinline__ void ffn_stream(const uint16_t* __restrict__ A, const
       }
     }
 
+    // where this lane's J columns of item row rl go: row-major [N, C, Ncols], or
+    // (o_tiles > 0) the fragment-blocked layout that the next GEMM reads
+    auto out_at = [&](int rl) -> uint16_t* {
+      const int col0 = cb * COLS + c * J;
+      const int r = m0 + rl;
+      if (o_tiles > 0)
+        return out + (int64_t)e * o_tiles * 16 * Ncols + ((int64_t)(col0 >> 5) * o_tiles + (r >> 4)) * 512 +
+               hblk_pos(r & 15, (col0 & 31) >> 3) * 8 + (col0 & 7);
+      return out + ((int64_t)e * C + r) * Ncols + col0;
+    };
     if (KW == 1) {
       // this wave owns the item: lane holds rows 4*kg + i, columns J*c .. J*c + J-1
       if (mtc > 0) {
@@ -301,7 +335,7 @@ __device__ __forceinline__ void ffn_stream(const uint16_t* __restrict__ A, const
               float v[J];
 #pragma unroll
               for (int j = 0; j < J; ++j) v[j] = acc[mt][j][i];
-              store_row<J>(out + ((int64_t)e * C + m0 + rl) * Ncols + cb * COLS + c * J, v, relu);
+              store_row<J>(out_at(rl), v, relu);
             }
           }
         }
@@ -326,7 +360,7 @@ __device__ __forceinline__ void ffn_stream(const uint16_t* __restrict__ A, const
               v[j] = sum;
             }
             const int rl = mt * 16 + kg * 4 + i;
-            if (rl < rows) store_row<J>(out + ((int64_t)e * C + m0 + rl) * Ncols + cb * COLS + c * J, v, relu);
+            if (rl < rows) store_row<J>(out_at(rl), v, relu);
           }
         }
         __syncthreads();
@@ -348,17 +382,18 @@ template <int MT, int WAVES, int STAGES, int JMAX>
 __global__ __launch_bounds__(WAVES * 64, SWM_FFN_MINB) void ffn_gemm_bf16(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, uint16_t* __restrict__ out,
     const int32_t* __restrict__ kept_count, const int32_t* __restrict__ active, const int32_t* __restrict__ n_active,
-    int N, int C, int K, int Ncols, int relu, int mch, const int32_t* __restrict__ gather, int64_t a_rows) {
+    int N, int C, int K, int Ncols, int relu, int mch, const int32_t* __restrict__ gather, int64_t a_rows, int a_tiles,
+    int o_tiles) {
   __shared__ float red[WAVES * 4 * JMAX * 64];
   int n_act = n_active[0];
   if (n_act > N) n_act = N;
   if (JMAX == 8 && Ncols % 128 == 0 &&
       (int64_t)n_act * (Ncols / 128) * mch * WAVES * 5 >= (int64_t)gridDim.x * WAVES * 2)
     ffn_stream<MT, WAVES, STAGES, JMAX>(A, W, out, kept_count, active, n_act, N, C, K, Ncols, relu, mch, red, gather,
-                                        a_rows);
+                                        a_rows, a_tiles, o_tiles);
   else
     ffn_stream<MT, WAVES, STAGES, 4>(A, W, out, kept_count, active, n_act, N, C, K, Ncols, relu, mch, red, gather,
-                                     a_rows);
+                                     a_rows, a_tiles, o_tiles);
 }
 
 __global__ __launch_bounds__(256) void ffn_gemm_f32(const float* __restrict__ A, const float* __restrict__ W,
@@ -403,17 +438,29 @@ __global__ void dense_plan(int32_t* kept, int32_t* active, int32_t* n_active, in
 #endif
 constexpr bool kAllow128 = SWM_FFN_ALLOW128;
 
+#ifndef SWM_HBLK
+#define SWM_HBLK 1
+#endif
+
 FfnPlan ffn_plan(int N, int C, int d, int dff, int dtype) {
   FfnPlan pl{};
   size_t off = 0;
   const size_t esz = dtype == 1 ? 2 : 4;
-  pl.off_h = off;
-  off = align_up(off + (size_t)N * C * dff * esz);
+  int64_t h_rows = C;  // rows of the hidden matrix per expert
   if (dtype == 1) {
     pl.mt = C <= 16 ? 1 : C <= 32 ? 2 : C <= 48 ? 3 : 4;
     pl.mch = (C + pl.mt * 16 - 1) / (pl.mt * 16);
     pl.grid = 0;  // persistent grid: resident workgroups per CU x CUs, resolved at launch
+    // fragment-blocked hidden matrix for the streaming GEMMs: every 16-row tile
+    // of every expert is whole, and an expert's block stays under 2^31 bytes
+    const int64_t tiles = (int64_t)pl.mch * pl.mt;
+    if (SWM_HBLK && !tiled_ffn_applies(C, d, dff) && tiles * 16 * dff * 2 < ((int64_t)1 << 31)) {
+      pl.h_tiles = (int)tiles;
+      h_rows = tiles * 16;
+    }
   }
+  pl.off_h = off;
+  off = align_up(off + (size_t)N * h_rows * dff * esz);
   pl.bytes = off;
   return pl;
 }
@@ -447,13 +494,13 @@ static int persistent_grid(const void* kernel, int threads) {
 template <int MT, int J>
 static hipError_t launch_gemm(const void* A, const void* W, void* out, const int32_t* kept, const int32_t* active,
                               const int32_t* n_active, int N, int C, int K, int Ncols, int relu, int mch,
-                              hipStream_t st, const int32_t* gather, int64_t a_rows) {
+                              hipStream_t st, const int32_t* gather, int64_t a_rows, int a_tiles, int o_tiles) {
   constexpr int kWaves = SWM_FFN_WAVES;
   auto kern = ffn_gemm_bf16<MT, kWaves, SWM_FFN_STAGES, J>;
   const int grid = persistent_grid(reinterpret_cast<const void*>(kern), kWaves * 64);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kWaves * 64), 0, st, static_cast<const uint16_t*>(A),
                      static_cast<const uint16_t*>(W), static_cast<uint16_t*>(out), kept, active, n_active, N, C, K,
-                     Ncols, relu, mch, gather, a_rows);
+                     Ncols, relu, mch, gather, a_rows, a_tiles, o_tiles);
   return hipGetLastError();
 }
 
@@ -462,26 +509,29 @@ static hipError_t launch_gemm(const void* A, const void* W, void* out, const int
 template <int MT>
 static hipError_t launch_gemm_cols(const void* A, const void* W, void* out, const int32_t* kept,
                                    const int32_t* active, const int32_t* n_active, int N, int C, int K, int Ncols,
-                                   int relu, int mch, hipStream_t st, const int32_t* gather, int64_t a_rows) {
+                                   int relu, int mch, hipStream_t st, const int32_t* gather, int64_t a_rows,
+                                   int a_tiles, int o_tiles) {
   if constexpr (kAllow128 && MT <= 3) {
     if (Ncols % 128 == 0)
-      return launch_gemm<MT, 8>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, mch, st, gather, a_rows);
+      return launch_gemm<MT, 8>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, mch, st, gather, a_rows,
+                                a_tiles, o_tiles);
   }
-  return launch_gemm<MT, 4>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, mch, st, gather, a_rows);
+  return launch_gemm<MT, 4>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, mch, st, gather, a_rows, a_tiles,
+                            o_tiles);
 }
 
 static hipError_t gemm_bf16(const FfnPlan& pl, const void* A, const void* W, void* out, const int32_t* kept,
                             const int32_t* active, const int32_t* n_active, int N, int C, int K, int Ncols, int relu,
-                            hipStream_t st, const int32_t* gather = nullptr, int64_t a_rows = 0) {
+                            hipStream_t st, const int32_t* gather, int64_t a_rows, int a_tiles, int o_tiles) {
   switch (pl.mt) {
     case 1: return launch_gemm_cols<1>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, pl.mch, st, gather,
-                                                a_rows);
+                                       a_rows, a_tiles, o_tiles);
     case 2: return launch_gemm_cols<2>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, pl.mch, st, gather,
-                                                a_rows);
+                                       a_rows, a_tiles, o_tiles);
     case 3: return launch_gemm_cols<3>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, pl.mch, st, gather,
-                                                a_rows);
+                                       a_rows, a_tiles, o_tiles);
     default: return launch_gemm_cols<4>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, pl.mch, st, gather,
-                                                a_rows);
+                                        a_rows, a_tiles, o_tiles);
   }
 }
 
@@ -508,9 +558,13 @@ hipError_t launch_ffn(const FfnPlan& pl, const void* xin, const void* w1, const 
     if (e != hipSuccess) return e;
     return launch_tiled_dma(h, w2, xout, kept_count, active, n_active, N, C, dff, d, 0, st);
   }
-  hipError_t e = gemm_bf16(pl, xin, w1, h, kept_count, active, n_active, N, C, d, dff, 1, st, gather, a_rows);
+  // The hidden matrix stays in the library's workspace unless the caller keeps
+  // it (training); then it is row-major [N, C, d_ff] as documented.  In the
+  // workspace it takes the fragment-blocked layout (ffn_plan sizes it).
+  const int tiles = h_out == nullptr ? pl.h_tiles : 0;
+  hipError_t e = gemm_bf16(pl, xin, w1, h, kept_count, active, n_active, N, C, d, dff, 1, st, gather, a_rows, 0, tiles);
   if (e != hipSuccess) return e;
-  return gemm_bf16(pl, h, w2, xout, kept_count, active, n_active, N, C, dff, d, 0, st);
+  return gemm_bf16(pl, h, w2, xout, kept_count, active, n_active, N, C, dff, d, 0, st, nullptr, 0, tiles, 0);
 }
 
 }  // namespace swm

@@ -77,6 +77,7 @@ struct FfnPlan {
   int mt;    // 16-row tiles per work item (bf16 path)
   int mch;   // m-chunks per expert
   int grid;  // persistent workgroups
+  int h_tiles;  // > 0: the workspace hidden matrix is fragment-blocked, h_tiles 16-row tiles per expert
   size_t off_h, bytes;
 };
 FfnPlan ffn_plan(int N, int C, int d, int dff, int dtype);
