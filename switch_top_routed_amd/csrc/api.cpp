@@ -208,14 +208,12 @@ struct FwdLayout {
   RoutePlan route;
   AssignPlan assign;
   FfnPlan ffn, sffn;
-  size_t off_route, off_assign, off_rank, off_toff, off_tos, off_active, off_nact, off_xin, off_xout, off_ffn;
+  size_t off_route, off_assign, off_term, off_tos, off_active, off_nact, off_xin, off_xout, off_ffn;
   size_t off_dense, off_sffn, off_sout, off_ev, off_gv, off_slotv, off_probs_t, off_pick, off_list, bytes;
 };
 
-// The fused path needs token order, the token matrix addressable through
-// 32-bit buffer offsets (GEMM 1 gathers its rows), and few enough router tiles
-// for the single-workgroup prefix.
-constexpr int64_t kFusedMaxTiles = 16384;
+// The fused path needs token order and the token matrix addressable through
+// 32-bit buffer offsets (GEMM 1 gathers its rows).
 
 FwdLayout fwd_layout(const switch_moe_desc& d, int32_t C) {
   FwdLayout L{};
@@ -226,16 +224,14 @@ FwdLayout fwd_layout(const switch_moe_desc& d, int32_t C) {
   L.ec = d.routing == SWITCH_EXPERT_CHOICE;
   L.route = route_plan(d.T, d.d_model, d.N, d.dtype);
   L.fused = !L.ec && L.K == 1 && d.priority == SWITCH_TOKEN_ORDER &&
-            (int64_t)d.T * d.d_model * (int64_t)esz < ((int64_t)1 << 31) && L.route.nblk <= kFusedMaxTiles;
+            (int64_t)d.T * d.d_model * (int64_t)esz < ((int64_t)1 << 31);
   L.ffn = ffn_plan(d.N, C, d.d_model, d.d_ff, d.dtype);
   size_t off = 0;
   L.off_route = off;
   off = align_up(off + L.route.bytes);
   if (L.fused) {
-    L.off_rank = off;
-    off = align_up(off + (size_t)d.T * 4);
-    L.off_toff = off;
-    off = align_up(off + (size_t)L.route.nblk * d.N * 4);
+    L.off_term = off;
+    off = align_up(off + (size_t)d.N * 8);
   } else if (!L.ec) {
     const int64_t TV = (int64_t)L.K * d.T;  // assignments ("virtual tokens")
     L.assign = assign_plan(TV, d.N, C, d.priority);
@@ -589,18 +585,17 @@ static switch_status moe_forward(const switch_moe_desc* desc, const switch_moe_i
 
   hipError_t e = mark(0);
   if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
-  int32_t* rank = L.fused ? reinterpret_cast<int32_t*>(w + L.off_rank) : nullptr;
   e = launch_route(L.route, in->x, in->w_gate, in->bias, d.T, d.d_model, d.N, d.dtype, out->expert_id, out->gate,
-                   out->routed_count, out->f, out->P, out->l_aux, w + L.off_route, st, rank, rex);
+                   out->routed_count, out->f, out->P, out->l_aux, w + L.off_route, st, L.fused, rex);
   if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/route");
   if ((e = mark(1)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
   if (L.fused) {
-    // token order: one kernel turns the router's tiles into slots (and the
-    // statistics); GEMM 1 then reads each slot's token row straight from x
-    e = launch_route_assign_token(L.route, d.T, d.N, C, out->expert_id, rank,
-                                  reinterpret_cast<int32_t*>(w + L.off_toff), out->routed_count, out->f, out->P,
-                                  out->l_aux, out->slot, tos, out->kept_count, out->n_dropped, active, nact,
-                                  w + L.off_route, st);
+    // token order: one workgroup per expert takes its tokens into slots (and
+    // reduces the router statistics); GEMM 1 then reads each slot's token row
+    // straight from x
+    e = launch_assign_token(L.route, d.T, d.N, C, out->expert_id, reinterpret_cast<double*>(w + L.off_term),
+                            out->routed_count, out->f, out->P, out->l_aux, out->slot, tos, out->kept_count,
+                            out->n_dropped, active, nact, w + L.off_route, st);
     if (e == hipSuccess && L.M > 1)
       e = launch_expand(rex.ev_cm, rex.gv_cm, d.T, d.N, C, L.M, 0, out->slot, out->expert_id, out->gate, tos,
                         out->kept_count, active, nact, out->n_dropped, reinterpret_cast<int32_t*>(w + L.off_list), st);

@@ -190,7 +190,11 @@ __device__ __forceinline__ void ffn_stream(const uint16_t* __restrict__ A, const
   const int ksteps = K >> 5;
   const int64_t base = (int64_t)n_act * NCB * mch;
   if (base <= 0) return;
+#ifdef SWM_KW_FORCE2
+  const int KW = relu ? waves_per_item(base, (int64_t)gridDim.x * WAVES, WAVES, ksteps) : SWM_KW_FORCE2;
+#else
   const int KW = waves_per_item(base, (int64_t)gridDim.x * WAVES, WAVES, ksteps);
+#endif
   const int groups = WAVES / KW;
   const int g = w / KW, kw = w - g * KW;
   // Workgroups are dealt to the 8 XCDs round-robin (blockIdx % 8).  Each XCD

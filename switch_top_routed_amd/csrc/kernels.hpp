@@ -18,9 +18,8 @@ struct RoutePlan {
   size_t off_part_p, off_part_cnt, off_logits, bytes;
 };
 RoutePlan route_plan(int64_t T, int d, int N, int dtype);
-// local_rank == NULL: statistics (routed_count, f, P, l_aux) by a final reduction
-// kernel; else every token's rank inside its tile is written and the statistics
-// are left to launch_route_assign_token
+// stats_later == false: statistics (routed_count, f, P, l_aux) by a final
+// reduction kernel; true: they are left to launch_assign_token
 // Router options beyond top-1:
 //   probs != NULL: the softmax of every token is written too ([T, N] fp32);
 //   K > 1: top-K choices, expert_id / gate are [T, K] (t * K + j), routed_count
@@ -40,15 +39,15 @@ struct RouteExtra {
 };
 hipError_t launch_route(const RoutePlan& pl, const void* x, const void* wg, const float* bias, int64_t T, int d, int N,
                         int dtype, int32_t* expert_id, float* gate, int32_t* routed_count, float* f, float* P,
-                        float* l_aux, char* ws, hipStream_t st, int32_t* local_rank = nullptr,
+                        float* l_aux, char* ws, hipStream_t st, bool stats_later = false,
                         const RouteExtra& ex = RouteExtra{});
-// token-order slots from the router's tiles (after launch_route with local_rank);
-// off: int32 [nblk x N] scratch
-hipError_t launch_route_assign_token(const RoutePlan& pl, int64_t T, int N, int C, const int32_t* expert_id,
-                                     const int32_t* local_rank, int32_t* off, int32_t* routed_count, float* f,
-                                     float* P, float* l_aux, int32_t* slot, int32_t* token_of_slot,
-                                     int32_t* kept_count, int32_t* n_dropped, int32_t* active, int32_t* n_active,
-                                     char* ws, hipStream_t st);
+// token-order slots and the router statistics (after launch_route with
+// stats_later): one workgroup per expert, then one for the cross-expert
+// results; term: fp64 [N] scratch
+hipError_t launch_assign_token(const RoutePlan& pl, int64_t T, int N, int C, const int32_t* expert_id, double* term,
+                               int32_t* routed_count, float* f, float* P, float* l_aux, int32_t* slot,
+                               int32_t* token_of_slot, int32_t* kept_count, int32_t* n_dropped, int32_t* active,
+                               int32_t* n_active, char* ws, hipStream_t st);
 
 // ---------------- capacity / slots ----------------
 struct AssignPlan {

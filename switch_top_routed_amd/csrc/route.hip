@@ -43,14 +43,11 @@ __device__ __forceinline__ void rt_dma16(__amdgpu_buffer_rsrc_t r, unsigned char
 // logits for `rows` tokens live in LDS lg[m * ldl + n] (no bias yet)
 // lg must hold >= 8 * N floats; it is reused for the cross-wave partial sums.
 // J = experts per lane (N <= 64 * J).
-// local_rank (may be NULL): rank of each token among the tokens of this tile
-// routed to the same expert, in token order (rows <= 64).
 template <int J>
 __device__ void route_epilogue(float* lg, int ldl, int rows, int64_t t0, int64_t T, int N,
                                const float* __restrict__ bias, int32_t* __restrict__ expert_id,
                                float* __restrict__ gate, float* __restrict__ part_p, int32_t* __restrict__ part_cnt,
-                               int32_t* __restrict__ local_rank, int64_t blk, const RouteExtra& ex) {
-  __shared__ int tile_e[64];
+                               int64_t blk, const RouteExtra& ex) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   float bs[J], ps[J];
   int cn[J];
@@ -101,7 +98,6 @@ __device__ void route_epilogue(float* lg, int ldl, int rows, int64_t t0, int64_t
       if (lane == 0) {
         expert_id[t] = bi;
         gate[t] = inv;
-        tile_e[m] = bi;
         if (ex.ev_cm != nullptr) {
           ex.ev_cm[t] = bi;
           ex.gv_cm[t] = inv;
@@ -165,13 +161,7 @@ __device__ void route_epilogue(float* lg, int ldl, int rows, int64_t t0, int64_t
       }
     }
   }
-  __syncthreads();  // every wave is done reading the logits; tile_e is complete
-  if (local_rank != nullptr && threadIdx.x < rows && t0 + threadIdx.x < T) {
-    const int m = threadIdx.x, em = tile_e[m];
-    int r = 0;
-    for (int q = 0; q < m; ++q) r += (tile_e[q] == em) ? 1 : 0;
-    local_rank[t0 + m] = r;
-  }
+  __syncthreads();  // every wave is done reading the logits
   float* red_p = lg;
   int* red_c = reinterpret_cast<int*>(lg + 4 * N);
 #pragma unroll
@@ -203,7 +193,7 @@ template <int TM, int NG, int J, bool XL>
 __global__ __launch_bounds__(kRouteThreads) void route_fused_bf16(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg, const float* __restrict__ bias, int64_t T, int d,
     int N, int32_t* __restrict__ expert_id, float* __restrict__ gate, float* __restrict__ part_p,
-    int32_t* __restrict__ part_cnt, int32_t* __restrict__ local_rank, RouteExtra ex) {
+    int32_t* __restrict__ part_cnt, RouteExtra ex) {
   extern __shared__ float smem[];
   const int NT = (N + 15) >> 4;
   const int ldl = NT * 16;
@@ -298,7 +288,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_fused_bf16(
       }
   }
   __syncthreads();
-  route_epilogue<J>(lg, ldl, TM * 16, t0, T, N, bias, expert_id, gate, part_p, part_cnt, local_rank, blockIdx.x, ex);
+  route_epilogue<J>(lg, ldl, TM * 16, t0, T, N, bias, expert_id, gate, part_p, part_cnt, blockIdx.x, ex);
 }
 
 // ----------------------------------------------------------------------------
@@ -359,8 +349,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_softmax_split(const float
                                                                      int32_t* __restrict__ expert_id,
                                                                      float* __restrict__ gate,
                                                                      float* __restrict__ part_p,
-                                                                     int32_t* __restrict__ part_cnt,
-                                                                     int32_t* __restrict__ local_rank, RouteExtra ex) {
+                                                                     int32_t* __restrict__ part_cnt, RouteExtra ex) {
   // one token per workgroup: its N logits are sums over the S k-chunks, in
   // chunk order, with 8 independent loads in flight per expert
   extern __shared__ float smem[];
@@ -382,7 +371,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_softmax_split(const float
     lg[n] = v;
   }
   __syncthreads();
-  route_epilogue<J>(lg, N, 1, t, T, N, bias, expert_id, gate, part_p, part_cnt, local_rank, blockIdx.x, ex);
+  route_epilogue<J>(lg, N, 1, t, T, N, bias, expert_id, gate, part_p, part_cnt, blockIdx.x, ex);
 }
 
 // ----------------------------------------------------------------------------
@@ -393,8 +382,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_f32(const float* __restri
                                                            const float* __restrict__ bias, int64_t T, int d, int N,
                                                            int32_t* __restrict__ expert_id, float* __restrict__ gate,
                                                            float* __restrict__ part_p,
-                                                           int32_t* __restrict__ part_cnt,
-                                                           int32_t* __restrict__ local_rank, RouteExtra ex) {
+                                                           int32_t* __restrict__ part_cnt, RouteExtra ex) {
   extern __shared__ float smem[];
   const int ldl = N;
   float* lg = smem;
@@ -411,7 +399,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_f32(const float* __restri
     lg[m * ldl + n] = acc;
   }
   __syncthreads();
-  route_epilogue<J>(lg, ldl, 16, t0, T, N, bias, expert_id, gate, part_p, part_cnt, local_rank, blockIdx.x, ex);
+  route_epilogue<J>(lg, ldl, 16, t0, T, N, bias, expert_id, gate, part_p, part_cnt, blockIdx.x, ex);
 }
 
 // ----------------------------------------------------------------------------
@@ -498,90 +486,169 @@ __global__ __launch_bounds__(1024) void route_finalize(const float* __restrict__
   finalize_partials(part_p, part_cnt, nblk, T, N, NP, routed_count, f, P, l_aux, cnt, K);
 }
 
-// Token-order capacity and slots straight from the router's tiles (one
-// workgroup; "Top-1 Routing" page, Token Dropping).  A token's rank inside its
-// expert is the number of earlier tokens routed there: the count in earlier
-// tiles (an exclusive prefix over the tiles of the per-tile counts that the
-// router already keeps for f_i) plus its rank inside its own tile
-// (local_rank, written by the router).  Kept iff rank < C.  Also writes the
-// statistics of route_finalize, kept_count, n_dropped, the active list and
-// token_of_slot (-1 for empty slots).  off = workspace [nblk x N] int32.
-__global__ __launch_bounds__(1024) void route_assign_token(
-    const float* __restrict__ part_p, const int32_t* __restrict__ part_cnt, int64_t nblk, int tile_rows, int64_t T,
-    int N, int NP, int C, const int32_t* __restrict__ expert_id, const int32_t* __restrict__ local_rank,
-    int32_t* __restrict__ off, int32_t* __restrict__ routed_count, float* __restrict__ f, float* __restrict__ P,
-    float* __restrict__ l_aux, int32_t* __restrict__ slot, int32_t* __restrict__ token_of_slot,
-    int32_t* __restrict__ kept_count, int32_t* __restrict__ n_dropped, int32_t* __restrict__ active,
-    int32_t* __restrict__ n_active) {
-  __shared__ int gsum[1024];
-  __shared__ int wsum[16];
-  finalize_partials(part_p, part_cnt, nblk, T, N, NP, routed_count, f, P, l_aux, gsum);
-  const int tid = threadIdx.x;
+// Token-order capacity and slots, one workgroup per expert ("Top-1 Routing"
+// page, Token Dropping: an expert keeps its first C tokens in token order).
+// Workgroup e finds the tokens routed to e in ascending token order (ballots
+// per wave, one LDS scan per 16K tokens); the r-th of them takes slot r if
+// r < C and is dropped otherwise.  It also reduces expert e's router partials
+// into routed_count, f and P, in the same order as route_finalize (group g of
+// G = 1024 / NP owns a contiguous tile range summed in tile order, then the
+// groups in group order), so both give the same bits, and leaves f_e * P_e in
+// term[e] for assign_token_finalize.  Every token is routed to exactly one
+// expert, so each slot[t] and token_of_slot row has exactly one writer.
+namespace {
+constexpr int kAtSub = 16;  // 1024-token chunks per LDS scan
+}  // namespace
+
+__global__ __launch_bounds__(1024) void assign_token_expert(
+    const float* __restrict__ part_p, const int32_t* __restrict__ part_cnt, int64_t nblk, int64_t T, int N, int NP,
+    int C, const int32_t* __restrict__ expert_id, int32_t* __restrict__ routed_count, float* __restrict__ f,
+    float* __restrict__ P, double* __restrict__ term, int32_t* __restrict__ slot, int32_t* __restrict__ token_of_slot,
+    int32_t* __restrict__ kept_count) {
+  __shared__ int woff[kAtSub * 16];
+  __shared__ float cp[1024];
+  __shared__ int cc[1024];
+  __shared__ double sp[16];
+  __shared__ int sc[16];
+  __shared__ int s_total;
+  const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  // the first chunk's expert ids are loaded together with the first tiles
+  int ev0[kAtSub];
+#pragma unroll
+  for (int j = 0; j < kAtSub; ++j) {
+    const int64_t t = (int64_t)j * 1024 + tid;
+    ev0[j] = t < T ? expert_id[t] : -1;
+  }
+
+  // statistics of expert e: the tiles' partials pass through LDS 1024 at a
+  // time; group g = tid < G adds the part of its tile range in each chunk
   const int G = 1024 / NP;
-  const int n = tid % NP, g = tid / NP;
-  // exclusive prefix over tiles, per expert: earlier groups' sums (gsum, in
-  // LDS), then the running count along this thread's own tile range
   const int64_t per = (nblk + G - 1) / G;
-  const int64_t b0 = (int64_t)g * per, b1 = (b0 + per < nblk) ? b0 + per : nblk;
-  if (n < N && g < G) {
-    int run = 0;
-    for (int i = 0; i < g; ++i) run += gsum[i * NP + n];
-    for (int64_t b = b0; b < b1; b += 16) {
-      int cv[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) cv[u] = (b + u < b1) ? part_cnt[(b + u) * N + n] : 0;
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        if (b + u < b1) off[(b + u) * N + n] = run;
-        run += cv[u];
+  const int64_t b0 = (int64_t)tid * per, b1 = (b0 + per < nblk) ? b0 + per : nblk;
+  double accp = 0.0;
+  int accc = 0;
+  for (int64_t c0 = 0; c0 < nblk; c0 += 1024) {
+    const int64_t b = c0 + tid;
+    cp[tid] = b < nblk ? part_p[b * N + e] : 0.f;
+    cc[tid] = b < nblk ? part_cnt[b * N + e] : 0;
+    __syncthreads();
+    if (tid < G) {
+      const int64_t lo = b0 > c0 ? b0 : c0, hi = b1 < c0 + 1024 ? b1 : c0 + 1024;
+      for (int64_t q = lo; q < hi; ++q) {
+        accp += (double)cp[q - c0];
+        accc += cc[q - c0];
       }
     }
+    __syncthreads();
   }
-  int kept = 0;
-  if (tid < N) {
-    const int total = routed_count[tid];  // written by this thread in finalize_partials
-    kept = total < C ? total : C;
-    kept_count[tid] = kept;
+  if (tid < G) {
+    sp[tid] = accp;
+    sc[tid] = accc;
   }
-  int tot_active, tot_kept;
-  const int pos = block_exclusive_scan(kept > 0 ? 1 : 0, wsum, &tot_active);
-  block_exclusive_scan(kept, wsum, &tot_kept);
-  if (tid < N && kept > 0) active[pos] = tid;
-  if (tid == 0) {
-    n_active[0] = tot_active;
-    n_dropped[0] = (int32_t)(T - tot_kept);
-  }
-  for (int64_t i = tid; i < (int64_t)N * C; i += 1024) token_of_slot[i] = -1;
-  __syncthreads();  // off[] and the -1 fill (global memory, this workgroup) are complete
-  // 8 tokens per thread at a time: their loads, then the dependent offset loads, then the stores
-  const int rows = tile_rows;
-  for (int64_t t0 = tid; t0 < T; t0 += 8 * 1024) {
-    int e[8], lr[8], o[8];
+
+  // slots: the tokens of expert e in ascending token order
+  int n_seen = 0;
+  for (int64_t c0 = 0; c0 < T; c0 += (int64_t)kAtSub * 1024) {
+    bool fl[kAtSub];
+    uint64_t m[kAtSub];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int64_t t = t0 + (int64_t)u * 1024;
-      e[u] = t < T ? expert_id[t] : 0;
-      lr[u] = t < T ? local_rank[t] : 0;
+    for (int j = 0; j < kAtSub; ++j) {
+      const int64_t t = c0 + (int64_t)j * 1024 + tid;
+      fl[j] = c0 == 0 ? ev0[j] == e : (t < T && expert_id[t] == e);
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int64_t t = t0 + (int64_t)u * 1024;
-      const int tile = (int)((uint32_t)t / (uint32_t)rows);  // T < 2^31
-      o[u] = t < T ? off[(int64_t)tile * N + e[u]] : 0;
+    for (int j = 0; j < kAtSub; ++j) {
+      m[j] = __ballot(fl[j]);
+      if (lane == 0) woff[j * 16 + w] = __popcll(m[j]);
     }
+    __syncthreads();
+    if (w == 0) {  // exclusive scan of the 256 counts, chunk-major then wave
+      int v[4], sum = 0;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int64_t t = t0 + (int64_t)u * 1024;
-      if (t < T) {
-        const int r = o[u] + lr[u];
+      for (int q = 0; q < 4; ++q) {
+        v[q] = woff[lane * 4 + q];
+        sum += v[q];
+      }
+      int incl = sum;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += u;
+      }
+      int run = incl - sum;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        woff[lane * 4 + q] = run;
+        run += v[q];
+      }
+      if (lane == 63) s_total = incl;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kAtSub; ++j) {
+      if (fl[j]) {
+        const int64_t t = c0 + (int64_t)j * 1024 + tid;
+        const int r = n_seen + woff[j * 16 + w] + __popcll(m[j] & below);
         if (r < C) {
           slot[t] = r;
-          token_of_slot[(int64_t)e[u] * C + r] = (int32_t)t;
+          token_of_slot[(int64_t)e * C + r] = (int32_t)t;
         } else {
           slot[t] = -1;
         }
       }
     }
+    n_seen += s_total;
+    __syncthreads();  // woff and s_total are rewritten by the next chunk
+  }
+  const int kept = n_seen < C ? n_seen : C;
+  for (int r = kept + tid; r < C; r += 1024) token_of_slot[(int64_t)e * C + r] = -1;
+  if (tid == 0) {
+    double sum = 0.0;
+    long long cnum = 0;
+    for (int g = 0; g < G; ++g) {
+      sum += sp[g];
+      cnum += sc[g];
+    }
+    const double fn = (double)cnum / (1.0 * (double)T);
+    const double pn = sum / (double)T;
+    routed_count[e] = (int32_t)cnum;
+    f[e] = (float)fn;
+    P[e] = (float)pn;
+    term[e] = fn * pn;
+    kept_count[e] = kept;
+  }
+}
+
+// The cross-expert results of the token-order assignment (one workgroup of
+// 1024 threads, N <= 1024): the active list in expert order, n_active,
+// n_dropped = T - sum of kept counts, and L_aux = N * sum_i f_i P_i through the
+// same fixed tree as route_finalize (xor tree inside each wave, then the 16
+// wave sums in wave order).
+__global__ __launch_bounds__(1024) void assign_token_finalize(const int32_t* __restrict__ kept_count,
+                                                              const double* __restrict__ term, int N, int64_t T,
+                                                              float* __restrict__ l_aux, int32_t* __restrict__ active,
+                                                              int32_t* __restrict__ n_active,
+                                                              int32_t* __restrict__ n_dropped) {
+  __shared__ int wsum[16];
+  __shared__ double sl[16];
+  const int n = threadIdx.x;
+  const int kept = n < N ? kept_count[n] : 0;
+  double tm = n < N ? term[n] : 0.0;
+  int tot_active, tot_kept;
+  const int pos = block_exclusive_scan(kept > 0 ? 1 : 0, wsum, &tot_active);
+  block_exclusive_scan(kept, wsum, &tot_kept);
+  if (n < N && kept > 0) active[pos] = n;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) tm += __shfl_xor(tm, o, 64);
+  if ((n & 63) == 0) sl[n >> 6] = tm;
+  __syncthreads();
+  if (n == 0) {
+    double a = 0.0;
+    for (int i = 0; i < 16; ++i) a += sl[i];
+    l_aux[0] = (float)((double)N * a);
+    n_active[0] = tot_active;
+    n_dropped[0] = (int32_t)(T - tot_kept);
   }
 }
 
@@ -630,7 +697,7 @@ RoutePlan route_plan(int64_t T, int d, int N, int dtype) {
 template <int J>
 static hipError_t launch_route_j(const RoutePlan& pl, const void* x, const void* wg, const float* bias, int64_t T,
                                  int d, int N, int dtype, int32_t* expert_id, float* gate, float* part_p,
-                                 int32_t* part_cnt, int32_t* local_rank, char* ws, hipStream_t st,
+                                 int32_t* part_cnt, char* ws, hipStream_t st,
                                  const RouteExtra& ex) {
   if (dtype == 1 && pl.split == 0) {
     const int NT = (N + 15) / 16;
@@ -642,16 +709,16 @@ static hipError_t launch_route_j(const RoutePlan& pl, const void* x, const void*
     auto* wb = static_cast<const uint16_t*>(wg);
     if (pl.tm == 4)
       hipLaunchKernelGGL((route_fused_bf16<4, 2, J, false>), grid, dim3(kRouteThreads), lds, st, xb, wb, bias, T, d, N,
-                         expert_id, gate, part_p, part_cnt, local_rank, ex);
+                         expert_id, gate, part_p, part_cnt, ex);
     else if (pl.tm == 2)
       hipLaunchKernelGGL((route_fused_bf16<2, 2, J, false>), grid, dim3(kRouteThreads), lds, st, xb, wb, bias, T, d, N,
-                         expert_id, gate, part_p, part_cnt, local_rank, ex);
+                         expert_id, gate, part_p, part_cnt, ex);
     else if (xl)
       hipLaunchKernelGGL((route_fused_bf16<1, 2, J, true>), grid, dim3(kRouteThreads), lds + xl_bytes, st, xb, wb, bias,
-                         T, d, N, expert_id, gate, part_p, part_cnt, local_rank, ex);
+                         T, d, N, expert_id, gate, part_p, part_cnt, ex);
     else
       hipLaunchKernelGGL((route_fused_bf16<1, 2, J, false>), grid, dim3(kRouteThreads), lds, st, xb, wb, bias, T, d, N,
-                         expert_id, gate, part_p, part_cnt, local_rank, ex);
+                         expert_id, gate, part_p, part_cnt, ex);
   } else if (dtype == 1) {
     float* plog = reinterpret_cast<float*>(ws + pl.off_logits);
     hipLaunchKernelGGL((route_logits_split_bf16<2>), dim3((unsigned)((T + 15) / 16), (unsigned)pl.split), dim3(kRouteThreads),
@@ -661,47 +728,49 @@ static hipError_t launch_route_j(const RoutePlan& pl, const void* x, const void*
     if (e != hipSuccess) return e;
     const size_t lds = (size_t)8 * N * 4;  // the epilogue reuses it for the cross-wave partials
     hipLaunchKernelGGL(route_softmax_split<J>, dim3((unsigned)pl.nblk), dim3(kRouteThreads), lds, st, plog, pl.split,
-                       T, N, bias, expert_id, gate, part_p, part_cnt, local_rank, ex);
+                       T, N, bias, expert_id, gate, part_p, part_cnt, ex);
   } else {
     const size_t lds = (size_t)16 * N * 4;
     hipLaunchKernelGGL(route_f32<J>, dim3((unsigned)pl.nblk), dim3(kRouteThreads), lds, st,
                        static_cast<const float*>(x), static_cast<const float*>(wg), bias, T, d, N, expert_id, gate,
-                       part_p, part_cnt, local_rank, ex);
+                       part_p, part_cnt, ex);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_route(const RoutePlan& pl, const void* x, const void* wg, const float* bias, int64_t T, int d, int N,
                         int dtype, int32_t* expert_id, float* gate, int32_t* routed_count, float* f, float* P,
-                        float* l_aux, char* ws, hipStream_t st, int32_t* local_rank, const RouteExtra& ex) {
+                        float* l_aux, char* ws, hipStream_t st, bool stats_later, const RouteExtra& ex) {
   float* part_p = reinterpret_cast<float*>(ws + pl.off_part_p);
   int32_t* part_cnt = reinterpret_cast<int32_t*>(ws + pl.off_part_cnt);
   hipError_t e;
   if (N <= 128)
-    e = launch_route_j<2>(pl, x, wg, bias, T, d, N, dtype, expert_id, gate, part_p, part_cnt, local_rank, ws, st, ex);
+    e = launch_route_j<2>(pl, x, wg, bias, T, d, N, dtype, expert_id, gate, part_p, part_cnt, ws, st, ex);
   else if (N <= 512)
-    e = launch_route_j<8>(pl, x, wg, bias, T, d, N, dtype, expert_id, gate, part_p, part_cnt, local_rank, ws, st, ex);
+    e = launch_route_j<8>(pl, x, wg, bias, T, d, N, dtype, expert_id, gate, part_p, part_cnt, ws, st, ex);
   else
-    e = launch_route_j<16>(pl, x, wg, bias, T, d, N, dtype, expert_id, gate, part_p, part_cnt, local_rank, ws, st, ex);
+    e = launch_route_j<16>(pl, x, wg, bias, T, d, N, dtype, expert_id, gate, part_p, part_cnt, ws, st, ex);
   if (e != hipSuccess) return e;
-  if (local_rank != nullptr) return hipSuccess;  // the statistics come from launch_route_assign_token
+  if (stats_later) return hipSuccess;  // the statistics come from launch_assign_token
   const int NP = (N + 63) / 64 * 64;
   hipLaunchKernelGGL(route_finalize, dim3(1), dim3(1024), 0, st, part_p, part_cnt, pl.nblk, T, N, NP, routed_count, f,
                      P, l_aux, (ex.K < 1 || ex.expand) ? 1 : ex.K);
   return hipGetLastError();
 }
 
-hipError_t launch_route_assign_token(const RoutePlan& pl, int64_t T, int N, int C, const int32_t* expert_id,
-                                     const int32_t* local_rank, int32_t* off, int32_t* routed_count, float* f,
-                                     float* P, float* l_aux, int32_t* slot, int32_t* token_of_slot,
-                                     int32_t* kept_count, int32_t* n_dropped, int32_t* active, int32_t* n_active,
-                                     char* ws, hipStream_t st) {
+hipError_t launch_assign_token(const RoutePlan& pl, int64_t T, int N, int C, const int32_t* expert_id, double* term,
+                               int32_t* routed_count, float* f, float* P, float* l_aux, int32_t* slot,
+                               int32_t* token_of_slot, int32_t* kept_count, int32_t* n_dropped, int32_t* active,
+                               int32_t* n_active, char* ws, hipStream_t st) {
   const float* part_p = reinterpret_cast<const float*>(ws + pl.off_part_p);
   const int32_t* part_cnt = reinterpret_cast<const int32_t*>(ws + pl.off_part_cnt);
   const int NP = (N + 63) / 64 * 64;
-  hipLaunchKernelGGL(route_assign_token, dim3(1), dim3(1024), 0, st, part_p, part_cnt, pl.nblk, pl.tile_rows, T, N,
-                     NP, C, expert_id, local_rank, off, routed_count, f, P, l_aux, slot, token_of_slot, kept_count,
-                     n_dropped, active, n_active);
+  hipLaunchKernelGGL(assign_token_expert, dim3((unsigned)N), dim3(1024), 0, st, part_p, part_cnt, pl.nblk, T, N, NP, C,
+                     expert_id, routed_count, f, P, term, slot, token_of_slot, kept_count);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(assign_token_finalize, dim3(1), dim3(1024), 0, st, kept_count, term, N, T, l_aux, active, n_active,
+                     n_dropped);
   return hipGetLastError();
 }
 
