@@ -54,13 +54,13 @@ FFN_SOURCES = ("switch_top_routed_amd/csrc/expert_ffn.hip", "switch_top_routed_a
 # profiles/*_hbm_traffic.md.
 TRAFFIC = {
     "switch-base-uniform": {
-        "sources_sha256": "9d26310dc016c0c7ceee167b366de382d58e9e37a34116409be632d28f9bd80f",
-        "fetch_kib": [306102.0, 315096.0], "write_kib": [25132.0, 7051.0],
+        "sources_sha256": "aeca613147d2856d5e20637249b4e46a5691ef64dfdd48a210bc801be002f789",
+        "fetch_kib": [305777.0, 315641.0], "write_kib": [24108.0, 6027.0],
         "fetch_scale": 2.0, "write_scale": 1.0,
     },
     "switch-large-shared": {
-        "sources_sha256": "9d26310dc016c0c7ceee167b366de382d58e9e37a34116409be632d28f9bd80f",
-        "fetch_kib": [5328314.0, 5490728.0], "write_kib": [262286.0, 163840.0],
+        "sources_sha256": "aeca613147d2856d5e20637249b4e46a5691ef64dfdd48a210bc801be002f789",
+        "fetch_kib": [5328343.0, 5498233.0], "write_kib": [262255.0, 163840.0],
         "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
@@ -72,12 +72,12 @@ BWD_SOURCES = ("switch_top_routed_amd/csrc/backward_fused.hip", "switch_top_rout
 BWD_TRAFFIC = {
     "switch-base-uniform": {
         "sources_sha256": "409d356bb35470314da9ef7f5376d0dd79ac1a74923680b28b0e5940205c76b4",
-        "fetch_kib": [322765.0, 313012.0], "write_kib": [614893.0, 601879.0],
+        "fetch_kib": [322771.0, 313072.0], "write_kib": [614904.0, 601879.0],
         "fetch_scale": 2.0, "write_scale": 1.0,
     },
     "switch-large-shared": {
         "sources_sha256": "409d356bb35470314da9ef7f5376d0dd79ac1a74923680b28b0e5940205c76b4",
-        "fetch_kib": [5867781.0, 5806157.0], "write_kib": [10759620.0, 10813443.0],
+        "fetch_kib": [5889120.0, 5793901.0], "write_kib": [10760959.0, 10813443.0],
         "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }

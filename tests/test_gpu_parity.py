@@ -230,7 +230,7 @@ def test_base_layer_matches_staged_path(base):
         np.testing.assert_array_equal(host_bits(o[k]), host_bits(st[k]), err_msg=k)
 
 
-@pytest.mark.parametrize("name", ["ragged", "f32-odd", "n1000", "tiled-c150"])
+@pytest.mark.parametrize("name", ["ragged", "f32-odd", "n1000", "tiled-c150", "f32-many-tiles"])
 def test_edge_layer_matches_staged_path(name):
     wl = next(w for w in EDGE if w.name == name)
     _say(f"edge layer vs staged path {name}")
@@ -308,6 +308,9 @@ EDGE = [
     _custom("tiled-c150", 1200, 256, 512, 8, 1.0, seed=13, bias_scale=0.5),     # C = 150: 160 x 256 tiles
     _custom("tiled-c180", 1440, 512, 256, 8, 1.0, seed=14, priority="gate"),    # C = 180: two 128-row m-chunks
     _custom("tiled-c200", 1600, 512, 256, 8, 1.0, seed=12, priority="gate"),    # C = 200: two 128-row m-chunks
+    # token-order assignment: 1250 router tiles (two LDS chunks of partials), one tile
+    # group per expert (N = 1024), tokens in two 16K chunks
+    _custom("f32-many-tiles", 20000, 32, 64, 1024, 1.0, dtype="f32", seed=16),
 ]
 
 
