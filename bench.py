@@ -229,8 +229,8 @@ def main():
     n_active = int((out["kept_count"] > 0).sum().item())
     T, d, F, N, C = wl.T, wl.d_model, wl.d_ff, wl.N, layer.C
     dropped = T - kept
-    # the library's top-1 token-order forward folds the dispatch into GEMM 1 (same rule as its workspace layout)
-    gathered = not variant and wl.priority == "token" and T * d * esz < 2 ** 31
+    # the library's forward folds the dispatch into GEMM 1 when x fits 32-bit offsets (same rule as its workspace layout)
+    gathered = T * d * esz < 2 ** 31
     route_bytes = T * d * esz + N * d * esz + T * 8 + N * 16
     disp_bytes = 2 * kept * d * esz + 4 * kept
     # combine: one row read per token (expert output if kept, x if dropped), one row written,
@@ -250,7 +250,7 @@ def main():
                   "hbm_frac": gbs(route_bytes, st_s["route"]) / HBM_PEAK_GBS},
         "assign": {"us": st_s["assign"] * 1e6},
         "dispatch": ({"us": st_s["dispatch"] * 1e6, "folded_into_gemm1": True,
-                      "note": "token order: GEMM 1 gathers the x rows; the span is the event pair alone"}
+                      "note": "GEMM 1 gathers the x rows; the span is the event pair alone"}
                      if gathered else
                      {"us": st_s["dispatch"] * 1e6, "GB_s": gbs(disp_bytes, st_s["dispatch"]),
                       "hbm_frac": gbs(disp_bytes, st_s["dispatch"]) / HBM_PEAK_GBS}),

@@ -204,7 +204,8 @@ struct FwdLayout {
   int K;       // token choice: experts per token
   int M;       // Expanded Drop candidates (1: off)
   bool ec;     // expert choice
-  bool fused;  // top-1 token order: slots from the router's tiles, dispatch folded into GEMM 1
+  bool fused;   // top-1 token order: slots from one workgroup per expert right after the router
+  bool gather;  // the dispatch folded into GEMM 1 (it reads each slot's token row from x)
   RoutePlan route;
   AssignPlan assign;
   FfnPlan ffn, sffn;
@@ -212,8 +213,9 @@ struct FwdLayout {
   size_t off_dense, off_sffn, off_sout, off_ev, off_gv, off_slotv, off_probs_t, off_pick, off_list, bytes;
 };
 
-// The fused path needs token order and the token matrix addressable through
-// 32-bit buffer offsets (GEMM 1 gathers its rows).
+// GEMM 1 gathers its rows from x through token_of_slot whenever the token
+// matrix is addressable through 32-bit buffer offsets; the fused assignment
+// also needs top-1 token order.
 
 FwdLayout fwd_layout(const switch_moe_desc& d, int32_t C) {
   FwdLayout L{};
@@ -223,8 +225,8 @@ FwdLayout fwd_layout(const switch_moe_desc& d, int32_t C) {
   L.M = d.expand_choices < 1 ? 1 : d.expand_choices;
   L.ec = d.routing == SWITCH_EXPERT_CHOICE;
   L.route = route_plan(d.T, d.d_model, d.N, d.dtype);
-  L.fused = !L.ec && L.K == 1 && d.priority == SWITCH_TOKEN_ORDER &&
-            (int64_t)d.T * d.d_model * (int64_t)esz < ((int64_t)1 << 31);
+  L.gather = (int64_t)d.T * d.d_model * (int64_t)esz < ((int64_t)1 << 31);
+  L.fused = !L.ec && L.K == 1 && d.priority == SWITCH_TOKEN_ORDER && L.gather;
   L.ffn = ffn_plan(d.N, C, d.d_model, d.d_ff, d.dtype);
   size_t off = 0;
   L.off_route = off;
@@ -266,7 +268,7 @@ FwdLayout fwd_layout(const switch_moe_desc& d, int32_t C) {
   L.off_nact = off;
   off = align_up(off + 4);
   L.off_xin = off;
-  if (!L.fused) off = align_up(off + (size_t)d.N * C * d.d_model * esz);
+  if (!L.gather) off = align_up(off + (size_t)d.N * C * d.d_model * esz);
   L.off_xout = off;
   off = align_up(off + (size_t)d.N * C * d.d_model * esz);
   L.off_ffn = off;
@@ -624,11 +626,13 @@ static switch_status moe_forward(const switch_moe_desc* desc, const switch_moe_i
     }
     if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/assign");
     if ((e = mark(2)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
-    e = launch_dispatch(in->x, d.dtype, d.T, d.d_model, tos, out->kept_count, d.N, C, xin, st);
-    if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/dispatch");
+    if (!L.gather) {
+      e = launch_dispatch(in->x, d.dtype, d.T, d.d_model, tos, out->kept_count, d.N, C, xin, st);
+      if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/dispatch");
+    }
     if ((e = mark(3)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
-    e = launch_ffn(L.ffn, xin, in->w1, in->w2, d.dtype, d.N, C, d.d_model, d.d_ff, out->kept_count, active, nact,
-                   xout, w + L.off_ffn, st, nullptr, 0, h_save, mxp);
+    e = launch_ffn(L.ffn, L.gather ? in->x : xin, in->w1, in->w2, d.dtype, d.N, C, d.d_model, d.d_ff, out->kept_count,
+                   active, nact, xout, w + L.off_ffn, st, L.gather ? tos : nullptr, L.gather ? d.T : 0, h_save, mxp);
   }
   if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/expert_ffn");
   if ((e = mark(4)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
