@@ -204,7 +204,7 @@ struct FwdLayout {
   int K;       // token choice: experts per token
   int M;       // Expanded Drop candidates (1: off)
   bool ec;     // expert choice
-  bool fused;   // top-1 token order: slots from one workgroup per expert right after the router
+  bool fused;   // token order (top-1 or top-K): slots from one workgroup per expert right after the router
   bool gather;  // the dispatch folded into GEMM 1 (it reads each slot's token row from x)
   RoutePlan route;
   AssignPlan assign;
@@ -215,7 +215,7 @@ struct FwdLayout {
 
 // GEMM 1 gathers its rows from x through token_of_slot whenever the token
 // matrix is addressable through 32-bit buffer offsets; the fused assignment
-// also needs top-1 token order.
+// also needs token order (top-1 or top-K token choice).
 
 FwdLayout fwd_layout(const switch_moe_desc& d, int32_t C) {
   FwdLayout L{};
@@ -226,7 +226,7 @@ FwdLayout fwd_layout(const switch_moe_desc& d, int32_t C) {
   L.ec = d.routing == SWITCH_EXPERT_CHOICE;
   L.route = route_plan(d.T, d.d_model, d.N, d.dtype);
   L.gather = (int64_t)d.T * d.d_model * (int64_t)esz < ((int64_t)1 << 31);
-  L.fused = !L.ec && L.K == 1 && d.priority == SWITCH_TOKEN_ORDER && L.gather;
+  L.fused = !L.ec && d.priority == SWITCH_TOKEN_ORDER && L.gather;
   L.ffn = ffn_plan(d.N, C, d.d_model, d.d_ff, d.dtype);
   size_t off = 0;
   L.off_route = off;
@@ -234,6 +234,12 @@ FwdLayout fwd_layout(const switch_moe_desc& d, int32_t C) {
   if (L.fused) {
     L.off_term = off;
     off = align_up(off + (size_t)d.N * 8);
+    if (L.K > 1) {  // the router's choice-major lists [K, T]
+      L.off_ev = off;
+      off = align_up(off + (size_t)L.K * d.T * 4);
+      L.off_gv = off;
+      off = align_up(off + (size_t)L.K * d.T * 4);
+    }
   } else if (!L.ec) {
     const int64_t TV = (int64_t)L.K * d.T;  // assignments ("virtual tokens")
     L.assign = assign_plan(TV, d.N, C, d.priority);
@@ -595,7 +601,8 @@ static switch_status moe_forward(const switch_moe_desc* desc, const switch_moe_i
     // token order: one workgroup per expert takes its tokens into slots (and
     // reduces the router statistics); GEMM 1 then reads each slot's token row
     // straight from x
-    e = launch_assign_token(L.route, d.T, d.N, C, out->expert_id, reinterpret_cast<double*>(w + L.off_term),
+    e = launch_assign_token(L.route, d.T, L.K, d.N, C, L.K > 1 ? rex.ev_cm : out->expert_id,
+                            reinterpret_cast<double*>(w + L.off_term),
                             out->routed_count, out->f, out->P, out->l_aux, out->slot, tos, out->kept_count,
                             out->n_dropped, active, nact, w + L.off_route, st);
     if (e == hipSuccess && L.M > 1)

@@ -44,7 +44,8 @@ hipError_t launch_route(const RoutePlan& pl, const void* x, const void* wg, cons
 // token-order slots and the router statistics (after launch_route with
 // stats_later): one workgroup per expert, then one for the cross-expert
 // results; term: fp64 [N] scratch
-hipError_t launch_assign_token(const RoutePlan& pl, int64_t T, int N, int C, const int32_t* expert_id, double* term,
+// (K > 1: expert_id is the choice-major [K, T] list, slot is [T, K])
+hipError_t launch_assign_token(const RoutePlan& pl, int64_t T, int K, int N, int C, const int32_t* expert_id, double* term,
                                int32_t* routed_count, float* f, float* P, float* l_aux, int32_t* slot,
                                int32_t* token_of_slot, int32_t* kept_count, int32_t* n_dropped, int32_t* active,
                                int32_t* n_active, char* ws, hipStream_t st);

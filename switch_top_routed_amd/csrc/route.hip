@@ -490,7 +490,10 @@ __global__ __launch_bounds__(1024) void route_finalize(const float* __restrict__
 // page, Token Dropping: an expert keeps its first C tokens in token order).
 // Workgroup e finds the tokens routed to e in ascending token order (ballots
 // per wave, one LDS scan per 16K tokens); the r-th of them takes slot r if
-// r < C and is dropped otherwise.  It also reduces expert e's router partials
+// r < C and is dropped otherwise.  Top-K (K > 1): the list is the K T choices
+// in choice-major order v = j T + t (every first choice before every second
+// one), expert_id is that [K, T] list, and choice v's slot goes to
+// slot[t K + j] and its token_of_slot entry is t.  It also reduces expert e's router partials
 // into routed_count, f and P, in the same order as route_finalize (group g of
 // G = 1024 / NP owns a contiguous tile range summed in tile order, then the
 // groups in group order), so both give the same bits, and leaves f_e * P_e in
@@ -501,8 +504,8 @@ constexpr int kAtSub = 16;  // 1024-token chunks per LDS scan
 }  // namespace
 
 __global__ __launch_bounds__(1024) void assign_token_expert(
-    const float* __restrict__ part_p, const int32_t* __restrict__ part_cnt, int64_t nblk, int64_t T, int N, int NP,
-    int C, const int32_t* __restrict__ expert_id, int32_t* __restrict__ routed_count, float* __restrict__ f,
+    const float* __restrict__ part_p, const int32_t* __restrict__ part_cnt, int64_t nblk, int64_t T, int K, int N,
+    int NP, int C, const int32_t* __restrict__ expert_id, int32_t* __restrict__ routed_count, float* __restrict__ f,
     float* __restrict__ P, double* __restrict__ term, int32_t* __restrict__ slot, int32_t* __restrict__ token_of_slot,
     int32_t* __restrict__ kept_count) {
   __shared__ int woff[kAtSub * 16];
@@ -513,12 +516,13 @@ __global__ __launch_bounds__(1024) void assign_token_expert(
   __shared__ int s_total;
   const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int64_t TV = T * K;  // choices in the list
   // the first chunk's expert ids are loaded together with the first tiles
   int ev0[kAtSub];
 #pragma unroll
   for (int j = 0; j < kAtSub; ++j) {
-    const int64_t t = (int64_t)j * 1024 + tid;
-    ev0[j] = t < T ? expert_id[t] : -1;
+    const int64_t v = (int64_t)j * 1024 + tid;
+    ev0[j] = v < TV ? expert_id[v] : -1;
   }
 
   // statistics of expert e: the tiles' partials pass through LDS 1024 at a
@@ -549,13 +553,13 @@ __global__ __launch_bounds__(1024) void assign_token_expert(
 
   // slots: the tokens of expert e in ascending token order
   int n_seen = 0;
-  for (int64_t c0 = 0; c0 < T; c0 += (int64_t)kAtSub * 1024) {
+  for (int64_t c0 = 0; c0 < TV; c0 += (int64_t)kAtSub * 1024) {
     bool fl[kAtSub];
     uint64_t m[kAtSub];
 #pragma unroll
     for (int j = 0; j < kAtSub; ++j) {
-      const int64_t t = c0 + (int64_t)j * 1024 + tid;
-      fl[j] = c0 == 0 ? ev0[j] == e : (t < T && expert_id[t] == e);
+      const int64_t v = c0 + (int64_t)j * 1024 + tid;
+      fl[j] = c0 == 0 ? ev0[j] == e : (v < TV && expert_id[v] == e);
     }
 #pragma unroll
     for (int j = 0; j < kAtSub; ++j) {
@@ -588,13 +592,14 @@ __global__ __launch_bounds__(1024) void assign_token_expert(
 #pragma unroll
     for (int j = 0; j < kAtSub; ++j) {
       if (fl[j]) {
-        const int64_t t = c0 + (int64_t)j * 1024 + tid;
+        const int64_t v = c0 + (int64_t)j * 1024 + tid;
+        const int64_t t = K == 1 ? v : v % T, ch = K == 1 ? 0 : v / T;
         const int r = n_seen + woff[j * 16 + w] + __popcll(m[j] & below);
         if (r < C) {
-          slot[t] = r;
+          slot[t * K + ch] = r;
           token_of_slot[(int64_t)e * C + r] = (int32_t)t;
         } else {
-          slot[t] = -1;
+          slot[t * K + ch] = -1;
         }
       }
     }
@@ -610,7 +615,7 @@ __global__ __launch_bounds__(1024) void assign_token_expert(
       sum += sp[g];
       cnum += sc[g];
     }
-    const double fn = (double)cnum / (1.0 * (double)T);
+    const double fn = (double)cnum / ((double)K * (double)T);  // K choices per token
     const double pn = sum / (double)T;
     routed_count[e] = (int32_t)cnum;
     f[e] = (float)fn;
@@ -758,19 +763,19 @@ hipError_t launch_route(const RoutePlan& pl, const void* x, const void* wg, cons
   return hipGetLastError();
 }
 
-hipError_t launch_assign_token(const RoutePlan& pl, int64_t T, int N, int C, const int32_t* expert_id, double* term,
+hipError_t launch_assign_token(const RoutePlan& pl, int64_t T, int K, int N, int C, const int32_t* expert_id, double* term,
                                int32_t* routed_count, float* f, float* P, float* l_aux, int32_t* slot,
                                int32_t* token_of_slot, int32_t* kept_count, int32_t* n_dropped, int32_t* active,
                                int32_t* n_active, char* ws, hipStream_t st) {
   const float* part_p = reinterpret_cast<const float*>(ws + pl.off_part_p);
   const int32_t* part_cnt = reinterpret_cast<const int32_t*>(ws + pl.off_part_cnt);
   const int NP = (N + 63) / 64 * 64;
-  hipLaunchKernelGGL(assign_token_expert, dim3((unsigned)N), dim3(1024), 0, st, part_p, part_cnt, pl.nblk, T, N, NP, C,
-                     expert_id, routed_count, f, P, term, slot, token_of_slot, kept_count);
+  hipLaunchKernelGGL(assign_token_expert, dim3((unsigned)N), dim3(1024), 0, st, part_p, part_cnt, pl.nblk, T, K, N, NP,
+                     C, expert_id, routed_count, f, P, term, slot, token_of_slot, kept_count);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(assign_token_finalize, dim3(1), dim3(1024), 0, st, kept_count, term, N, T, l_aux, active, n_active,
-                     n_dropped);
+  hipLaunchKernelGGL(assign_token_finalize, dim3(1), dim3(1024), 0, st, kept_count, term, N, T * K, l_aux, active,
+                     n_active, n_dropped);
   return hipGetLastError();
 }
 
