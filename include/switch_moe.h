@@ -206,11 +206,12 @@ switch_status switch_quantize_mxfp4(const void* w, int32_t dtype, int64_t batche
 /* ------------------------------------------------------------------------
  * The whole layer: route -> capacity/slots -> dispatch -> expert FFN ->
  * (shared FFN) -> combine, enqueued on one stream.  Results equal those of
- * the per-stage entry points above, bit for bit.  With token-order priority
- * (and T * d_model * sizeof(dtype) < 2^31) the slots come from the router's
- * tiles in one kernel and the first expert GEMM reads each slot's token row
- * from x, so no dispatched copy is made; gate-descending priority runs the
- * separate assignment and dispatch kernels.
+ * the per-stage entry points above, bit for bit.  When
+ * T * d_model * sizeof(dtype) < 2^31 the first expert GEMM reads each slot's
+ * token row from x through token_of_slot, so no dispatched copy is made (every
+ * routing); with token-order priority the slots also come from one workgroup
+ * per expert right after the router, while gate-descending priority runs the
+ * assignment kernels of switch_assign_capacity.
  * ---------------------------------------------------------------------- */
 typedef struct switch_moe_desc {
   int64_t T;
@@ -314,8 +315,8 @@ switch_status switch_moe_forward(const switch_moe_desc* desc, const switch_moe_i
      [2] before the dispatch, [3] before the routed expert FFN (two GEMM
      launches), [4] after it (before the shared dense expert, if any),
      [5] before the combine, [6] after the combine.
-   With token-order priority the first expert GEMM reads each slot's token
-   row straight from x (no dispatch copy), so [2] and [3] mark one point.
+   When the first expert GEMM reads each slot's token row straight from x (no
+   dispatch copy; see above), [2] and [3] mark one point.
    Outputs, workspace, validation and errors are those of switch_moe_forward;
    a failed event record returns SWITCH_E_HIP. */
 switch_status switch_moe_forward_timed(const switch_moe_desc* desc, const switch_moe_inputs* in,
