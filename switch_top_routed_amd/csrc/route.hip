@@ -503,9 +503,9 @@ namespace {
 constexpr int kAtSub = 16;  // NT-token chunks per LDS scan
 }  // namespace
 
-template <int NT>
+template <int NT, bool MULTI>
 __global__ __launch_bounds__(NT) void assign_token_expert(
-    const float* __restrict__ part_p, const int32_t* __restrict__ part_cnt, int64_t nblk, int64_t T, int K, int N,
+    const float* __restrict__ part_p, const int32_t* __restrict__ part_cnt, int64_t nblk, int64_t T, int K_, int N,
     int NP, int C, const int32_t* __restrict__ expert_id, int32_t* __restrict__ routed_count, float* __restrict__ f,
     float* __restrict__ P, double* __restrict__ term, int32_t* __restrict__ slot, int32_t* __restrict__ token_of_slot,
     int32_t* __restrict__ kept_count) {
@@ -517,6 +517,7 @@ __global__ __launch_bounds__(NT) void assign_token_expert(
   __shared__ int s_total;
   const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int K = MULTI ? K_ : 1;  // choices per token (top-K); 1 compiles the top-1 path
   const int64_t TV = T * K;  // choices in the list
   // the first chunk's expert ids are loaded together with the first tiles
   int ev0[kAtSub];
@@ -595,7 +596,14 @@ __global__ __launch_bounds__(NT) void assign_token_expert(
     for (int j = 0; j < kAtSub; ++j) {
       if (fl[j]) {
         const int64_t v = c0 + (int64_t)j * NT + tid;
-        const int64_t t = K == 1 ? v : v % T, ch = K == 1 ? 0 : v / T;
+        // choice-major position -> (token, choice); K T < 2^31 on this path (x
+        // itself is under 2^31 bytes), so 32-bit division suffices
+        int64_t t = v;
+        int ch = 0;
+        if (MULTI) {
+          ch = (int)((uint32_t)v / (uint32_t)T);
+          t = v - (int64_t)ch * T;
+        }
         const int r = n_seen + woff[j * (NT / 64) + w] + __popcll(m[j] & below);
         if (r < C) {
           slot[t * K + ch] = r;
@@ -775,12 +783,17 @@ hipError_t launch_assign_token(const RoutePlan& pl, int64_t T, int K, int N, int
   // 256-thread workgroups for short lists (measured on the 384-expert decode
   // batch, T = 128: 15.7 against 22.7 us for the assignment stage); 1024 threads
   // otherwise (top-2 on the base layer, 8192 choices: 17.2 against 25.8 us)
-  if (T * K <= 2048)
-    hipLaunchKernelGGL(assign_token_expert<256>, dim3((unsigned)N), dim3(256), 0, st, part_p, part_cnt, pl.nblk, T, K, N,
-                       NP, C, expert_id, routed_count, f, P, term, slot, token_of_slot, kept_count);
-  else
-    hipLaunchKernelGGL(assign_token_expert<1024>, dim3((unsigned)N), dim3(1024), 0, st, part_p, part_cnt, pl.nblk, T, K,
-                       N, NP, C, expert_id, routed_count, f, P, term, slot, token_of_slot, kept_count);
+#define SWM_ASSIGN_TOKEN(NTH, MULTI)                                                                              \
+  hipLaunchKernelGGL((assign_token_expert<NTH, MULTI>), dim3((unsigned)N), dim3(NTH), 0, st, part_p, part_cnt, pl.nblk, \
+                     T, K, N, NP, C, expert_id, routed_count, f, P, term, slot, token_of_slot, kept_count)
+  if (T * K <= 2048) {
+    if (K > 1) SWM_ASSIGN_TOKEN(256, true);
+    else SWM_ASSIGN_TOKEN(256, false);
+  } else {
+    if (K > 1) SWM_ASSIGN_TOKEN(1024, true);
+    else SWM_ASSIGN_TOKEN(1024, false);
+  }
+#undef SWM_ASSIGN_TOKEN
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(assign_token_finalize, dim3(1), dim3(1024), 0, st, kept_count, term, N, T * K, l_aux, active,
