@@ -55,12 +55,12 @@ FFN_SOURCES = ("switch_top_routed_amd/csrc/expert_ffn.hip", "switch_top_routed_a
 TRAFFIC = {
     "switch-base-uniform": {
         "sources_sha256": "aeca613147d2856d5e20637249b4e46a5691ef64dfdd48a210bc801be002f789",
-        "fetch_kib": [305786.0, 315497.0], "write_kib": [24108.0, 6027.0],
+        "fetch_kib": [305788.0, 315606.0], "write_kib": [24108.0, 6027.0],
         "fetch_scale": 2.0, "write_scale": 1.0,
     },
     "switch-large-shared": {
         "sources_sha256": "aeca613147d2856d5e20637249b4e46a5691ef64dfdd48a210bc801be002f789",
-        "fetch_kib": [5328777.0, 5501460.0], "write_kib": [262215.0, 163840.0],
+        "fetch_kib": [5328288.0, 5495674.0], "write_kib": [262218.0, 163840.0],
         "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
@@ -72,12 +72,12 @@ BWD_SOURCES = ("switch_top_routed_amd/csrc/backward_fused.hip", "switch_top_rout
 BWD_TRAFFIC = {
     "switch-base-uniform": {
         "sources_sha256": "409d356bb35470314da9ef7f5376d0dd79ac1a74923680b28b0e5940205c76b4",
-        "fetch_kib": [322773.0, 313080.0], "write_kib": [614911.0, 601879.0],
+        "fetch_kib": [322781.0, 313115.0], "write_kib": [614900.0, 601879.0],
         "fetch_scale": 2.0, "write_scale": 1.0,
     },
     "switch-large-shared": {
         "sources_sha256": "409d356bb35470314da9ef7f5376d0dd79ac1a74923680b28b0e5940205c76b4",
-        "fetch_kib": [5871749.0, 5803658.0], "write_kib": [10760390.0, 10813443.0],
+        "fetch_kib": [5889809.0, 5801174.0], "write_kib": [10760901.0, 10813443.0],
         "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
