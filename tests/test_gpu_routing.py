@@ -130,6 +130,9 @@ TOPK_EDGE = [
     (_custom("k4-f32-odd", 301, 20, 36, 7, 1.3, dtype="f32", seed=5), 4),
     (_custom("k8-all-experts", 256, 128, 128, 8, 2.0, seed=6), 8),
     (_custom("k2-t1", 1, 128, 256, 4, 1.0, seed=7), 2),
+    # 18000 choices: the per-expert token-order assignment's 1024-thread top-K
+    # instance over two 16K-choice chunks, with a ragged last chunk
+    (_custom("k2-two-chunks", 9000, 128, 128, 16, 1.0, seed=8, bias_scale=0.5), 2),
 ]
 
 
