@@ -597,6 +597,20 @@ static switch_status moe_forward(const switch_moe_desc* desc, const switch_moe_i
                    out->routed_count, out->f, out->P, out->l_aux, w + L.off_route, st, L.fused, rex);
   if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/route");
   if ((e = mark(1)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
+  // the first (streaming) GEMM builds the assignment's cross-expert results
+  // itself, so no kernel runs between the assignment and the GEMM
+  const bool gemm_finalizes =
+      L.fused && L.M == 1 && ffn_stream_applies(d.dtype, C, d.d_model, d.d_ff, mxp != nullptr);
+  ActiveFromKept afk;
+  if (gemm_finalizes) {
+    afk.kept = out->kept_count;
+    afk.term = reinterpret_cast<const double*>(w + L.off_term);
+    afk.active = active;
+    afk.n_active = nact;
+    afk.n_dropped = out->n_dropped;
+    afk.l_aux = out->l_aux;
+    afk.TV = (int64_t)L.K * d.T;
+  }
   if (L.fused) {
     // token order: one workgroup per expert takes its tokens into slots (and
     // reduces the router statistics); GEMM 1 then reads each slot's token row
@@ -604,7 +618,7 @@ static switch_status moe_forward(const switch_moe_desc* desc, const switch_moe_i
     e = launch_assign_token(L.route, d.T, L.K, d.N, C, L.K > 1 ? rex.ev_cm : out->expert_id,
                             reinterpret_cast<double*>(w + L.off_term),
                             out->routed_count, out->f, out->P, out->l_aux, out->slot, tos, out->kept_count,
-                            out->n_dropped, active, nact, w + L.off_route, st);
+                            out->n_dropped, active, nact, w + L.off_route, st, !gemm_finalizes);
     if (e == hipSuccess && L.M > 1)
       e = launch_expand(rex.ev_cm, rex.gv_cm, d.T, d.N, C, L.M, 0, out->slot, out->expert_id, out->gate, tos,
                         out->kept_count, active, nact, out->n_dropped, reinterpret_cast<int32_t*>(w + L.off_list), st);
@@ -612,7 +626,7 @@ static switch_status moe_forward(const switch_moe_desc* desc, const switch_moe_i
     if ((e = mark(2)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
     if ((e = mark(3)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
     e = launch_ffn(L.ffn, in->x, in->w1, in->w2, d.dtype, d.N, C, d.d_model, d.d_ff, out->kept_count, active, nact,
-                   xout, w + L.off_ffn, st, tos, d.T, h_save, mxp);
+                   xout, w + L.off_ffn, st, tos, d.T, h_save, mxp, gemm_finalizes ? &afk : nullptr);
   } else {
     if (L.ec) {
       e = launch_ec_select(rex.probs_t, d.T, d.N, C, tos, reinterpret_cast<int32_t*>(w + L.off_pick),

@@ -373,6 +373,52 @@ __device__ __forceinline__ void ffn_stream(const uint16_t* __restrict__ A, const
   }
 }
 
+// Every workgroup of the first GEMM builds the active list from the kept
+// counts (thread i takes experts 4i .. 4i + 3, so a block scan keeps expert
+// order); workgroup 0 also writes the list, n_active, n_dropped and L_aux.
+// Returns n_active; the list is left in s_act.
+template <int NTH>
+__device__ int active_from_kept(const ActiveFromKept& afk, int N, int* s_act, int* wsum, double* sl) {
+  constexpr int PER = 1024 / NTH;  // N <= 1024
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int kv[PER], cnt = 0, ksum = 0;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int n = tid * PER + q;
+    kv[q] = n < N ? afk.kept[n] : 0;
+    cnt += kv[q] > 0 ? 1 : 0;
+    ksum += kv[q];
+  }
+  int n_act, kept_tot;
+  int pos = block_exclusive_scan(cnt, wsum, &n_act);
+  block_exclusive_scan(ksum, wsum, &kept_tot);
+#pragma unroll
+  for (int q = 0; q < PER; ++q)
+    if (kv[q] > 0) s_act[pos++] = tid * PER + q;
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    for (int a = tid; a < n_act; a += NTH) afk.active[a] = s_act[a];
+    // L_aux through route_finalize's tree: 16 groups of 64 experts, an xor tree
+    // inside each group, then the group sums in group order
+    for (int g = w; g < 16; g += NTH / 64) {
+      const int n = g * 64 + lane;
+      double t = n < N ? afk.term[n] : 0.0;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, 64);
+      if (lane == 0) sl[g] = t;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      double a = 0.0;
+      for (int i = 0; i < 16; ++i) a += sl[i];
+      afk.l_aux[0] = (float)((double)N * a);
+      afk.n_active[0] = n_act;
+      afk.n_dropped[0] = (int32_t)(afk.TV - kept_tot);
+    }
+  }
+  return n_act;
+}
+
 // 128-column work items (16-byte weight loads, J = 8) unless, even at the
 // largest K split, they would give fewer than 2/5 of the grid's wave slots a
 // task; then 64-column items (twice as many).  The threshold sits between
@@ -387,9 +433,18 @@ __global__ __launch_bounds__(WAVES * 64, SWM_FFN_MINB) void ffn_gemm_bf16(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, uint16_t* __restrict__ out,
     const int32_t* __restrict__ kept_count, const int32_t* __restrict__ active, const int32_t* __restrict__ n_active,
     int N, int C, int K, int Ncols, int relu, int mch, const int32_t* __restrict__ gather, int64_t a_rows, int a_tiles,
-    int o_tiles) {
+    int o_tiles, ActiveFromKept afk) {
   __shared__ float red[WAVES * 4 * JMAX * 64];
-  int n_act = n_active[0];
+  __shared__ int s_act[1024];
+  __shared__ int wsum[16];
+  __shared__ double sl[16];
+  int n_act;
+  if (afk.kept != nullptr) {
+    n_act = active_from_kept<WAVES * 64>(afk, N, s_act, wsum, sl);
+    active = s_act;
+  } else {
+    n_act = n_active[0];
+  }
   if (n_act > N) n_act = N;
   if (JMAX == 8 && Ncols % 128 == 0 &&
       (int64_t)n_act * (Ncols / 128) * mch * WAVES * 5 >= (int64_t)gridDim.x * WAVES * 2)
@@ -498,13 +553,14 @@ static int persistent_grid(const void* kernel, int threads) {
 template <int MT, int J>
 static hipError_t launch_gemm(const void* A, const void* W, void* out, const int32_t* kept, const int32_t* active,
                               const int32_t* n_active, int N, int C, int K, int Ncols, int relu, int mch,
-                              hipStream_t st, const int32_t* gather, int64_t a_rows, int a_tiles, int o_tiles) {
+                              hipStream_t st, const int32_t* gather, int64_t a_rows, int a_tiles, int o_tiles,
+                              const ActiveFromKept& afk) {
   constexpr int kWaves = SWM_FFN_WAVES;
   auto kern = ffn_gemm_bf16<MT, kWaves, SWM_FFN_STAGES, J>;
   const int grid = persistent_grid(reinterpret_cast<const void*>(kern), kWaves * 64);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kWaves * 64), 0, st, static_cast<const uint16_t*>(A),
                      static_cast<const uint16_t*>(W), static_cast<uint16_t*>(out), kept, active, n_active, N, C, K,
-                     Ncols, relu, mch, gather, a_rows, a_tiles, o_tiles);
+                     Ncols, relu, mch, gather, a_rows, a_tiles, o_tiles, afk);
   return hipGetLastError();
 }
 
@@ -514,36 +570,38 @@ template <int MT>
 static hipError_t launch_gemm_cols(const void* A, const void* W, void* out, const int32_t* kept,
                                    const int32_t* active, const int32_t* n_active, int N, int C, int K, int Ncols,
                                    int relu, int mch, hipStream_t st, const int32_t* gather, int64_t a_rows,
-                                   int a_tiles, int o_tiles) {
+                                   int a_tiles, int o_tiles, const ActiveFromKept& afk) {
   if constexpr (kAllow128 && MT <= 3) {
     if (Ncols % 128 == 0)
       return launch_gemm<MT, 8>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, mch, st, gather, a_rows,
-                                a_tiles, o_tiles);
+                                a_tiles, o_tiles, afk);
   }
   return launch_gemm<MT, 4>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, mch, st, gather, a_rows, a_tiles,
-                            o_tiles);
+                            o_tiles, afk);
 }
 
 static hipError_t gemm_bf16(const FfnPlan& pl, const void* A, const void* W, void* out, const int32_t* kept,
                             const int32_t* active, const int32_t* n_active, int N, int C, int K, int Ncols, int relu,
-                            hipStream_t st, const int32_t* gather, int64_t a_rows, int a_tiles, int o_tiles) {
+                            hipStream_t st, const int32_t* gather, int64_t a_rows, int a_tiles, int o_tiles,
+                            const ActiveFromKept& afk = ActiveFromKept{}) {
   switch (pl.mt) {
     case 1: return launch_gemm_cols<1>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, pl.mch, st, gather,
-                                       a_rows, a_tiles, o_tiles);
+                                       a_rows, a_tiles, o_tiles, afk);
     case 2: return launch_gemm_cols<2>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, pl.mch, st, gather,
-                                       a_rows, a_tiles, o_tiles);
+                                       a_rows, a_tiles, o_tiles, afk);
     case 3: return launch_gemm_cols<3>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, pl.mch, st, gather,
-                                       a_rows, a_tiles, o_tiles);
+                                       a_rows, a_tiles, o_tiles, afk);
     default: return launch_gemm_cols<4>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, pl.mch, st, gather,
-                                        a_rows, a_tiles, o_tiles);
+                                        a_rows, a_tiles, o_tiles, afk);
   }
 }
 
 hipError_t launch_ffn(const FfnPlan& pl, const void* xin, const void* w1, const void* w2, int dtype, int N, int C, int d,
                       int dff, const int32_t* kept_count, const int32_t* active, const int32_t* n_active, void* xout,
                       char* ws, hipStream_t st, const int32_t* gather, int64_t a_rows, void* h_out,
-                      const MxWeights* mx) {
+                      const MxWeights* mx, const ActiveFromKept* afk) {
   void* h = h_out != nullptr ? h_out : static_cast<void*>(ws + pl.off_h);
+  if (afk != nullptr && !ffn_stream_applies(dtype, C, d, dff, mx != nullptr)) return hipErrorInvalidValue;
   if (mx != nullptr)  // MXFP4 weights (bf16 activations; the caller checked mx_ffn_applies)
     return launch_ffn_mx(xin, *mx, N, C, d, dff, kept_count, active, n_active, xout, h, st, gather, a_rows);
   if (dtype == 0) {
@@ -566,9 +624,14 @@ hipError_t launch_ffn(const FfnPlan& pl, const void* xin, const void* w1, const 
   // it (training); then it is row-major [N, C, d_ff] as documented.  In the
   // workspace it takes the fragment-blocked layout (ffn_plan sizes it).
   const int tiles = h_out == nullptr ? pl.h_tiles : 0;
-  hipError_t e = gemm_bf16(pl, xin, w1, h, kept_count, active, n_active, N, C, d, dff, 1, st, gather, a_rows, 0, tiles);
+  hipError_t e = gemm_bf16(pl, xin, w1, h, kept_count, active, n_active, N, C, d, dff, 1, st, gather, a_rows, 0, tiles,
+                           afk != nullptr ? *afk : ActiveFromKept{});
   if (e != hipSuccess) return e;
   return gemm_bf16(pl, h, w2, xout, kept_count, active, n_active, N, C, dff, d, 0, st, nullptr, 0, tiles, 0);
+}
+
+bool ffn_stream_applies(int dtype, int C, int d, int dff, bool mx) {
+  return dtype == 1 && !mx && !tiled_ffn_applies(C, d, dff);
 }
 
 }  // namespace swm

@@ -45,10 +45,11 @@ hipError_t launch_route(const RoutePlan& pl, const void* x, const void* wg, cons
 // stats_later): one workgroup per expert, then one for the cross-expert
 // results; term: fp64 [N] scratch
 // (K > 1: expert_id is the choice-major [K, T] list, slot is [T, K])
+// finalize == false: the cross-expert results are left to the first GEMM (ActiveFromKept)
 hipError_t launch_assign_token(const RoutePlan& pl, int64_t T, int K, int N, int C, const int32_t* expert_id, double* term,
                                int32_t* routed_count, float* f, float* P, float* l_aux, int32_t* slot,
                                int32_t* token_of_slot, int32_t* kept_count, int32_t* n_dropped, int32_t* active,
-                               int32_t* n_active, char* ws, hipStream_t st);
+                               int32_t* n_active, char* ws, hipStream_t st, bool finalize = true);
 
 // ---------------- capacity / slots ----------------
 struct AssignPlan {
@@ -86,10 +87,26 @@ FfnPlan ffn_plan(int N, int C, int d, int dff, int dtype);
 // token gather[e * C + r] (token_of_slot), so no dispatched copy is needed.
 // h_out != NULL: the hidden activation [N, C, dff] goes there instead of the
 // workspace (kept for the backward pass).
+// The cross-expert results of the token-order assignment, built by every
+// workgroup of the first GEMM from the kept counts instead of by a kernel of
+// their own (streaming bf16 GEMMs only, ffn_stream_applies): the active list
+// in expert order and n_active (workgroup 0 writes both for the second GEMM),
+// n_dropped = TV - sum of kept counts, and L_aux = N sum_i f_i P_i through
+// route_finalize's tree.  kept == NULL: off (active / n_active are read).
+struct ActiveFromKept {
+  const int32_t* kept = nullptr;
+  const double* term = nullptr;  // f_i P_i [N]
+  int32_t* active = nullptr;
+  int32_t* n_active = nullptr;
+  int32_t* n_dropped = nullptr;
+  float* l_aux = nullptr;
+  int64_t TV = 0;  // choices in the assignment list (T K)
+};
+bool ffn_stream_applies(int dtype, int C, int d, int dff, bool mx);
 hipError_t launch_ffn(const FfnPlan& pl, const void* xin, const void* w1, const void* w2, int dtype, int N, int C, int d,
                       int dff, const int32_t* kept_count, const int32_t* active, const int32_t* n_active, void* xout,
                       char* ws, hipStream_t st, const int32_t* gather = nullptr, int64_t a_rows = 0,
-                      void* h_out = nullptr, const MxWeights* mx = nullptr);
+                      void* h_out = nullptr, const MxWeights* mx = nullptr, const ActiveFromKept* afk = nullptr);
 bool mx_ffn_applies(int C, int d, int dff);
 hipError_t launch_ffn_mx(const void* xin, const MxWeights& mw, int N, int C, int d, int dff,
                          const int32_t* kept_count, const int32_t* active, const int32_t* n_active, void* xout,

@@ -776,7 +776,7 @@ hipError_t launch_route(const RoutePlan& pl, const void* x, const void* wg, cons
 hipError_t launch_assign_token(const RoutePlan& pl, int64_t T, int K, int N, int C, const int32_t* expert_id, double* term,
                                int32_t* routed_count, float* f, float* P, float* l_aux, int32_t* slot,
                                int32_t* token_of_slot, int32_t* kept_count, int32_t* n_dropped, int32_t* active,
-                               int32_t* n_active, char* ws, hipStream_t st) {
+                               int32_t* n_active, char* ws, hipStream_t st, bool finalize) {
   const float* part_p = reinterpret_cast<const float*>(ws + pl.off_part_p);
   const int32_t* part_cnt = reinterpret_cast<const int32_t*>(ws + pl.off_part_cnt);
   const int NP = (N + 63) / 64 * 64;
@@ -795,7 +795,7 @@ hipError_t launch_assign_token(const RoutePlan& pl, int64_t T, int K, int N, int
   }
 #undef SWM_ASSIGN_TOKEN
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !finalize) return e;
   hipLaunchKernelGGL(assign_token_finalize, dim3(1), dim3(1024), 0, st, kept_count, term, N, T * K, l_aux, active,
                      n_active, n_dropped);
   return hipGetLastError();
