@@ -35,6 +35,7 @@
 // No reduction ever crosses workgroups, so no agent-scope fences (which write
 // back and invalidate whole L2 caches on this multi-XCD part) are needed.
 // fp32 kernel: plain fp32 FMA, one workgroup per (slot row, expert).
+#include "active_list.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -373,52 +374,6 @@ __device__ __forceinline__ void ffn_stream(const uint16_t* __restrict__ A, const
   }
 }
 
-// Every workgroup of the first GEMM builds the active list from the kept
-// counts (thread i takes experts 4i .. 4i + 3, so a block scan keeps expert
-// order); workgroup 0 also writes the list, n_active, n_dropped and L_aux.
-// Returns n_active; the list is left in s_act.
-template <int NTH>
-__device__ int active_from_kept(const ActiveFromKept& afk, int N, int* s_act, int* wsum, double* sl) {
-  constexpr int PER = 1024 / NTH;  // N <= 1024
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  int kv[PER], cnt = 0, ksum = 0;
-#pragma unroll
-  for (int q = 0; q < PER; ++q) {
-    const int n = tid * PER + q;
-    kv[q] = n < N ? afk.kept[n] : 0;
-    cnt += kv[q] > 0 ? 1 : 0;
-    ksum += kv[q];
-  }
-  int n_act, kept_tot;
-  int pos = block_exclusive_scan(cnt, wsum, &n_act);
-  block_exclusive_scan(ksum, wsum, &kept_tot);
-#pragma unroll
-  for (int q = 0; q < PER; ++q)
-    if (kv[q] > 0) s_act[pos++] = tid * PER + q;
-  __syncthreads();
-  if (blockIdx.x == 0) {
-    for (int a = tid; a < n_act; a += NTH) afk.active[a] = s_act[a];
-    // L_aux through route_finalize's tree: 16 groups of 64 experts, an xor tree
-    // inside each group, then the group sums in group order
-    for (int g = w; g < 16; g += NTH / 64) {
-      const int n = g * 64 + lane;
-      double t = n < N ? afk.term[n] : 0.0;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, 64);
-      if (lane == 0) sl[g] = t;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      double a = 0.0;
-      for (int i = 0; i < 16; ++i) a += sl[i];
-      afk.l_aux[0] = (float)((double)N * a);
-      afk.n_active[0] = n_act;
-      afk.n_dropped[0] = (int32_t)(afk.TV - kept_tot);
-    }
-  }
-  return n_act;
-}
-
 // 128-column work items (16-byte weight loads, J = 8) unless, even at the
 // largest K split, they would give fewer than 2/5 of the grid's wave slots a
 // task; then 64-column items (twice as many).  The threshold sits between
@@ -603,7 +558,8 @@ hipError_t launch_ffn(const FfnPlan& pl, const void* xin, const void* w1, const 
   void* h = h_out != nullptr ? h_out : static_cast<void*>(ws + pl.off_h);
   if (afk != nullptr && !ffn_stream_applies(dtype, C, d, dff, mx != nullptr)) return hipErrorInvalidValue;
   if (mx != nullptr)  // MXFP4 weights (bf16 activations; the caller checked mx_ffn_applies)
-    return launch_ffn_mx(xin, *mx, N, C, d, dff, kept_count, active, n_active, xout, h, st, gather, a_rows);
+    return launch_ffn_mx(xin, *mx, N, C, d, dff, kept_count, active, n_active, xout, h, st, gather, a_rows,
+                         afk != nullptr ? *afk : ActiveFromKept{});
   if (dtype == 0) {
     hipLaunchKernelGGL(ffn_gemm_f32, dim3((unsigned)C, (unsigned)N), dim3(256), 0, st, static_cast<const float*>(xin),
                        static_cast<const float*>(w1), static_cast<float*>(h), kept_count, active, n_active, N, C, d,
@@ -631,7 +587,7 @@ hipError_t launch_ffn(const FfnPlan& pl, const void* xin, const void* w1, const 
 }
 
 bool ffn_stream_applies(int dtype, int C, int d, int dff, bool mx) {
-  return dtype == 1 && !mx && !tiled_ffn_applies(C, d, dff);
+  return dtype == 1 && (mx ? mx_ffn_applies(C, d, dff) : !tiled_ffn_applies(C, d, dff));
 }
 
 }  // namespace swm

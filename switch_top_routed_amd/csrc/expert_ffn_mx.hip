@@ -22,6 +22,7 @@
 // contiguous bytes of the token row.  Work items, the K split across waves and
 // the output layout (4 consecutive columns per lane) follow the bf16
 // weight-streaming kernel.
+#include "active_list.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -78,11 +79,20 @@ __global__ __launch_bounds__(WAVES * 64, 2) void ffn_mx_stream(
     const uint16_t* __restrict__ A, const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Ws,
     uint16_t* __restrict__ out, const int32_t* __restrict__ kept_count, const int32_t* __restrict__ active,
     const int32_t* __restrict__ n_active, int N, int C, int K, int Ncols, int relu, int mch,
-    const int32_t* __restrict__ gather, int64_t a_rows) {
+    const int32_t* __restrict__ gather, int64_t a_rows, ActiveFromKept afk) {
   __shared__ float red[WAVES * 4 * 4 * 64];
+  __shared__ int s_act[1024];
+  __shared__ int wsum[16];
+  __shared__ double sl[16];
   const int tid = threadIdx.x, lane = tid & 63, c = lane & 15, kg = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int n_act = n_active[0];
+  int n_act;
+  if (afk.kept != nullptr) {  // first GEMM of the token-order forward: the active list from the kept counts
+    n_act = active_from_kept<WAVES * 64>(afk, N, s_act, wsum, sl);
+    active = s_act;
+  } else {
+    n_act = n_active[0];
+  }
   if (n_act > N) n_act = N;
   const int NCB = Ncols / 64;
   const int nk = K >> 7;  // 128-deep steps
@@ -315,14 +325,16 @@ static int mx_grid(const void* kernel, int threads) {
 template <int MT>
 static hipError_t launch_mx_mt(const void* A, const uint8_t* q, const uint8_t* s, void* out, const int32_t* kept,
                                const int32_t* active, const int32_t* n_active, int N, int C, int K, int Ncols,
-                               int relu, hipStream_t st, const int32_t* gather, int64_t a_rows) {
+                               int relu, hipStream_t st, const int32_t* gather, int64_t a_rows,
+                               const ActiveFromKept& afk) {
   constexpr int kWaves = 4;
   constexpr int kStages = MT <= 2 ? 3 : 2;
   auto kern = ffn_mx_stream<MT, kWaves, kStages>;
   const int mch = (C + MT * 16 - 1) / (MT * 16);
   const int grid = mx_grid(reinterpret_cast<const void*>(kern), kWaves * 64);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kWaves * 64), 0, st, static_cast<const uint16_t*>(A), q, s,
-                     static_cast<uint16_t*>(out), kept, active, n_active, N, C, K, Ncols, relu, mch, gather, a_rows);
+                     static_cast<uint16_t*>(out), kept, active, n_active, N, C, K, Ncols, relu, mch, gather, a_rows,
+                     afk);
   return hipGetLastError();
 }
 
@@ -330,21 +342,21 @@ bool mx_ffn_applies(int C, int d, int dff) { return C <= 64 && d % 128 == 0 && d
 
 hipError_t launch_ffn_mx(const void* xin, const MxWeights& mw, int N, int C, int d, int dff,
                          const int32_t* kept_count, const int32_t* active, const int32_t* n_active, void* xout,
-                         void* h, hipStream_t st, const int32_t* gather, int64_t a_rows) {
+                         void* h, hipStream_t st, const int32_t* gather, int64_t a_rows, const ActiveFromKept& afk) {
   // up to 48 rows in one item; 49 .. 64 rows as two 32-row m-chunks (4 row tiles
   // of accumulators and A fragments would not fit in registers)
   const int mt = C <= 16 ? 1 : C <= 32 ? 2 : C <= 48 ? 3 : 2;
   auto one = [&](const void* A, const uint8_t* q, const uint8_t* s, void* o, int K, int Ncols, int relu,
-                 const int32_t* ga, int64_t ar) -> hipError_t {
+                 const int32_t* ga, int64_t ar, const ActiveFromKept& ak) -> hipError_t {
     switch (mt) {
-      case 1: return launch_mx_mt<1>(A, q, s, o, kept_count, active, n_active, N, C, K, Ncols, relu, st, ga, ar);
-      case 2: return launch_mx_mt<2>(A, q, s, o, kept_count, active, n_active, N, C, K, Ncols, relu, st, ga, ar);
-      default: return launch_mx_mt<3>(A, q, s, o, kept_count, active, n_active, N, C, K, Ncols, relu, st, ga, ar);
+      case 1: return launch_mx_mt<1>(A, q, s, o, kept_count, active, n_active, N, C, K, Ncols, relu, st, ga, ar, ak);
+      case 2: return launch_mx_mt<2>(A, q, s, o, kept_count, active, n_active, N, C, K, Ncols, relu, st, ga, ar, ak);
+      default: return launch_mx_mt<3>(A, q, s, o, kept_count, active, n_active, N, C, K, Ncols, relu, st, ga, ar, ak);
     }
   };
-  hipError_t e = one(xin, mw.w1_codes, mw.w1_scales, h, d, dff, 1, gather, a_rows);
+  hipError_t e = one(xin, mw.w1_codes, mw.w1_scales, h, d, dff, 1, gather, a_rows, afk);
   if (e != hipSuccess) return e;
-  return one(h, mw.w2_codes, mw.w2_scales, xout, dff, d, 0, nullptr, 0);
+  return one(h, mw.w2_codes, mw.w2_scales, xout, dff, d, 0, nullptr, 0, ActiveFromKept{});
 }
 
 hipError_t launch_mx_quantize(const void* w, int dtype, int64_t batches, int K, int Ncols, uint8_t* codes,

@@ -110,7 +110,8 @@ hipError_t launch_ffn(const FfnPlan& pl, const void* xin, const void* w1, const 
 bool mx_ffn_applies(int C, int d, int dff);
 hipError_t launch_ffn_mx(const void* xin, const MxWeights& mw, int N, int C, int d, int dff,
                          const int32_t* kept_count, const int32_t* active, const int32_t* n_active, void* xout,
-                         void* h, hipStream_t st, const int32_t* gather, int64_t a_rows);
+                         void* h, hipStream_t st, const int32_t* gather, int64_t a_rows,
+                         const ActiveFromKept& afk);
 hipError_t launch_mx_quantize(const void* w, int dtype, int64_t batches, int K, int Ncols, uint8_t* codes,
                               uint8_t* scales, hipStream_t st);
 // writes {M}, {0}, {1} for the dense (shared-expert) FFN
