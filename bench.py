@@ -54,13 +54,13 @@ FFN_SOURCES = ("switch_top_routed_amd/csrc/expert_ffn.hip", "switch_top_routed_a
 # profiles/*_hbm_traffic.md.
 TRAFFIC = {
     "switch-base-uniform": {
-        "sources_sha256": "aeca613147d2856d5e20637249b4e46a5691ef64dfdd48a210bc801be002f789",
-        "fetch_kib": [305788.0, 315606.0], "write_kib": [24108.0, 6027.0],
+        "sources_sha256": "6326c28ee506bec22c84c4b4bd246c6aadb40285278bee8fd6a10af2473318af",
+        "fetch_kib": [305818.0, 315590.0], "write_kib": [24109.0, 6027.0],
         "fetch_scale": 2.0, "write_scale": 1.0,
     },
     "switch-large-shared": {
-        "sources_sha256": "aeca613147d2856d5e20637249b4e46a5691ef64dfdd48a210bc801be002f789",
-        "fetch_kib": [5328288.0, 5495674.0], "write_kib": [262218.0, 163840.0],
+        "sources_sha256": "6326c28ee506bec22c84c4b4bd246c6aadb40285278bee8fd6a10af2473318af",
+        "fetch_kib": [5329371.0, 5498002.0], "write_kib": [262272.0, 163840.0],
         "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
@@ -72,12 +72,12 @@ BWD_SOURCES = ("switch_top_routed_amd/csrc/backward_fused.hip", "switch_top_rout
 BWD_TRAFFIC = {
     "switch-base-uniform": {
         "sources_sha256": "409d356bb35470314da9ef7f5376d0dd79ac1a74923680b28b0e5940205c76b4",
-        "fetch_kib": [322781.0, 313115.0], "write_kib": [614900.0, 601879.0],
+        "fetch_kib": [322784.0, 313059.0], "write_kib": [614909.0, 601879.0],
         "fetch_scale": 2.0, "write_scale": 1.0,
     },
     "switch-large-shared": {
         "sources_sha256": "409d356bb35470314da9ef7f5376d0dd79ac1a74923680b28b0e5940205c76b4",
-        "fetch_kib": [5889809.0, 5801174.0], "write_kib": [10760901.0, 10813443.0],
+        "fetch_kib": [5879322.0, 5801339.0], "write_kib": [10761420.0, 10813443.0],
         "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
