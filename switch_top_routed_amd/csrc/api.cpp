@@ -618,10 +618,11 @@ static switch_status moe_forward(const switch_moe_desc* desc, const switch_moe_i
     e = launch_assign_token(L.route, d.T, L.K, d.N, C, L.K > 1 ? rex.ev_cm : out->expert_id,
                             reinterpret_cast<double*>(w + L.off_term),
                             out->routed_count, out->f, out->P, out->l_aux, out->slot, tos, out->kept_count,
-                            out->n_dropped, active, nact, w + L.off_route, st, !gemm_finalizes);
-    if (e == hipSuccess && L.M > 1)
+                            out->n_dropped, active, nact, w + L.off_route, st, !gemm_finalizes && L.M == 1);
+    if (e == hipSuccess && L.M > 1)  // the expansion's finalize also takes L_aux over
       e = launch_expand(rex.ev_cm, rex.gv_cm, d.T, d.N, C, L.M, 0, out->slot, out->expert_id, out->gate, tos,
-                        out->kept_count, active, nact, out->n_dropped, reinterpret_cast<int32_t*>(w + L.off_list), st);
+                        out->kept_count, active, nact, out->n_dropped, reinterpret_cast<int32_t*>(w + L.off_list), st,
+                        reinterpret_cast<const double*>(w + L.off_term), out->l_aux);
     if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/assign");
     if ((e = mark(2)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
     if ((e = mark(3)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");

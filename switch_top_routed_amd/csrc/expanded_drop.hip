@@ -222,11 +222,29 @@ __global__ __launch_bounds__(kXdThreads) void expand_round(const int32_t* __rest
   if (tid == 0) kept_count[e] = kept0 + take;
 }
 
+// term != NULL (token order, whose assignment left its cross-expert step to
+// this kernel): also L_aux = N sum_i f_i P_i from term[i] = f_i P_i through
+// route_finalize's tree (xor tree inside each wave, then the wave sums in
+// wave order).
 __global__ __launch_bounds__(1024) void expand_finalize(const int32_t* __restrict__ kept_count, int N, int64_t T,
                                                         int32_t* __restrict__ active, int32_t* __restrict__ n_active,
-                                                        int32_t* __restrict__ n_dropped) {
+                                                        int32_t* __restrict__ n_dropped,
+                                                        const double* __restrict__ term, float* __restrict__ l_aux) {
   __shared__ int wsum[16];
+  __shared__ double sl[16];
   const int n = threadIdx.x;
+  if (term != nullptr) {
+    double t = n < N ? term[n] : 0.0;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, 64);
+    if ((n & 63) == 0) sl[n >> 6] = t;
+    __syncthreads();
+    if (n == 0) {
+      double a = 0.0;
+      for (int i = 0; i < 16; ++i) a += sl[i];
+      l_aux[0] = (float)((double)N * a);
+    }
+  }
   const int kept = n < N ? kept_count[n] : 0;
   int tot_active, tot_kept;
   const int pos = block_exclusive_scan(kept > 0 ? 1 : 0, wsum, &tot_active);
@@ -243,14 +261,16 @@ size_t expand_lds_bytes(int C, int gate_order) { return gate_order ? (size_t)kXd
 
 hipError_t launch_expand(const int32_t* ev_cm, const float* gv_cm, int64_t T, int N, int C, int M, int gate_order,
                          int32_t* slot, int32_t* expert_id, float* gate, int32_t* tos, int32_t* kept_count,
-                         int32_t* active, int32_t* n_active, int32_t* n_dropped, int32_t* list, hipStream_t st) {
+                         int32_t* active, int32_t* n_active, int32_t* n_dropped, int32_t* list, hipStream_t st,
+                         const double* term, float* l_aux) {
   for (int r = 1; r < M; ++r) {
     hipLaunchKernelGGL(expand_round, dim3((unsigned)N), dim3(kXdThreads), expand_lds_bytes(C, gate_order), st, ev_cm + r * T,
                        gv_cm + r * T, T, C, gate_order, slot, expert_id, gate, tos, kept_count, list);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(expand_finalize, dim3(1), dim3(1024), 0, st, kept_count, N, T, active, n_active, n_dropped);
+  hipLaunchKernelGGL(expand_finalize, dim3(1), dim3(1024), 0, st, kept_count, N, T, active, n_active, n_dropped, term,
+                     l_aux);
   return hipGetLastError();
 }
 

@@ -210,7 +210,8 @@ hipError_t launch_combine_picks(int mode, const void* expert_out, const void* x,
 // n_dropped.  list: workspace [N, T] int32.  C <= kMaxExpertChoiceK.
 hipError_t launch_expand(const int32_t* ev_cm, const float* gv_cm, int64_t T, int N, int C, int M, int gate_order,
                          int32_t* slot, int32_t* expert_id, float* gate, int32_t* tos, int32_t* kept_count,
-                         int32_t* active, int32_t* n_active, int32_t* n_dropped, int32_t* list, hipStream_t st);
+                         int32_t* active, int32_t* n_active, int32_t* n_dropped, int32_t* list, hipStream_t st,
+                         const double* term = nullptr, float* l_aux = nullptr);
 
 // shared dense expert backward on LDS-tiled MFMA (bf16): dZs = (dY Ws2^T) *
 // [Hs > 0], dWs2 = Hs^T dY, dWs1 = x^T dZs, dXs = dZs Ws1^T (fp32)
