@@ -47,19 +47,19 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 # counters is reported only while these files are byte-identical to the ones
 # the counters were taken on.
 FFN_SOURCES = ("switch_top_routed_amd/csrc/expert_ffn.hip", "switch_top_routed_amd/csrc/expert_ffn_dma.hip",
-               "switch_top_routed_amd/csrc/common.hpp")
+               "switch_top_routed_amd/csrc/common.hpp", "switch_top_routed_amd/csrc/active_list.hpp")
 # FETCH_SIZE / WRITE_SIZE (KiB per dispatch, as rocprofv3 prints them) of the two
 # routed-FFN launches of one step, and the scale factors that a plain 1 GiB
 # device copy gives those counters (bytes moved / bytes counted).  Source:
 # profiles/*_hbm_traffic.md.
 TRAFFIC = {
     "switch-base-uniform": {
-        "sources_sha256": "6326c28ee506bec22c84c4b4bd246c6aadb40285278bee8fd6a10af2473318af",
+        "sources_sha256": "533499f2a76a80bf41b470834ada78ebd22318b8af21b9e1e25403c5005574ee",
         "fetch_kib": [305818.0, 315590.0], "write_kib": [24109.0, 6027.0],
         "fetch_scale": 2.0, "write_scale": 1.0,
     },
     "switch-large-shared": {
-        "sources_sha256": "6326c28ee506bec22c84c4b4bd246c6aadb40285278bee8fd6a10af2473318af",
+        "sources_sha256": "533499f2a76a80bf41b470834ada78ebd22318b8af21b9e1e25403c5005574ee",
         "fetch_kib": [5329371.0, 5498002.0], "write_kib": [262272.0, 163840.0],
         "fetch_scale": 2.0, "write_scale": 1.0,
     },
