@@ -5,27 +5,38 @@
 
 One step = one whole-layer forward (route -> capacity/slots -> dispatch ->
 expert FFN -> combine, plus the shared dense expert where the workload has
-one) over one batch of synthetic tokens already resident in HBM.  Prints one
-JSON line with:
-  value          tokens/s of the whole layer (T * K / wall time of K steps)
+one) over one batch of synthetic tokens already resident in HBM.  The default
+workload is the large layer (T=16384, d_model=5120, d_ff=8192, N=128 routed
+experts, cf=1.25, plus one always-on shared FFN of width 8192, bf16); the
+others run with --workload.  Prints one JSON line with:
+  value          tokens/s of the whole layer (T * K / wall time of K steps);
+                 value_median / ms_per_step_median from one event per step
+                 boundary (median over the K steps)
   roofline       the routed expert-FFN GEMM (2 launches per step, bound by the
                  HBM bytes of the expert weights it touches): algorithmic bytes
-                 per launch / average launch time, the latter from HIP events
-                 that the library records around the routed FFN inside every
-                 timed step (switch_moe_forward_timed, on the launch stream);
-                 `traffic` = HBM bytes per launch from rocprofv3 FETCH_SIZE /
-                 WRITE_SIZE counters, kept below together with a fingerprint of
-                 the kernel sources they were taken on (null when the sources
-                 have changed since)
+                 per launch (touched weights + kept rows in and out; the hidden
+                 matrix is listed apart) / average launch time, the latter from
+                 HIP events that the library records around the routed FFN
+                 inside every 8th timed step (switch_moe_forward_timed, on the
+                 launch stream); `traffic` = HBM bytes per launch from rocprofv3
+                 FETCH_SIZE / WRITE_SIZE counters, kept below together with a
+                 fingerprint of the kernel sources they were taken on (null when
+                 the sources have changed since)
+  layer_roofline the sum over stages of max(bytes / 8 TB/s, FLOPs / 2.5166
+                 PFLOP/s) against the median step, and the bound with every
+                 stage overlapped
   stages         per-stage time from the same stage events over extra steps:
                  HBM GB/s and % of peak for route, dispatch, combine; TFLOP/s
                  and % of the bf16 MFMA peak for the expert GEMMs
-  cpu_baseline   the fp64 CPU oracle timed on the host on the same batch
+  cpu_baseline   the fp64 CPU oracle timed on the host on the same batch (for
+                 the large layer: a bounded, scaled sample, described in the
+                 record)
   backward       the layer backward on the same batch (switch_moe_backward after
                  a training forward): tokens/s, the roofline of its dominant
                  weight pass (read w + write dw, timed with HIP events inside
                  the timed steps), per-stage times, and the fp64 backward
                  oracle timed on the host
+  host, gpu_clocks  CPU model and cores; amd-smi clocks after the timed steps
 Inputs are the seeded synthetic workload (x ~ N(0,1), Gaussian weights), no
 dataset.  Only one GPU is supported.
 """
@@ -88,7 +99,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="switch-base-uniform")
+    ap.add_argument("--workload", default="switch-large-shared")
     ap.add_argument("--capacity-factor", type=float, default=None, help="override the workload's capacity factor")
     ap.add_argument("--priority", choices=("token", "gate"), default=None, help="override the overflow priority")
     ap.add_argument("--no-gate-scale", action="store_true", help="combine without the gate multiplier")
@@ -106,6 +117,10 @@ def parse():
     ap.add_argument("--stage-steps", type=int, default=20, help="extra steps with every stage boundary timed")
     ap.add_argument("--ffn-event-every", type=int, default=8,
                     help="timed steps between the ones that record HIP events around the routed FFN")
+    ap.add_argument("--flush-mall", action="store_true",
+                    help="write a 512 MB scratch buffer between timed steps (outside each step's events), so no "
+                         "step reuses what the previous one left in the 256 MB memory-side cache; value then comes "
+                         "from the per-step events")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat oracle layer passes until this much CPU time has elapsed (at most 30 passes)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -208,17 +223,33 @@ def main():
         step()
     # every ffn_event_every-th timed step records the two events around the routed FFN (each
     # event record costs ~2.5 us of GPU time, so they are not put into every step); the other
-    # timed steps run the plain forward
+    # timed steps run the plain forward.  One torch event per step boundary gives the per-step
+    # times whose median is reported beside the wall-clock mean.
     every = max(1, args.ffn_event_every)
     ffn_ev = {i: sw.StageEvents(which=(3, 4)) for i in range(0, args.steps, every)}
+    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)] if args.flush_mall else None
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if args.flush_mall else None
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        if flush is not None:
+            flush.fill_(i & 0xFF)
+        bounds[i].record(stream)
         step(ffn_ev.get(i))
+        if ends is not None:
+            ends[i].record(stream)
+    bounds[args.steps].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    clocks = gpu_clocks()
+    if ends is not None:
+        step_ms = [bounds[i].elapsed_time(ends[i]) for i in range(args.steps)]
+    else:
+        step_ms = [bounds[i].elapsed_time(bounds[i + 1]) for i in range(args.steps)]
+    ms_median = float(np.median(step_ms))
     ms_per_step = elapsed / args.steps * 1e3
-    value = wl.T * args.steps / elapsed
+    value = wl.T * args.steps / elapsed if flush is None else wl.T / (ms_median * 1e-3)
     ffn_stage_ms = [e.ms(3, 4) for e in ffn_ev.values()]
 
     # every stage boundary, over extra (untimed) steps
@@ -227,53 +258,82 @@ def main():
         step(e)
     torch.cuda.synchronize()
     names = ["route", "assign", "dispatch", "expert_ffn", "shared_ffn", "combine"]
-    st_s = {n: float(np.mean([e.ms(i, i + 1) for e in full_ev])) * 1e-3 for i, n in enumerate(names)}
+    st_s = {n: float(np.median([e.ms(i, i + 1) for e in full_ev])) * 1e-3 for i, n in enumerate(names)}
 
     out = layer.out
     kept = int(out["kept_count"].sum().item())
     n_active = int((out["kept_count"] > 0).sum().item())
     T, d, F, N, C = wl.T, wl.d_model, wl.d_ff, wl.N, layer.C
     dropped = T - kept
+    Fs = wl.d_ff_shared
     # the library's forward folds the dispatch into GEMM 1 when x fits 32-bit offsets (same rule as its workspace layout)
     gathered = T * d * esz < 2 ** 31
-    route_bytes = T * d * esz + N * d * esz + T * 8 + N * 16
-    disp_bytes = 2 * kept * d * esz + 4 * kept
-    # combine: one row read per token (expert output if kept, x if dropped), one row written,
-    # plus the shared-expert row when there is one, and expert id, slot and gate per token
-    comb_bytes = 2 * T * d * esz + (T * d * esz if wl.d_ff_shared else 0) + T * 12
-    if variant:  # every kept pick's expert row, every x row, every y row
-        comb_bytes = (kept + 2 * T) * d * esz + (T * d * esz if wl.d_ff_shared else 0)
     wbytes_per = (0.5 + 1.0 / 32) if mxw else esz  # bytes per weight: MXFP4 codes + E8M0 scales
-    ffn_launch_bytes = n_active * d * F * wbytes_per + kept * (d + F) * esz  # one GEMM launch
-    ffn_flops = 4.0 * kept * d * F
+    # algorithmic work of each stage of the layer (HBM bytes, FLOPs)
+    work = {
+        # x, W_g, bias, ids + gates out; slots, token_of_slot
+        "route": (T * d * esz + N * d * esz + 4 * N + 8 * T + 12 * T + 4 * N * C, 2.0 * T * d * N),
+        "dispatch": (2 * kept * d * esz + 4 * kept, 0.0),
+        # touched weights once + the kept rows in and out (H is not algorithmic)
+        "expert_ffn": (2 * n_active * d * F * wbytes_per + 2 * kept * d * esz, 4.0 * kept * d * F),
+        # one row read per token (expert output or x), one written, plus the shared row; ids, slots, gates
+        "combine": (2 * T * d * esz + (T * d * esz if Fs else 0) + 12 * T, float(kept * d)),
+    }
+    if variant:  # every kept pick's expert row, every x row, every y row
+        work["combine"] = ((kept + 2 * T) * d * esz + (T * d * esz if Fs else 0), float(kept * d))
+    if Fs:
+        work["shared_ffn"] = (2 * d * Fs * esz + 2 * T * d * esz, 4.0 * T * d * Fs)
+    ffn_launch_bytes = work["expert_ffn"][0] / 2  # per GEMM launch (each streams one weight matrix)
+    h_launch_bytes = kept * F * esz  # hidden matrix: written by GEMM 1, read by GEMM 2 (reported, not algorithmic)
+    ffn_flops = work["expert_ffn"][1]
 
     def gbs(b, t):
         return b / t / 1e9
 
+    def bound_s(b, f):
+        return max(b / (HBM_PEAK_GBS * 1e9), f / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+
     stages = {
-        "route": {"us": st_s["route"] * 1e6, "GB_s": gbs(route_bytes, st_s["route"]),
-                  "hbm_frac": gbs(route_bytes, st_s["route"]) / HBM_PEAK_GBS},
+        "route": {"us": st_s["route"] * 1e6, "GB_s": gbs(work["route"][0], st_s["route"]),
+                  "hbm_frac": gbs(work["route"][0], st_s["route"]) / HBM_PEAK_GBS},
         "assign": {"us": st_s["assign"] * 1e6},
         "dispatch": ({"us": st_s["dispatch"] * 1e6, "folded_into_gemm1": True,
                       "note": "GEMM 1 gathers the x rows; the span is the event pair alone"}
                      if gathered else
-                     {"us": st_s["dispatch"] * 1e6, "GB_s": gbs(disp_bytes, st_s["dispatch"]),
-                      "hbm_frac": gbs(disp_bytes, st_s["dispatch"]) / HBM_PEAK_GBS}),
+                     {"us": st_s["dispatch"] * 1e6, "GB_s": gbs(work["dispatch"][0], st_s["dispatch"]),
+                      "hbm_frac": gbs(work["dispatch"][0], st_s["dispatch"]) / HBM_PEAK_GBS}),
         "expert_ffn": {"us": st_s["expert_ffn"] * 1e6, "launches": 2,
-                       "GB_s": gbs(2 * ffn_launch_bytes, st_s["expert_ffn"]),
-                       "hbm_frac": gbs(2 * ffn_launch_bytes, st_s["expert_ffn"]) / HBM_PEAK_GBS,
+                       "GB_s": gbs(work["expert_ffn"][0], st_s["expert_ffn"]),
+                       "hbm_frac": gbs(work["expert_ffn"][0], st_s["expert_ffn"]) / HBM_PEAK_GBS,
                        "TFLOP_s": ffn_flops / st_s["expert_ffn"] / 1e12,
-                       "mfma_frac": ffn_flops / st_s["expert_ffn"] / 1e12 / MFMA_BF16_PEAK_TFLOPS},
-        "combine": {"us": st_s["combine"] * 1e6, "GB_s": gbs(comb_bytes, st_s["combine"]),
-                    "hbm_frac": gbs(comb_bytes, st_s["combine"]) / HBM_PEAK_GBS},
+                       "mfma_frac": ffn_flops / st_s["expert_ffn"] / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                       "h_bytes_per_launch": h_launch_bytes},
+        "combine": {"us": st_s["combine"] * 1e6, "GB_s": gbs(work["combine"][0], st_s["combine"]),
+                    "hbm_frac": gbs(work["combine"][0], st_s["combine"]) / HBM_PEAK_GBS},
         "n_active": n_active, "kept": kept, "dropped": dropped, "stage_steps": args.stage_steps,
+        "timing": "median over the stage_steps extra steps of the HIP events at the stage boundaries",
     }
-    if wl.d_ff_shared:
-        Fs = wl.d_ff_shared
-        sh_flops = 4.0 * T * d * Fs
+    if Fs:
+        sh_flops = work["shared_ffn"][1]
         stages["shared_ffn"] = {"us": st_s["shared_ffn"] * 1e6, "launches": 2,
                                 "TFLOP_s": sh_flops / st_s["shared_ffn"] / 1e12,
                                 "mfma_frac": sh_flops / st_s["shared_ffn"] / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+
+    # layer roofline: the sum of the stage bounds, each max(bytes / HBM peak, FLOPs / MFMA peak),
+    # against the median step; and the bound with every stage overlapped (total bytes vs total FLOPs)
+    bsum = sum(bound_s(b, f) for b, f in work.values())
+    tot_b = sum(b for b, _ in work.values())
+    tot_f = sum(f for _, f in work.values())
+    boverlap = bound_s(tot_b, tot_f)
+    layer_roofline = {
+        "bound_us": bsum * 1e6, "step_us_median": ms_median * 1e3, "frac": bsum / (ms_median * 1e-3),
+        "overlap_bound_us": boverlap * 1e6, "frac_overlap": boverlap / (ms_median * 1e-3),
+        "peaks": {"hbm_GB_s": HBM_PEAK_GBS, "mfma_bf16_TFLOP_s": MFMA_BF16_PEAK_TFLOPS},
+        "stages": {k: {"bytes": b, "flops": f, "bound_us": bound_s(b, f) * 1e6,
+                       "bound_by": "hbm" if b / (HBM_PEAK_GBS * 1e9) >= f / (MFMA_BF16_PEAK_TFLOPS * 1e12) else "mfma"}
+                   for k, (b, f) in work.items()},
+        "note": "dispatch is counted as its own stage although GEMM 1 gathers the rows itself" if gathered else "",
+    }
 
     launch_s = float(np.mean(ffn_stage_ms)) * 1e-3 / 2
     achieved = gbs(ffn_launch_bytes, launch_s)
@@ -286,13 +346,20 @@ def main():
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": None if over else traffic_bytes(wl.name),
                 "kernel": f"{kernel} (routed expert FFN GEMM, 2 launches per step)",
-                "bytes_per_launch": ffn_launch_bytes, "launch_us": launch_s * 1e6,
+                "bytes_per_launch": ffn_launch_bytes, "h_bytes_per_launch": h_launch_bytes,
+                "bytes_rule": "touched experts' weight matrix + kept rows in + kept rows out, per launch; "
+                              "the hidden matrix H (written by GEMM 1, read by GEMM 2) is listed apart",
+                "launch_us": launch_s * 1e6,
                 "launch_timing": f"HIP events around the routed FFN in {len(ffn_stage_ms)} of the {args.steps} timed steps"}
 
     cpu = None
-    if not args.no_cpu_baseline and not on_device:
-        cpu = cpu_baseline(inp, args.cpu_seconds, args.top_k, args.routing, args.renorm, args.weights,
-                           args.expand)
+    if not args.no_cpu_baseline:
+        if on_device:
+            cpu = cpu_baseline_sampled(inp, {"w1": w1, "w2": w2, "ws1": ws1, "ws2": ws2}, layer.C,
+                                       args.cpu_seconds)
+        else:
+            cpu = cpu_baseline(inp, args.cpu_seconds, args.top_k, args.routing, args.renorm, args.weights,
+                               args.expand)
 
     backward = None
     if not args.no_backward and not variant and not mxw and not xd:  # the backward: top-1, native weights
@@ -300,7 +367,9 @@ def main():
 
     line = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "ms_per_step_median": ms_median,
+        "value_median": wl.T / (ms_median * 1e-3),
+        "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic (seeded Gaussian tokens and weights)",
         "config": {"workload": wl.name, "T": T, "d_model": d, "d_ff": F, "N": N,
                    "capacity_factor": wl.capacity_factor, "C": C, "priority": wl.priority,
@@ -308,10 +377,58 @@ def main():
                    "routing": ("expert choice" if args.routing == "expert" else
                                f"top-1 + Expanded Drop over {args.expand} candidates" if xd else
                                f"top-{max(1, args.top_k)}"),
-                   "expert_weights": "MXFP4 (E2M1 + E8M0 per 32)" if mxw else wl.dtype},
-        "roofline": roofline, "stages": stages, "cpu_baseline": cpu, "backward": backward,
+                   "expert_weights": "MXFP4 (E2M1 + E8M0 per 32)" if mxw else wl.dtype,
+                   "mall_flush": bool(args.flush_mall)},
+        "roofline": roofline, "layer_roofline": layer_roofline, "stages": stages, "cpu_baseline": cpu,
+        "backward": backward, "host": host_info(), "gpu_clocks": clocks,
     }
     print(json.dumps(line), flush=True)
+
+
+
+def host_info():
+    """CPU model and the cores this process may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count()
+    return {"cpu_model": model, "affinity_cores": cores}
+
+
+def gpu_clocks():
+    """Current GPU clocks as amd-smi reports them right after the timed steps
+    (best effort: None when the tool is missing or prints nothing usable)."""
+    import subprocess
+    for cmd in (["amd-smi", "metric", "-g", "0", "--clock", "--json"], ["amd-smi", "metric", "--clock", "--json"]):
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
+        except (OSError, subprocess.TimeoutExpired):
+            continue
+        if r.returncode != 0 or not r.stdout.strip():
+            continue
+        try:
+            data = json.loads(r.stdout)
+        except ValueError:
+            return {"raw": r.stdout[:400]}
+        if isinstance(data, list) and data:
+            data = data[0]
+        clk = data.get("clock", data) if isinstance(data, dict) else {}
+        picked = {}
+        if isinstance(clk, dict):
+            for k, v in clk.items():
+                if k.lower().startswith(("gfx_0", "mem_0", "fclk_0", "socclk_0")) and isinstance(v, dict):
+                    picked[k] = {kk: v.get(kk) for kk in ("clk", "min_clk", "max_clk") if kk in v}
+        return picked or {"raw": json.dumps(clk)[:400]}
+    return None
 
 
 def measure_backward(args, wl, inp, C, x, wg, w1, w2, bias, ws1, ws2, stream, on_device):
@@ -500,6 +617,80 @@ def cpu_baseline(inp, seconds, top_k=1, routing="token", renorm=False, weights="
                                      f"{'expert choice' if routing == 'expert' else f'top-{max(1, top_k)}'}"
                                      f"{f', Expanded Drop over {expand} candidates' if expand > 1 else ''}"
                                      f"{', MXFP4 experts' if weights == 'mxfp4' else ''})"}
+
+
+def cpu_baseline_sampled(inp, W, C, seconds):
+    """The fp64 oracle, as it stands, on a bounded sample of a layer whose
+    weights exist only on the device (the 22 GB large layer).  The router,
+    load statistics, capacity, slots, dispatch and combine run over the whole
+    batch; the expert FFN runs for active experts in a seeded order until
+    about `seconds` / 2 of it have elapsed, and is scaled by n_active / experts
+    done; the shared FFN runs on 512 seeded tokens and is scaled by T / 512
+    (its weights are widened once, counted in full).  Each sampled expert's
+    weights are copied to the host before its timed step (input marshalling,
+    not oracle work).  value = T / (sum of the full and scaled step times)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    wl, dt = inp.wl, inp.wl.dtype
+
+    def host_u16(t):
+        return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+
+    tm = {}
+    t0 = time.perf_counter()
+    x = oracle.widen(inp.x, dt)
+    _, p, e, g = oracle.route(x, oracle.widen(inp.w_gate, dt), inp.bias)
+    oracle.aux_loss(e, p, wl.N)
+    a = oracle.assign_slots(e, g, wl.N, C, wl.priority)
+    tm["route_assign"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    buf = oracle.dispatch(x, a["token_of_slot"], a["kept_count"])
+    tm["dispatch"] = time.perf_counter() - t0
+    active = np.asarray(a["active"])
+    order = np.random.default_rng(wl.seed + 5).permutation(active)
+    out = np.full(buf.shape, np.nan)
+    done, t_ffn = 0, 0.0
+    for ex in order:
+        w1h, w2h = host_u16(W["w1"][int(ex)]), host_u16(W["w2"][int(ex)])
+        k = int(a["kept_count"][ex])
+        t0 = time.perf_counter()
+        out[ex, :k] = oracle.ffn(buf[ex, :k], oracle.widen(w1h, dt), oracle.widen(w2h, dt))
+        t_ffn += time.perf_counter() - t0
+        done += 1
+        if t_ffn >= seconds / 2:
+            break
+    tm["expert_ffn_scaled"] = t_ffn * active.size / max(done, 1)
+    shared = None
+    ns = 0
+    if W.get("ws1") is not None:
+        ns = min(512, wl.T)
+        rows = np.sort(np.random.default_rng(wl.seed + 6).choice(wl.T, size=ns, replace=False))
+        s1h, s2h = host_u16(W["ws1"]), host_u16(W["ws2"])
+        t0 = time.perf_counter()
+        s1, s2 = oracle.widen(s1h, dt), oracle.widen(s2h, dt)
+        t_w = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        oracle.ffn(x[rows], s1, s2)
+        t_mm = time.perf_counter() - t0
+        tm["shared_ffn_scaled"] = t_w + t_mm * wl.T / ns
+        shared = np.zeros_like(x)
+    t0 = time.perf_counter()
+    oracle.combine(out, x, e, a["slot"], g, wl.gate_scale, wl.residual_all, shared)
+    tm["combine"] = time.perf_counter() - t0
+    total = sum(tm.values())
+    return {"value": wl.T / total, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "seconds": total, "step_seconds": tm,
+            "sample": f"fp64 oracle over the {wl.name} batch (T={wl.T}): router, statistics, slots, dispatch and "
+                      f"combine in full; expert FFN on {done} of {active.size} active experts, scaled by "
+                      f"{active.size}/{done}; shared FFN on {ns} of {wl.T} tokens, scaled by {wl.T}/{ns} "
+                      f"(weights widened once, in full)"}
 
 
 if __name__ == "__main__":

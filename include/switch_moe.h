@@ -95,8 +95,12 @@ typedef enum switch_routing {
 
 /* ------------------------------------------------------------------------
  * Capacity ([TOP1] Token Dropping; [SWT] expert capacity; [CAP] Where
- * capacity comes from): C = max(1, ceil(capacity_factor * T / N)).
- * Host-only.  Returns -1 if T < 1, N < 1 or capacity_factor <= 0.
+ * capacity comes from): C = max(1, ceil(capacity_factor * T / N)), clamped
+ * to T.  capacity_factor is taken at its decimal value (the shortest decimal
+ * string that reads back as the same double), and the ceiling is exact: 1.1
+ * with T = 100, N = 10 gives 11, not the 12 that double arithmetic rounds to.
+ * Host-only.  Returns -1 if T < 1, N < 1 or capacity_factor is not a finite
+ * value > 0.
  * ---------------------------------------------------------------------- */
 int32_t switch_capacity(int64_t T, int32_t N, double capacity_factor);
 

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "kernels.hpp"
@@ -421,11 +422,44 @@ BwdLayout bwd_layout(const switch_moe_desc& d, int32_t C) {
 extern "C" {
 
 int32_t switch_capacity(int64_t T, int32_t N, double capacity_factor) {
-  if (T < 1 || N < 1 || !(capacity_factor > 0.0)) return -1;
-  const double v = std::ceil(capacity_factor * (double)T / (double)N);
-  if (v > (double)T) return (int32_t)(T < INT32_MAX ? T : INT32_MAX);
-  const int32_t c = (int32_t)v;
-  return c < 1 ? 1 : c;
+  if (T < 1 || N < 1 || !(capacity_factor > 0.0) || !std::isfinite(capacity_factor)) return -1;
+  const int32_t cap_t = (int32_t)(T < INT32_MAX ? T : INT32_MAX);
+  // far from both ends the double estimate decides alone
+  const double est = capacity_factor * (double)T / (double)N;
+  if (est > 2.0 * (double)T + 2.0) return cap_t;
+  if (est < 0.25) return 1;
+  // capacity_factor is taken at its decimal value: the shortest decimal string
+  // that reads back as the same double (what a caller wrote, e.g. 1.1, not
+  // 1.100000000000000088817...).  cf = M 10^E, C = ceil(M 10^E T / N), exact.
+  char buf[40];
+  for (int prec = 1; prec <= 17; ++prec) {
+    snprintf(buf, sizeof(buf), "%.*e", prec - 1, capacity_factor);
+    if (std::strtod(buf, nullptr) == capacity_factor) break;
+  }
+  unsigned __int128 M = 0;
+  int digits_after = 0, exp10 = 0;
+  bool after = false;
+  const char* q = buf;
+  for (; *q && *q != 'e' && *q != 'E'; ++q) {
+    if (*q == '.') {
+      after = true;
+    } else if (*q >= '0' && *q <= '9') {
+      M = M * 10 + (unsigned)(*q - '0');
+      if (after) ++digits_after;
+    }
+  }
+  if (*q == 'e' || *q == 'E') exp10 = (int)std::strtol(q + 1, nullptr, 10);
+  const int E = exp10 - digits_after;  // cf = M 10^E, M < 10^17
+  unsigned __int128 num = M * (unsigned __int128)T, den = (unsigned __int128)N;
+  // |E| stays small here: est in [0.25, 2T + 2] with M < 10^17 bounds it
+  if (E >= 0) {
+    for (int i = 0; i < E; ++i) num *= 10;
+  } else {
+    for (int i = 0; i < -E; ++i) den *= 10;
+  }
+  const unsigned __int128 c = (num + den - 1) / den;
+  if (c > (unsigned __int128)cap_t) return cap_t;
+  return c < 1 ? 1 : (int32_t)c;
 }
 
 size_t switch_route_workspace_bytes(int64_t T, int32_t d_model, int32_t N, int32_t dtype) {

@@ -55,9 +55,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64
 // batch 49 -> 46 us.  A layer whose active weights fit the 256 MB memory-side
 // cache (17 experts, 160 MB) loses its reuse across back-to-back launches
 // instead (20.5 -> 25.2 us per launch).
-#ifndef SWM_W_CPOL
-#define SWM_W_CPOL 2
-#endif
+constexpr int kWeightCpol = 2;  // the nt bit of the buffer load's cache-policy operand
 
 __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
@@ -65,11 +63,11 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int vof
 
 // weight stream: read once, so it may carry a streaming cache policy
 __device__ __forceinline__ u32x4 buffer_load16_w(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, SWM_W_CPOL));
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kWeightCpol));
 }
 
 __device__ __forceinline__ u32x2 buffer_load8(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, SWM_W_CPOL));
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kWeightCpol));
 }
 
 
@@ -101,9 +99,6 @@ __device__ __forceinline__ u32x4 pack8(const float (&v)[8], bool relu) {
   return o;
 }
 
-#ifndef SWM_FFN_MINB
-#define SWM_FFN_MINB 2
-#endif
 
 
 // Waves of one workgroup that share a work item along K (1, 2 or 4), the same
@@ -191,11 +186,7 @@ __device__ __forceinline__ void ffn_stream(const uint16_t* __restrict__ A, const
   const int ksteps = K >> 5;
   const int64_t base = (int64_t)n_act * NCB * mch;
   if (base <= 0) return;
-#ifdef SWM_KW_FORCE2
-  const int KW = relu ? waves_per_item(base, (int64_t)gridDim.x * WAVES, WAVES, ksteps) : SWM_KW_FORCE2;
-#else
   const int KW = waves_per_item(base, (int64_t)gridDim.x * WAVES, WAVES, ksteps);
-#endif
   const int groups = WAVES / KW;
   const int g = w / KW, kw = w - g * KW;
   // Workgroups are dealt to the 8 XCDs round-robin (blockIdx % 8).  Each XCD
@@ -384,7 +375,7 @@ __device__ __forceinline__ void ffn_stream(const uint16_t* __restrict__ A, const
 // active (20 per 100 slots: 22.4 against 18.9 us).  The choice needs n_active,
 // so it is taken on the device; JMAX = 4 compiles the 64-column path only.
 template <int MT, int WAVES, int STAGES, int JMAX>
-__global__ __launch_bounds__(WAVES * 64, SWM_FFN_MINB) void ffn_gemm_bf16(
+__global__ __launch_bounds__(WAVES * 64, 2) void ffn_gemm_bf16(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, uint16_t* __restrict__ out,
     const int32_t* __restrict__ kept_count, const int32_t* __restrict__ active, const int32_t* __restrict__ n_active,
     int N, int C, int K, int Ncols, int relu, int mch, const int32_t* __restrict__ gather, int64_t a_rows, int a_tiles,
@@ -441,20 +432,9 @@ __global__ void dense_plan(int32_t* kept, int32_t* active, int32_t* n_active, in
 }
 
 // ----------------------------------------------------------------------------
-#ifndef SWM_FFN_STAGES
-#define SWM_FFN_STAGES 2
-#endif
-#ifndef SWM_FFN_WAVES
-#define SWM_FFN_WAVES 4
-#endif
-#ifndef SWM_FFN_ALLOW128
-#define SWM_FFN_ALLOW128 1
-#endif
-constexpr bool kAllow128 = SWM_FFN_ALLOW128;
-
-#ifndef SWM_HBLK
-#define SWM_HBLK 1
-#endif
+// streaming GEMM launch shape: 4 waves per workgroup, a 2-deep register ring
+constexpr int kStreamWaves = 4;
+constexpr int kStreamStages = 2;
 
 FfnPlan ffn_plan(int N, int C, int d, int dff, int dtype) {
   FfnPlan pl{};
@@ -468,7 +448,7 @@ FfnPlan ffn_plan(int N, int C, int d, int dff, int dtype) {
     // fragment-blocked hidden matrix for the streaming GEMMs: every 16-row tile
     // of every expert is whole, and an expert's block stays under 2^31 bytes
     const int64_t tiles = (int64_t)pl.mch * pl.mt;
-    if (SWM_HBLK && !tiled_ffn_applies(C, d, dff) && tiles * 16 * dff * 2 < ((int64_t)1 << 31)) {
+    if (!tiled_ffn_applies(C, d, dff) && tiles * 16 * dff * 2 < ((int64_t)1 << 31)) {
       pl.h_tiles = (int)tiles;
       h_rows = tiles * 16;
     }
@@ -510,8 +490,8 @@ static hipError_t launch_gemm(const void* A, const void* W, void* out, const int
                               const int32_t* n_active, int N, int C, int K, int Ncols, int relu, int mch,
                               hipStream_t st, const int32_t* gather, int64_t a_rows, int a_tiles, int o_tiles,
                               const ActiveFromKept& afk) {
-  constexpr int kWaves = SWM_FFN_WAVES;
-  auto kern = ffn_gemm_bf16<MT, kWaves, SWM_FFN_STAGES, J>;
+  constexpr int kWaves = kStreamWaves;
+  auto kern = ffn_gemm_bf16<MT, kWaves, kStreamStages, J>;
   const int grid = persistent_grid(reinterpret_cast<const void*>(kern), kWaves * 64);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kWaves * 64), 0, st, static_cast<const uint16_t*>(A),
                      static_cast<const uint16_t*>(W), static_cast<uint16_t*>(out), kept, active, n_active, N, C, K,
@@ -526,7 +506,7 @@ static hipError_t launch_gemm_cols(const void* A, const void* W, void* out, cons
                                    const int32_t* active, const int32_t* n_active, int N, int C, int K, int Ncols,
                                    int relu, int mch, hipStream_t st, const int32_t* gather, int64_t a_rows,
                                    int a_tiles, int o_tiles, const ActiveFromKept& afk) {
-  if constexpr (kAllow128 && MT <= 3) {
+  if constexpr (MT <= 3) {
     if (Ncols % 128 == 0)
       return launch_gemm<MT, 8>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, mch, st, gather, a_rows,
                                 a_tiles, o_tiles, afk);

@@ -287,13 +287,6 @@ static hipError_t launch_dma(const void* A, const void* W, void* out, const int3
   return hipGetLastError();
 }
 
-#ifndef SWM_DMA_R
-#define SWM_DMA_R 5, 8, 2
-#endif
-#ifndef SWM_DMA_D
-#define SWM_DMA_D 4, 8, 3
-#endif
-
 // Tiles need K and Ncols to be multiples of 256 (whole 32-deep steps in
 // groups of 8, whole 128- or 256-column blocks).
 bool tiled_ffn_applies(int C, int d, int dff) { return C > 64 && d % 256 == 0 && dff % 256 == 0; }
@@ -310,10 +303,10 @@ hipError_t launch_tiled_dma(const void* A, const void* W, void* out, const int32
                             const int32_t* n_active, int N, int C, int K, int Ncols, int relu, hipStream_t st,
                             const int32_t* gather, int64_t a_rows) {
   if (C > 128 && C <= 160)
-    return launch_dma<SWM_DMA_R>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st, gather, a_rows);
+    return launch_dma<5, 8, 2>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st, gather, a_rows);
   if (C > 64 && C <= 96)
     return launch_dma<3, 8, 2>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st, gather, a_rows);
-  return launch_dma<SWM_DMA_D>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st, gather, a_rows);
+  return launch_dma<4, 8, 3>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st, gather, a_rows);
 }
 
 }  // namespace swm

@@ -13,6 +13,7 @@ namespace swm {
 struct RoutePlan {
   int split;        // 0: fused kernel; >0: number of k-chunks of the split path
   int tm;           // 16-token tiles per workgroup (fused path)
+  bool kslice;      // fused path with the 4 waves splitting K (long rows, N <= 128)
   int tile_rows;    // tokens per workgroup (= per partial row)
   int64_t nblk;     // number of per-workgroup partial rows
   size_t off_part_p, off_part_cnt, off_logits, bytes;

@@ -292,6 +292,100 @@ __global__ __launch_bounds__(kRouteThreads) void route_fused_bf16(
 }
 
 // ----------------------------------------------------------------------------
+// K-sliced bf16 router for many tokens with long rows (the 16384 x 5120 layer):
+// the 4 waves of a workgroup split K into quarters, and each wave covers every
+// expert tile (N <= 128) of the workgroup's 16 TM tokens.  The fused kernel
+// above splits the expert tiles instead, so all 4 waves stream the same token
+// rows and a CU keeps only (RP - 1) steps x 16 TM x 64 bytes of distinct x in
+// flight; here each wave streams its own quarter of the rows, 4x the distinct
+// bytes in flight per CU for the same ring depth, which is what an HBM-bound
+// read of 16 TM rows x d needs.  One workgroup per CU (the 128 accumulator
+// registers plus a 4-step ring take more than half the register file).  The
+// quarters' partial logits meet in LDS and are summed in wave order, then the
+// shared epilogue runs.
+// ----------------------------------------------------------------------------
+template <int TM, int J>
+__global__ __launch_bounds__(kRouteThreads, 1) void route_kslice_bf16(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg, const float* __restrict__ bias, int64_t T, int d,
+    int N, int32_t* __restrict__ expert_id, float* __restrict__ gate, float* __restrict__ part_p,
+    int32_t* __restrict__ part_cnt, RouteExtra ex) {
+  constexpr int NT = 8;  // expert tiles: N <= 128
+  constexpr int ldl = NT * 16;
+  constexpr int RP = 4;  // register ring depth (RP - 1 steps of loads ahead)
+  extern __shared__ float smem[];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, kg = lane >> 4;
+  const int64_t t0 = (int64_t)blockIdx.x * TM * 16;
+  const int ksteps = d >> 5;
+  const int ks0 = ksteps * w / 4, nks = ksteps * (w + 1) / 4 - ks0;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  const int64_t rows_here = (T - t0) < TM * 16 ? (T - t0) : TM * 16;
+  const __amdgpu_buffer_rsrc_t xres =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x + t0 * d), (short)0, (int)(rows_here * d * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t wres =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(wg), (short)0, (int)((int64_t)N * d * 2), 0x00020000);
+  int a_voff[TM], b_voff[NT];
+#pragma unroll
+  for (int mt = 0; mt < TM; ++mt) {
+    const int r = mt * 16 + c;
+    a_voff[mt] = r < rows_here ? (r * d + kg * 8) * 2 : 0x7ffffff0;
+  }
+#pragma unroll
+  for (int g = 0; g < NT; ++g) {
+    const int n = g * 16 + c;
+    b_voff[g] = n < N ? (n * d + kg * 8) * 2 : 0x7ffffff0;
+  }
+  f32x4 acc[TM][NT];
+#pragma unroll
+  for (int mt = 0; mt < TM; ++mt)
+#pragma unroll
+    for (int g = 0; g < NT; ++g) acc[mt][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 ra[RP][TM], rb[RP][NT];
+  auto load = [&](int slot, int s) {
+    const int so = (ks0 + (s < nks ? s : nks - 1)) * 64;  // past the end: re-read the last step
+#pragma unroll
+    for (int mt = 0; mt < TM; ++mt)
+      ra[slot][mt] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, a_voff[mt], so, 0));
+#pragma unroll
+    for (int g = 0; g < NT; ++g)
+      rb[slot][g] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, b_voff[g], so, 0));
+  };
+#pragma unroll
+  for (int s0 = 0; s0 < RP - 1; ++s0) load(s0, s0);
+  const int kpad = (nks + RP - 1) / RP * RP;
+  for (int it = 0; it < kpad; it += RP) {
+#pragma unroll
+    for (int u = 0; u < RP; ++u) {
+      const int ks = it + u;
+      load((u + RP - 1) % RP, ks + RP - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      const bool live = ks < nks;
+#pragma unroll
+      for (int mt = 0; mt < TM; ++mt) {
+        const u32x4 a = live ? ra[u][mt] : zero;
+#pragma unroll
+        for (int g = 0; g < NT; ++g) acc[mt][g] = mfma_bf16_16x16x32(a, rb[u][g], acc[mt][g]);
+      }
+    }
+  }
+  // the quarters' partial logits, each in its own LDS region, summed in wave order
+  constexpr int REG = TM * 16 * ldl;
+  float* mine = smem + w * REG;
+#pragma unroll
+  for (int mt = 0; mt < TM; ++mt)
+#pragma unroll
+    for (int g = 0; g < NT; ++g)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mine[(mt * 16 + kg * 4 + i) * ldl + g * 16 + c] = acc[mt][g][i];
+  __syncthreads();
+  for (int q = threadIdx.x; q < REG; q += kRouteThreads)
+    smem[q] = ((smem[q] + smem[REG + q]) + smem[2 * REG + q]) + smem[3 * REG + q];
+  __syncthreads();
+  route_epilogue<J>(smem, ldl, TM * 16, t0, T, N, bias, expert_id, gate, part_p, part_cnt, blockIdx.x, ex);
+}
+
+// ----------------------------------------------------------------------------
 // split path: partial logits plog[s][t][n] over k-chunk s
 // ----------------------------------------------------------------------------
 template <int NG>
@@ -681,6 +775,8 @@ RoutePlan route_plan(int64_t T, int d, int N, int dtype) {
     pl.split = 0;
     pl.tm = tm;
     pl.nblk = (T + tm * 16 - 1) / (tm * 16);
+    // K-sliced kernel: long rows (>= 64 k-steps, 16 per wave) and N <= 128
+    pl.kslice = tm >= 2 && N <= 128 && d >= 2048;
   } else if (dtype == 1) {
     // split path: 16-token tiles x S k-chunks for the logits, then one
     // workgroup per token for the chunk sums and the softmax
@@ -718,11 +814,21 @@ static hipError_t launch_route_j(const RoutePlan& pl, const void* x, const void*
     const int NT = (N + 15) / 16;
     const size_t lds = (size_t)pl.tm * 16 * NT * 16 * 4;
     const size_t xl_bytes = (size_t)pl.tm * 16 * d * 2;  // the token rows of a workgroup
-    const bool xl = xl_bytes <= kRouteXlMax;
+    // the XOR swizzle of the staged rows (row & 15 over 16-byte chunks) is a
+    // bijection only when a row holds a multiple of 16 chunks: d % 128 == 0
+    const bool xl = xl_bytes <= kRouteXlMax && d % 128 == 0;
     dim3 grid((unsigned)pl.nblk);
     auto* xb = static_cast<const uint16_t*>(x);
     auto* wb = static_cast<const uint16_t*>(wg);
-    if (pl.tm == 4)
+    if (pl.kslice) {
+      const size_t klds = (size_t)4 * pl.tm * 16 * 128 * 4;  // four quarters' partial logits
+      if (pl.tm == 4)
+        hipLaunchKernelGGL((route_kslice_bf16<4, J>), grid, dim3(kRouteThreads), klds, st, xb, wb, bias, T, d, N,
+                           expert_id, gate, part_p, part_cnt, ex);
+      else
+        hipLaunchKernelGGL((route_kslice_bf16<2, J>), grid, dim3(kRouteThreads), klds, st, xb, wb, bias, T, d, N,
+                           expert_id, gate, part_p, part_cnt, ex);
+    } else if (pl.tm == 4)
       hipLaunchKernelGGL((route_fused_bf16<4, 2, J, false>), grid, dim3(kRouteThreads), lds, st, xb, wb, bias, T, d, N,
                          expert_id, gate, part_p, part_cnt, ex);
     else if (pl.tm == 2)

@@ -34,6 +34,26 @@ def test_capacity(L):
     assert L.switch_capacity(10, 1, 5.0) == 10  # clamped to T
 
 
+def test_capacity_decimal_rule_matches_oracle(L):
+    """C = max(1, ceil(cf T / N)) on the decimal value of cf, as the oracle
+    computes it (exact rationals); double arithmetic would round 1.1 * 100 / 10
+    up to 12."""
+    import oracle
+    from oracle import routing as orr
+    assert L.switch_capacity(100, 10, 1.1) == oracle.capacity(100, 10, 1.1) == 11
+    assert L.switch_capacity(100, 2, 1.1) == oracle.capacity(100, 2, 1.1) == 55
+    assert L.switch_capacity(30, 10, 0.7) == oracle.capacity(30, 10, 0.7) == 3
+    cfs = [0.1, 0.2, 0.3, 0.5, 0.7, 0.8, 0.9, 1.0, 1.1, 1.2, 1.25, 1.3, 1.5, 1.7, 2.0, 2.2, 3.3, 0.05, 1.15, 1.35]
+    for cf in cfs:
+        for T in (1, 7, 10, 30, 100, 128, 1000, 4096, 16384, 100_000):
+            for N in (1, 2, 3, 7, 8, 10, 128, 384, 1000):
+                want = min(T, oracle.capacity(T, N, cf))
+                assert L.switch_capacity(T, N, cf) == want, (T, N, cf)
+                assert min(T, orr.capacity_topk(T, N, 1, cf)) == want
+    assert L.switch_capacity(10, 8, float("nan")) == -1
+    assert L.switch_capacity(10, 8, float("inf")) == -1
+
+
 def test_status_strings(L):
     for s in range(7):
         assert L.switch_status_str(s)

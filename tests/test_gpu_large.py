@@ -5,11 +5,14 @@ d_ff=8192, N=128, cf=1.25 -> C=160, plus one always-on dense FFN of width
 The routed and shared weights (~22 GB of bf16) are drawn on the device with
 torch's seeded generator; x and W_g are drawn on the host and conditioned to a
 top-2 logit margin >= 1e-3.  Routing, load statistics, slots and counts are
-checked in full against the fp64 oracle; the layer output is checked on every
-kept token of a seeded sample of experts and on a sample of dropped tokens,
-with the oracle evaluating those tokens one expert at a time from the
+checked in full against the fp64 oracle; the layer output is checked on the
+first and the last kept slot of every one of the 128 experts and on 1024
+seeded tokens across the batch (kept or dropped), each including the shared
+term, with the oracle evaluating those tokens one expert at a time from the
 weights copied back to the host.
 """
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -54,21 +57,33 @@ def test_large_shared_layer():
     check_slots(out, ref)
 
     print("[case] switch-large-shared: sampled outputs", flush=True)
+    # every active expert's first and last kept slot, plus 1024 seeded tokens
+    # across the batch (kept or dropped), each with the shared term
+    slot = ref["slot"]
+    tos, kc = ref["token_of_slot"], ref["kept_count"]
+    ends = [tos[i, j] for i in ref["active"] for j in {0, int(kc[i]) - 1}]
     rng = np.random.default_rng(123)
-    experts = rng.choice(ref["active"], size=4, replace=False)
-    dropped = np.nonzero(ref["slot"] < 0)[0]
-    drop_sample = rng.choice(dropped, size=min(32, dropped.size), replace=False) if dropped.size else dropped
-    toks = np.concatenate([np.nonzero((e == i) & (ref["slot"] >= 0))[0] for i in experts] + [drop_sample])
-    ws1 = _host_bf16(W["ws1"])
-    ws2 = _host_bf16(W["ws2"])
-    shared = oracle.ffn(xf[toks], ws1, ws2)
-    del ws1, ws2
-    yref = xf[toks] + shared  # dropped tokens: x + shared term
-    for i in experts:
-        sel = np.nonzero(e[toks] == i)[0]
-        sel = sel[ref["slot"][toks[sel]] >= 0]
-        o = oracle.ffn(xf[toks[sel]], _host_bf16(W["w1"][i]), _host_bf16(W["w2"][i]))
-        yref[sel] = g[toks[sel], None] * o + shared[sel]
+    toks = np.unique(np.concatenate([np.asarray(ends, dtype=np.int64),
+                                     rng.choice(wl.T, size=1024, replace=False)]))
+    assert len(ref["active"]) == wl.N
     y = host(out["y"])[toks]
+    yref = xf[toks].copy()  # dropped tokens: x + shared term
+    shared = oracle.ffn(xf[toks], _host_bf16(W["ws1"]), _host_bf16(W["ws2"]))
+    W1, W2 = W["w1"], W["w2"]
+
+    def one(i):
+        sel = np.nonzero((e[toks] == i) & (slot[toks] >= 0))[0]
+        if sel.size == 0:
+            return sel, None
+        w1h = W1[i].detach().cpu().view(torch.int16).numpy().view(np.uint16)
+        w2h = W2[i].detach().cpu().view(torch.int16).numpy().view(np.uint16)
+        return sel, oracle.ffn(xf[toks[sel]], oracle.widen(w1h, "bf16"), oracle.widen(w2h, "bf16"))
+
+    with ThreadPoolExecutor(8) as ex:
+        for sel, o in ex.map(one, range(wl.N)):
+            if o is not None:
+                yref[sel] = g[toks[sel], None] * o
+    yref += shared
     r = row_rel(y, yref)
     assert r.max() <= TOL_OUT["bf16"], f"max row rel err {r.max():.3g} (token {toks[r.argmax()]})"
+    print(f"[case] switch-large-shared: {toks.size} tokens checked, max row rel err {r.max():.3g}", flush=True)

@@ -1,0 +1,51 @@
+"""GPU parity of the router kernels beyond the workload configs, through the C
+ABI (switch_route) against the fp64 oracle ("Top-1 Routing" page, Core
+mechanism and Load balancing).
+
+* d_model a multiple of 32 but not of 128, at token counts where the router
+  would stage a workgroup's rows in LDS (T = 4096): the staging's swizzle
+  needs d % 128 == 0, so these shapes must take the streaming path and still
+  match;
+* the K-sliced kernel (many tokens, rows of >= 2048 elements, N <= 128) at
+  both tile heights (32 and 64 tokens per workgroup), with a ragged last
+  tile and N not a multiple of 16.
+Expert ids and counts bit-exact, gate / P / L_aux at the router tolerances.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests import inputs_util
+from tests.gpu_util import check_routing, dev
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # (T, d_model, N, bias_scale)
+    (4096, 96, 64, 0.0),      # one 16-token tile per workgroup, 3 k-steps
+    (4096, 160, 40, 1.0),     # 5 k-steps, N ragged, Zipf-like bias
+    (8200, 2048, 100, 0.0),   # K-sliced, 32 tokens per workgroup, last tile 8 tokens
+    (16400, 2048, 128, 1.0),  # K-sliced, 64 tokens per workgroup, last tile 16 tokens
+    (8192, 4096, 128, 0.0),   # K-sliced, 32 tokens per workgroup, 128 k-steps
+]
+
+
+@pytest.mark.parametrize("T,d,N,bias_scale", CASES)
+def test_route_shapes(T, d, N, bias_scale):
+    import switch_top_routed_amd as sw
+
+    wl = workloads.Workload(f"route-{T}x{d}x{N}", T, d, 4 * d, N, 1.0, "bf16", 1.0 / math.sqrt(d),
+                            bias_scale=bias_scale, seed=20_000 + T + d + N)
+    print(f"[case] route T={T} d={d} N={N} bias={bias_scale}", flush=True)
+    inp = inputs_util.conditioned_inputs(wl, weights=False)
+    _, p, e, g = inputs_util.stored_router(inp)
+    cnt, f, P, l_aux = oracle.aux_loss(e, p, N)
+    ref = dict(expert_id=e, gate=g, routed_count=cnt, f=f, P=P, l_aux=l_aux)
+    bias = None if inp.bias is None else torch.from_numpy(inp.bias).cuda()
+    o = sw.switch_route(dev(inp.x, "bf16"), dev(inp.w_gate, "bf16"), bias)
+    torch.cuda.synchronize()
+    check_routing(o, ref, N)
