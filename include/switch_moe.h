@@ -327,6 +327,24 @@ switch_status switch_moe_forward_timed(const switch_moe_desc* desc, const switch
                                        const switch_moe_outputs* out, void* ws, size_t ws_bytes, void* stream,
                                        void* const* stage_events);
 
+/* switch_moe_forward for callers that cannot allocate device memory (code
+   under HIP graph capture, tight serving loops, harnesses that forbid
+   hipMalloc): the same launches, outputs, validation and errors, with the
+   workspace taken from a library-owned device array of
+   switch_moe_noalloc_max_bytes() bytes (64 MiB) instead of an argument.  The
+   array is resident on every GPU the library runs on, from its first use
+   until the process ends; this call allocates nothing (no hipMalloc, no
+   hipFree, no allocating library routine).  A layer whose workspace
+   (switch_moe_workspace_bytes) exceeds the array is rejected with
+   SWITCH_E_WORKSPACE before anything is enqueued.  All calls on one GPU
+   share its array, which keeps the last call's contents: calls that overlap
+   on one GPU (two streams or threads) race and must be serialised by the
+   caller.  Not for training (no saved tensors). */
+switch_status switch_moe_forward_noalloc(const switch_moe_desc* desc, const switch_moe_inputs* in,
+                                         const switch_moe_outputs* out, void* stream);
+/* size of the array behind switch_moe_forward_noalloc, in bytes */
+size_t switch_moe_noalloc_max_bytes(void);
+
 /* ------------------------------------------------------------------------
  * Training: the forward that keeps what the backward needs, and the
  * backward pass of the whole layer.

@@ -718,6 +718,20 @@ static switch_status moe_forward(const switch_moe_desc* desc, const switch_moe_i
   return ok();
 }
 
+namespace swm {
+switch_status abi_forward(const switch_moe_desc* desc, const switch_moe_inputs* in, const switch_moe_outputs* out,
+                          void* ws, size_t ws_bytes, void* stream) {
+  return moe_forward(desc, in, out, ws, ws_bytes, stream, nullptr);
+}
+switch_status abi_forward_bytes(const switch_moe_desc* desc, size_t* bytes) {
+  int32_t C = 0;
+  TRY(validate_desc(desc, &C));
+  *bytes = fwd_layout(*desc, C).bytes;
+  return SWITCH_OK;
+}
+switch_status abi_fail(switch_status s, const char* msg) { return fail(s, "%s", msg); }
+}  // namespace swm
+
 extern "C" {
 
 switch_status switch_moe_forward(const switch_moe_desc* desc, const switch_moe_inputs* in,

@@ -223,4 +223,13 @@ hipError_t launch_shared_bwd_dense(const void* x, const void* dy, const void* ws
 
 inline size_t align_up(size_t v, size_t a = 256) { return (v + a - 1) / a * a; }
 
+// ---------------- C ABI internals shared by the entry-point sources ----------------
+// switch_moe_forward itself (validation, then the launches on `ws`)
+switch_status abi_forward(const switch_moe_desc* desc, const switch_moe_inputs* in, const switch_moe_outputs* out,
+                          void* ws, size_t ws_bytes, void* stream);
+// validates desc; *bytes = the forward's workspace size
+switch_status abi_forward_bytes(const switch_moe_desc* desc, size_t* bytes);
+// sets the thread-local message of switch_last_error and returns s
+switch_status abi_fail(switch_status s, const char* msg);
+
 }  // namespace swm

@@ -73,6 +73,9 @@ _SIGS = {
                                   ctypes.POINTER(SwitchMoeOutputs), _vp, _sz, _vp]),
     "switch_moe_forward_timed": (_i32, [ctypes.POINTER(SwitchMoeDesc), ctypes.POINTER(SwitchMoeInputs),
                                         ctypes.POINTER(SwitchMoeOutputs), _vp, _sz, _vp, ctypes.POINTER(_vp)]),
+    "switch_moe_forward_noalloc": (_i32, [ctypes.POINTER(SwitchMoeDesc), ctypes.POINTER(SwitchMoeInputs),
+                                          ctypes.POINTER(SwitchMoeOutputs), _vp]),
+    "switch_moe_noalloc_max_bytes": (_sz, []),
     "switch_moe_forward_train": (_i32, [ctypes.POINTER(SwitchMoeDesc), ctypes.POINTER(SwitchMoeInputs),
                                         ctypes.POINTER(SwitchMoeOutputs), ctypes.POINTER(SwitchMoeSaved), _vp, _sz,
                                         _vp]),
@@ -353,16 +356,21 @@ class SwitchMoE:
                               dws2=_empty((d_ff_shared, d_model), wdt, dev) if d_ff_shared else None)
 
     def __call__(self, x, w_gate, w1, w2, bias=None, ws1=None, ws2=None, stream=None, stage_events=None,
-                 w1_scale=None, w2_scale=None):
+                 w1_scale=None, w2_scale=None, noalloc=False):
         """One layer forward.  stage_events: optional StageEvents (7 HIP events) recorded at the stage
         boundaries (switch_moe_forward_timed).  MXFP4 weights: w1 / w2 are the codes and
-        w1_scale / w2_scale the E8M0 scales (switch_quantize_mxfp4)."""
+        w1_scale / w2_scale the E8M0 scales (switch_quantize_mxfp4).  noalloc: call
+        switch_moe_forward_noalloc (the library's own scratch array instead of self.ws)."""
         ins = SwitchMoeInputs(x.data_ptr(), w_gate.data_ptr(), None if bias is None else bias.data_ptr(),
                               w1.data_ptr(), w2.data_ptr(), None if ws1 is None else ws1.data_ptr(),
                               None if ws2 is None else ws2.data_ptr(),
                               None if w1_scale is None else w1_scale.data_ptr(),
                               None if w2_scale is None else w2_scale.data_ptr())
-        if stage_events is None:
+        if noalloc:
+            _check("switch_moe_forward_noalloc",
+                   lib().switch_moe_forward_noalloc(ctypes.byref(self.desc), ctypes.byref(ins),
+                                                    ctypes.byref(self._outs), _stream(stream)))
+        elif stage_events is None:
             _check("switch_moe_forward", lib().switch_moe_forward(ctypes.byref(self.desc), ctypes.byref(ins),
                                                                   ctypes.byref(self._outs), _p(self.ws),
                                                                   self.ws.numel(), _stream(stream)))
