@@ -65,13 +65,13 @@ FFN_SOURCES = ("switch_top_routed_amd/csrc/expert_ffn.hip", "switch_top_routed_a
 # profiles/*_hbm_traffic.md.
 TRAFFIC = {
     "switch-base-uniform": {
-        "sources_sha256": "533499f2a76a80bf41b470834ada78ebd22318b8af21b9e1e25403c5005574ee",
-        "fetch_kib": [305818.0, 315590.0], "write_kib": [24109.0, 6027.0],
+        "sources_sha256": "0d519c177a34f984ce871c158551c41b333b8582de73f98cd133de1c504359df",
+        "fetch_kib": [305815.0, 315422.0], "write_kib": [24109.0, 6027.0],
         "fetch_scale": 2.0, "write_scale": 1.0,
     },
     "switch-large-shared": {
-        "sources_sha256": "533499f2a76a80bf41b470834ada78ebd22318b8af21b9e1e25403c5005574ee",
-        "fetch_kib": [5329371.0, 5498002.0], "write_kib": [262272.0, 163840.0],
+        "sources_sha256": "0d519c177a34f984ce871c158551c41b333b8582de73f98cd133de1c504359df",
+        "fetch_kib": [5345023.0, 5420117.0], "write_kib": [262145.0, 163840.0],
         "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
@@ -94,6 +94,11 @@ BWD_TRAFFIC = {
 }
 
 
+def say(msg):
+    """Progress line on stderr (stdout carries only the JSON record)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -112,6 +117,9 @@ def parse():
                     help="expert weights in the layer dtype, or MXFP4 (quantized on the device before timing)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the layer backward measurement")
+    ap.add_argument("--grad-accumulate", action="store_true",
+                    help="backward with SWITCH_ACCUM_EXPERT_GRADS: the routed experts' weight gradients accumulate "
+                         "into the gradient buffers and idle experts are not touched")
     ap.add_argument("--backward-steps", type=int, default=None,
                     help="timed backward steps (default: min(steps, 50); 5 with a shared expert)")
     ap.add_argument("--stage-steps", type=int, default=20, help="extra steps with every stage boundary timed")
@@ -150,6 +158,7 @@ def main():
                           "requested_gpus": args.gpus}), flush=True)
         sys.exit(2)
 
+    helper = None if (args.calibrate_copy or args.sources_sha) else clock_helper()  # before the GPU is touched
     import numpy as np
     import torch
 
@@ -179,6 +188,7 @@ def main():
     esz = 2 if wl.dtype == "bf16" else 4
     weight_bytes = 2 * wl.N * wl.d_model * wl.d_ff * esz
     on_device = weight_bytes > (4 << 30)  # draw very large weight sets on the GPU
+    say(f"inputs for {wl.name}")
     inp = workloads.make_inputs(wl, weights=not on_device)
 
     def dev(a):
@@ -219,8 +229,10 @@ def main():
         layer(x, wg, w1, w2, bias=bias, ws1=ws1, ws2=ws2, stream=stream, stage_events=ev, w1_scale=w1s,
               w2_scale=w2s)
 
+    say("warmup")
     for _ in range(args.warmup):
         step()
+    say(f"{args.steps} timed steps")
     # every ffn_event_every-th timed step records the two events around the routed FFN (each
     # event record costs ~2.5 us of GPU time, so they are not put into every step); the other
     # timed steps run the plain forward.  One torch event per step boundary gives the per-step
@@ -242,7 +254,7 @@ def main():
     bounds[args.steps].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    clocks = gpu_clocks()
+    clocks = gpu_clocks(helper)
     if ends is not None:
         step_ms = [bounds[i].elapsed_time(ends[i]) for i in range(args.steps)]
     else:
@@ -354,6 +366,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
+        say("cpu baseline")
         if on_device:
             cpu = cpu_baseline_sampled(inp, {"w1": w1, "w2": w2, "ws1": ws1, "ws2": ws2}, layer.C,
                                        args.cpu_seconds)
@@ -363,6 +376,7 @@ def main():
 
     backward = None
     if not args.no_backward and not variant and not mxw and not xd:  # the backward: top-1, native weights
+        say("backward")
         backward = measure_backward(args, wl, inp, layer.C, x, wg, w1, w2, bias, ws1, ws2, stream, on_device)
 
     line = {
@@ -404,31 +418,73 @@ def host_info():
     return {"cpu_model": model, "affinity_cores": cores}
 
 
-def gpu_clocks():
-    """Current GPU clocks as amd-smi reports them right after the timed steps
-    (best effort: None when the tool is missing or prints nothing usable)."""
+_CLOCK_HELPER = r"""
+import json, subprocess, sys
+sys.stdin.readline()  # asked for the clocks once the timed steps are done
+out = None
+for cmd in (["amd-smi", "metric", "-g", "0", "--clock", "--json"], ["amd-smi", "metric", "--clock", "--json"]):
+    try:
+        r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
+    except (OSError, subprocess.TimeoutExpired):
+        continue
+    if r.returncode == 0 and r.stdout.strip():
+        out = r.stdout
+        break
+print(json.dumps(out))
+"""
+
+
+def clock_helper():
+    """A child process that runs amd-smi when asked.  It is started before this
+    process touches the GPU, so the tool it starts is never launched from a
+    process that holds a GPU context.  None under a profiler (whose preloaded
+    library initialises the GPU in every child) or when it cannot start."""
     import subprocess
-    for cmd in (["amd-smi", "metric", "-g", "0", "--clock", "--json"], ["amd-smi", "metric", "--clock", "--json"]):
-        try:
-            r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
-        except (OSError, subprocess.TimeoutExpired):
-            continue
-        if r.returncode != 0 or not r.stdout.strip():
-            continue
-        try:
-            data = json.loads(r.stdout)
-        except ValueError:
-            return {"raw": r.stdout[:400]}
-        if isinstance(data, list) and data:
-            data = data[0]
-        clk = data.get("clock", data) if isinstance(data, dict) else {}
-        picked = {}
-        if isinstance(clk, dict):
-            for k, v in clk.items():
-                if k.lower().startswith(("gfx_0", "mem_0", "fclk_0", "socclk_0")) and isinstance(v, dict):
-                    picked[k] = {kk: v.get(kk) for kk in ("clk", "min_clk", "max_clk") if kk in v}
-        return picked or {"raw": json.dumps(clk)[:400]}
-    return None
+    if any(k.startswith("ROCPROF") for k in os.environ) or "rocprof" in os.environ.get("LD_PRELOAD", ""):
+        return None
+    try:
+        return subprocess.Popen([sys.executable, "-c", _CLOCK_HELPER], stdin=subprocess.PIPE, stdout=subprocess.PIPE,
+                                stderr=subprocess.DEVNULL, text=True)
+    except OSError:
+        return None
+
+
+def gpu_clocks(helper):
+    """Current GPU clocks as amd-smi reports them right after the timed steps
+    (best effort: None when the helper is missing or prints nothing usable)."""
+    if helper is None:
+        return None
+    try:
+        raw, _ = helper.communicate("go\n", timeout=60)
+        raw = json.loads(raw.strip() or "null")
+    except Exception:  # noqa: BLE001 -- the clocks are informative only
+        helper.kill()
+        return None
+    if not raw:
+        return None
+    try:
+        data = json.loads(raw)
+    except ValueError:
+        return {"raw": raw[:400]}
+    if isinstance(data, dict) and isinstance(data.get("gpu_data"), list):
+        data = data["gpu_data"]
+    if isinstance(data, list) and data:
+        data = data[0]
+    clk = data.get("clock", data) if isinstance(data, dict) else {}
+
+    def mhz(v):
+        return v.get("value") if isinstance(v, dict) else v
+    picked = {}
+    if isinstance(clk, dict):
+        for k, v in clk.items():
+            if isinstance(v, dict) and k.lower().startswith(("gfx_", "mem_", "fclk_", "socclk_")):
+                picked[k] = mhz(v.get("clk"))
+    if picked:
+        gfx = [x for k, x in picked.items() if k.startswith("gfx_") and isinstance(x, (int, float))]
+        return {"MHz": picked, "gfx_mean_MHz": sum(gfx) / len(gfx) if gfx else None,
+                "note": "amd-smi right after the timed steps (the GPU may already be idling); the clock each kernel "
+                        "ran at is in the MFMA counter profiles (GRBM_GUI_ACTIVE / time)"}
+    return {"raw": json.dumps(clk)[:400]}
 
 
 def measure_backward(args, wl, inp, C, x, wg, w1, w2, bias, ws1, ws2, stream, on_device):
@@ -448,7 +504,7 @@ def measure_backward(args, wl, inp, C, x, wg, w1, w2, bias, ws1, ws2, stream, on
     T, d, F, N = wl.T, wl.d_model, wl.d_ff, wl.N
     tl = sw.SwitchMoE(T, d, F, N, dtype=dt, capacity_factor=wl.capacity_factor, priority=wl.priority,
                       gate_scale=wl.gate_scale, residual_all=wl.residual_all, d_ff_shared=wl.d_ff_shared,
-                      train=True)
+                      train=True, accumulate_expert_grads=args.grad_accumulate)
     tl.forward_train(x, wg, w1, w2, bias=bias, ws1=ws1, ws2=ws2, stream=stream)
     g = torch.Generator(device="cuda")
     g.manual_seed(wl.seed + 17)
@@ -492,7 +548,8 @@ def measure_backward(args, wl, inp, C, x, wg, w1, w2, bias, ws1, ws2, stream, on
     kname = ("bwd_expert_fused" if fused else "gemm_generic") + f" ({'w2' if dom == 'w2_pass' else 'w1'} pass)"
     out = {
         "value": T * steps / elapsed, "unit": "tokens/s", "ms_per_step": elapsed / steps * 1e3, "steps": steps,
-        "step": "one layer backward (switch_moe_backward) after a training forward on the same batch",
+        "step": "one layer backward (switch_moe_backward) after a training forward on the same batch"
+                + (", expert weight gradients accumulated (idle experts untouched)" if args.grad_accumulate else ""),
         "dl_aux": workloads.DL_AUX,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,

@@ -84,6 +84,18 @@ typedef enum switch_priority {
 /* Top-K only: divide each token's K gates by their sum (the gate of choice j
  * is otherwise p[t, e_tj], the top-1 definition applied to every choice). */
 #define SWITCH_RENORM 4u
+/* Backward only: the routed experts' weight gradients accumulate into the
+ * caller's dw1 / dw2 (dW[e] += dL/dW[e], the fp32 sum of the stored bf16
+ * value and the new one, rounded once) instead of overwriting them.  An
+ * expert that kept no token has a zero gradient and is not touched at all,
+ * which spares a layer with many idle experts (the 384-expert decode batch)
+ * the write of their zeros.  Gradient accumulation over several batches is
+ * the use ([CAP] training-step flowchart: the step backpropagates into the
+ * experts); every other output is written as without the flag.  Needs the
+ * fused bf16 expert backward (C <= 160, d_model and d_ff multiples of 64):
+ * otherwise switch_moe_backward returns SWITCH_E_UNSUPPORTED.  The forward
+ * ignores it. */
+#define SWITCH_ACCUM_EXPERT_GRADS 8u
 
 /* Routing ("Top-1 Routing" page, Variants: token choice, where each token
  * picks its top-K experts, and expert choice, where each expert picks its top

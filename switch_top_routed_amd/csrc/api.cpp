@@ -306,7 +306,7 @@ switch_status validate_desc(const switch_moe_desc* d, int32_t* C) {
     return fail(SWITCH_E_SHAPE, "d_model * d_ff (or d_ff_shared) exceeds 2^30");
   if (d->priority != SWITCH_TOKEN_ORDER && d->priority != SWITCH_GATE_DESC)
     return fail(SWITCH_E_UNSUPPORTED, "priority %d is not supported", d->priority);
-  if (d->flags & ~(SWITCH_GATE_SCALE | SWITCH_RESIDUAL_ALL | SWITCH_RENORM))
+  if (d->flags & ~(SWITCH_GATE_SCALE | SWITCH_RESIDUAL_ALL | SWITCH_RENORM | SWITCH_ACCUM_EXPERT_GRADS))
     return fail(SWITCH_E_UNSUPPORTED, "unknown flag bits 0x%x", d->flags);
   if (d->routing != SWITCH_TOKEN_CHOICE && d->routing != SWITCH_EXPERT_CHOICE)
     return fail(SWITCH_E_UNSUPPORTED, "routing %d is not supported", d->routing);
@@ -809,6 +809,10 @@ static switch_status moe_backward(const switch_moe_desc* desc, const switch_moe_
     REQUIRE_ALIGN(grads->dws2, 16);
   }
   const BwdLayout L = bwd_layout(d, C);
+  const bool accum = (d.flags & SWITCH_ACCUM_EXPERT_GRADS) != 0;
+  if (accum && !L.fused)
+    return fail(SWITCH_E_UNSUPPORTED,
+                "SWITCH_ACCUM_EXPERT_GRADS needs the fused bf16 expert backward (C <= 160, d and d_ff multiples of 64)");
   TRY(check_ws(ws, ws_bytes, L.bytes));
   char* w = static_cast<char*>(ws);
   hipStream_t st = as_stream(stream);
@@ -853,7 +857,8 @@ static switch_status moe_backward(const switch_moe_desc* desc, const switch_moe_
     A.C = C;
     A.d = dm;
     A.dff = dff;
-    BWD_TRY(launch_zero_idle_experts(A, st), "switch_moe_backward/zero");
+    A.accum = accum ? 1 : 0;
+    if (!accum) BWD_TRY(launch_zero_idle_experts(A, st), "switch_moe_backward/zero");
     BWD_TRY(mark(1), "switch_moe_backward/event");
     BWD_TRY(launch_expert_bwd_pass(A, 2, st), "switch_moe_backward/w2_pass");
     BWD_TRY(mark(2), "switch_moe_backward/event");

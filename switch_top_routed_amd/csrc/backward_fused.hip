@@ -30,6 +30,9 @@
 //    consecutive elements); the weight-gradient tile is computed transposed and
 //    passes through LDS so that its stores write whole 128-byte rows.
 // Rows m at or beyond kept_count are zero in LDS and never stored.
+// ACC (the caller's accumulate flag): each weight-gradient piece is added to
+// what the buffer holds (fp32 sum of the two bf16 values, rounded once) instead
+// of overwriting it; experts that kept no token are not visited at all.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -67,7 +70,7 @@ constexpr int kBwdXcds = 8;
 // MODE 2: pass over W2 (epilogue dZ, dg partials); MODE 1: pass over W1
 // (epilogue dX_e).  MT = 16-row tiles of m (kept <= 16 MT); MQ = m rows in LDS
 // (a multiple of 32: whole MFMA k-steps for the weight gradient).
-template <int MT, int MODE, int STAGES>
+template <int MT, int MODE, int STAGES, bool ACC>
 __global__ __launch_bounds__(256, 2) void bwd_expert_fused(
     const uint16_t* __restrict__ Wt, int rows, int cols,
     const uint16_t* __restrict__ Q, const int32_t* __restrict__ q_gather,      // Q rows: gathered or [N][C][cols]
@@ -241,8 +244,15 @@ __global__ __launch_bounds__(256, 2) void bwd_expert_fused(
 #pragma unroll
           for (int hlf = 0; hlf < 2; ++hlf) {
             const int row = 8 * hlf + (lane >> 3), q = lane & 7;
-            const u32x4 v = *reinterpret_cast<const u32x4*>(gs + row * 144 + q * 16);
-            *reinterpret_cast<u32x4*>(gbase + (int64_t)row * cols + ch * 64 + q * 8) = v;
+            u32x4 v = *reinterpret_cast<const u32x4*>(gs + row * 144 + q * 16);
+            uint16_t* gp = gbase + (int64_t)row * cols + ch * 64 + q * 8;
+            if constexpr (ACC) {  // accumulate: the stored gradient plus this one, summed in fp32
+              const u32x4 old = *reinterpret_cast<const u32x4*>(gp);
+#pragma unroll
+              for (int u = 0; u < 4; ++u)
+                v[u] = pack_bf2(bf2f(old[u] & 0xffffu) + bf2f(v[u] & 0xffffu), bf2f(old[u] >> 16) + bf2f(v[u] >> 16));
+            }
+            *reinterpret_cast<u32x4*>(gp) = v;
           }
         }
         if (ch + 1 < nch) store_q(qn, (ch + 1) & 1);
@@ -315,24 +325,29 @@ bool fused_expert_bwd_applies(int64_t T, int C, int d, int dff) {
   return C <= 160 && d % 64 == 0 && dff % 64 == 0 && T * d * 2 < ((int64_t)1 << 31);
 }
 
-template <int MT, int MODE>
-static hipError_t launch_fused_mt(const ExpertBwdArgs& A, hipStream_t st) {
+template <int MT, int MODE, bool ACC>
+static hipError_t launch_fused_acc(const ExpertBwdArgs& A, hipStream_t st) {
   const int rows = MODE == 2 ? A.dff : A.d, cols = MODE == 2 ? A.d : A.dff;
   int64_t grid = (int64_t)A.N * (rows / 64);
   grid = (grid + kBwdXcds - 1) / kBwdXcds * kBwdXcds;
   const auto* W = static_cast<const uint16_t*>(MODE == 2 ? A.w2 : A.w1);
   if (MODE == 2)
-    hipLaunchKernelGGL((bwd_expert_fused<MT, 2, 3>), dim3((unsigned)grid), dim3(256), 0, st, W, rows, cols,
+    hipLaunchKernelGGL((bwd_expert_fused<MT, 2, 3, ACC>), dim3((unsigned)grid), dim3(256), 0, st, W, rows, cols,
                        static_cast<const uint16_t*>(A.dy), A.tos, static_cast<const uint16_t*>(A.h), nullptr,
                        A.gate, static_cast<uint16_t*>(A.dw2), static_cast<uint16_t*>(A.dz),
                        static_cast<const uint16_t*>(A.h), A.dgp, nullptr, A.kept, A.active, A.n_active, A.tos, A.N,
                        A.C, A.T);
   else
-    hipLaunchKernelGGL((bwd_expert_fused<MT, 1, 3>), dim3((unsigned)grid), dim3(256), 0, st, W, rows, cols,
+    hipLaunchKernelGGL((bwd_expert_fused<MT, 1, 3, ACC>), dim3((unsigned)grid), dim3(256), 0, st, W, rows, cols,
                        static_cast<const uint16_t*>(A.dz), nullptr, static_cast<const uint16_t*>(A.x), A.tos,
                        nullptr, static_cast<uint16_t*>(A.dw1), nullptr, nullptr, nullptr, A.dxe, A.kept, A.active,
                        A.n_active, A.tos, A.N, A.C, (int64_t)0);
   return hipGetLastError();
+}
+
+template <int MT, int MODE>
+static hipError_t launch_fused_mt(const ExpertBwdArgs& A, hipStream_t st) {
+  return A.accum ? launch_fused_acc<MT, MODE, true>(A, st) : launch_fused_acc<MT, MODE, false>(A, st);
 }
 
 template <int MODE>

@@ -62,6 +62,10 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, unsigned char* lds, int voff, int soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
 }
+// the same with the non-temporal cache policy (bytes read once per launch)
+__device__ __forceinline__ void dma16_nt(__amdgpu_buffer_rsrc_t r, unsigned char* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 2);
+}
 __device__ __forceinline__ u32x2 lds_read_tr16(const unsigned char* lds) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)lds));
 }
@@ -69,9 +73,11 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const unsigned char* lds) {
 }  // namespace
 
 // MTW m-tiles x NJ n-tiles of 16 x 16 per wave (2 x 2 waves): a BM = 32 MTW
-// by TN = 32 NJ tile; S LDS stages.
-template <int MTW, int NJ, int S>
-__global__ __launch_bounds__(256, 2) void ffn_tile_dma(
+// by TN = 32 NJ tile; S LDS stages.  WNT: the weights are read once per launch
+// (one m-chunk per expert), so their loads carry the non-temporal policy and
+// leave the caches to the token rows, which every column block re-reads.
+template <int MTW, int NJ, int S, bool WNT>
+__global__ __launch_bounds__(256, MTW * NJ >= 48 ? 1 : 2) void ffn_tile_dma(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, uint16_t* __restrict__ out,
     const int32_t* __restrict__ kept_count, const int32_t* __restrict__ active, const int32_t* __restrict__ n_active,
     int N, int C, int K, int Ncols, int relu, int mch, const int32_t* __restrict__ gather, int64_t a_rows) {
@@ -160,7 +166,10 @@ __global__ __launch_bounds__(256, 2) void ffn_tile_dma(
     for (int i = 0; i < LW; ++i) {
       const __amdgpu_buffer_rsrc_t rs = is_a[i] ? ares : wres;
       const int so = sc * (is_a[i] ? a_step : w_step);
-      dma16(rs, base + lds_blk[i], voff[i], so);
+      if (WNT && !is_a[i])
+        dma16_nt(rs, base + lds_blk[i], voff[i], so);
+      else
+        dma16(rs, base + lds_blk[i], voff[i], so);
     }
   };
 
@@ -186,6 +195,11 @@ __global__ __launch_bounds__(256, 2) void ffn_tile_dma(
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // 16-row m-tiles of this wave that hold a filled slot: an expert with fewer
+  // rows than the tile skips the MFMAs (and A reads) of its empty m-tiles
+  int live_mt = (rows - wm * (BM / 2) + 15) >> 4;
+  live_mt = live_mt < 0 ? 0 : live_mt > MTW ? MTW : live_mt;
+  live_mt = __builtin_amdgcn_readfirstlane(live_mt);
   auto compute = [&](int st) {
     const unsigned char* base = stage(st);
     u32x4 bf[NJ];
@@ -196,9 +210,11 @@ __global__ __launch_bounds__(256, 2) void ffn_tile_dma(
     }
 #pragma unroll
     for (int mt = 0; mt < MTW; ++mt) {
-      const u32x4 af = *reinterpret_cast<const u32x4*>(base + a_rd[mt]);
+      if (mt < live_mt) {
+        const u32x4 af = *reinterpret_cast<const u32x4*>(base + a_rd[mt]);
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) acc[mt][j] = mfma_bf16_16x16x32(af, bf[j], acc[mt][j]);
+        for (int j = 0; j < NJ; ++j) acc[mt][j] = mfma_bf16_16x16x32(af, bf[j], acc[mt][j]);
+      }
     }
   };
   // this wave's loads of the oldest in-flight step have landed and its reads
@@ -281,9 +297,15 @@ static hipError_t launch_dma(const void* A, const void* W, void* out, const int3
   const int mch = (C + BM - 1) / BM;
   int64_t grid = (int64_t)N * mch * (Ncols / TN);
   grid = (grid + kDmaXcds - 1) / kDmaXcds * kDmaXcds;
-  hipLaunchKernelGGL((ffn_tile_dma<MTW, NJ, S>), dim3((unsigned)grid), dim3(256), 0, st,
-                     static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(W), static_cast<uint16_t*>(out), kept,
-                     active, n_active, N, C, K, Ncols, relu, mch, gather, a_rows);
+  // one m-chunk per expert: each weight panel is streamed by exactly one tile
+  if (mch == 1)
+    hipLaunchKernelGGL((ffn_tile_dma<MTW, NJ, S, true>), dim3((unsigned)grid), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(W), static_cast<uint16_t*>(out),
+                       kept, active, n_active, N, C, K, Ncols, relu, mch, gather, a_rows);
+  else
+    hipLaunchKernelGGL((ffn_tile_dma<MTW, NJ, S, false>), dim3((unsigned)grid), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(W), static_cast<uint16_t*>(out),
+                       kept, active, n_active, N, C, K, Ncols, relu, mch, gather, a_rows);
   return hipGetLastError();
 }
 

@@ -16,7 +16,7 @@ struct RoutePlan {
   bool kslice;      // fused path with the 4 waves splitting K (long rows, N <= 128)
   int tile_rows;    // tokens per workgroup (= per partial row)
   int64_t nblk;     // number of per-workgroup partial rows
-  size_t off_part_p, off_part_cnt, off_logits, bytes;
+  size_t off_part_p, off_part_cnt, off_logits, off_wgf, bytes;
 };
 RoutePlan route_plan(int64_t T, int d, int N, int dtype);
 // stats_later == false: statistics (routed_count, f, P, l_aux) by a final
@@ -166,6 +166,7 @@ struct ExpertBwdArgs {
   float *dgp, *dxe;   // dg partials [N*C][d_ff/64]; dX_e [N][C][d]
   int64_t T;
   int N, C, d, dff;
+  int accum = 0;      // add the weight gradients to dw1 / dw2 (idle experts untouched)
 };
 bool fused_expert_bwd_applies(int64_t T, int C, int d, int dff);
 hipError_t launch_zero_idle_experts(const ExpertBwdArgs& a, hipStream_t st);

@@ -38,6 +38,9 @@ typedef __attribute__((address_space(3))) void lds_void_rt;
 __device__ __forceinline__ void rt_dma16(__amdgpu_buffer_rsrc_t r, unsigned char* lds, int voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_rt*)lds, 16, voff, 0, 0, 0);
 }
+__device__ __forceinline__ void rt_dma16_so(__amdgpu_buffer_rsrc_t r, unsigned char* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_rt*)lds, 16, voff, soff, 0, 0);
+}
 }  // namespace
 
 // logits for `rows` tokens live in LDS lg[m * ldl + n] (no bias yet)
@@ -383,6 +386,155 @@ __global__ __launch_bounds__(kRouteThreads, 1) void route_kslice_bf16(
     smem[q] = ((smem[q] + smem[REG + q]) + smem[2 * REG + q]) + smem[3 * REG + q];
   __syncthreads();
   route_epilogue<J>(smem, ldl, TM * 16, t0, T, N, bias, expert_id, gate, part_p, part_cnt, blockIdx.x, ex);
+}
+
+// ----------------------------------------------------------------------------
+// Streaming bf16 router for many tokens with long rows (the 16384 x 5120
+// layer; d % 1024 == 0), where reading x from HBM is the whole cost: the
+// workgroup's 16 TM token rows are staged in LDS chunk by chunk (KC = 256 k
+// per row) by direct global-to-LDS loads, whole 512-byte row segments per
+// chunk, with three chunks in flight while a fourth is multiplied, so a CU
+// keeps 3 x 16 TM x 512 bytes of distinct x in flight.  The 4 waves split the
+// expert tiles (N <= 128: two 16-expert tiles each); each wave holds its W_g
+// fragments for a whole chunk in registers (from L2), loaded one chunk ahead
+// into a second register set.  Loads retire in order, so one wait per chunk
+// covers the chunk's W_g and x.  The four chunk buffers are separate LDS
+// arrays named by compile-time indices, so the compiler's wait counts see
+// that a fragment read does not alias the loads in flight to the other
+// buffers.  16-byte pieces of a staged row are XOR-swizzled by the row's low
+// 4 bits, so the 16 rows an A-fragment read touches fall on distinct banks.
+// ----------------------------------------------------------------------------
+#define SWM_RT_WAIT_VMCNT_LGKM0(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4))
+
+// W_g in MFMA-fragment order for the streaming kernel: fragment (k-step ks,
+// expert tile g) is 64 lanes x 16 bytes, lane (c, kg) holding W_g[16 g + c,
+// 32 ks + 8 kg .. + 7] (zero past N), so that a wave reads each fragment as
+// one contiguous 1 KB (whole cache lines) instead of 16 half-lines.
+__global__ __launch_bounds__(256) void route_wg_frag(const uint16_t* __restrict__ wg, int d, int N,
+                                                     u32x4* __restrict__ wgf) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // fragment element
+  const int64_t total = (int64_t)8 * (d / 32) * 64;
+  if (i >= total) return;
+  const int lane = (int)(i & 63), g = (int)((i >> 6) & 7), ks = (int)(i >> 9);
+  const int n = g * 16 + (lane & 15), k = ks * 32 + (lane >> 4) * 8;
+  wgf[i] = n < N ? *reinterpret_cast<const u32x4*>(wg + (int64_t)n * d + k) : u32x4{0u, 0u, 0u, 0u};
+}
+
+template <int TM, int J>
+__global__ __launch_bounds__(kRouteThreads, 1) void route_stream_bf16(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg, const float* __restrict__ bias, int64_t T, int d,
+    int N, int32_t* __restrict__ expert_id, float* __restrict__ gate, float* __restrict__ part_p,
+    int32_t* __restrict__ part_cnt, RouteExtra ex, const u32x4* __restrict__ wgf) {
+  constexpr int NG = 2;                 // expert tiles per wave: 4 waves x 2 x 16 = 128 experts
+  constexpr int KC = 256;               // k per chunk
+  constexpr int KS = KC / 32;           // 32-deep MFMA steps per chunk
+  constexpr int ROWS = TM * 16;         // tokens per workgroup
+  constexpr int CB = ROWS * KC * 2;     // bytes of one staged chunk
+  constexpr int DW = CB / 1024 / 4;     // 1 KB global-to-LDS loads per wave per chunk
+  constexpr int CPR = KC / 8;           // 16-byte pieces per staged row
+  constexpr int RB = KC * 2;            // bytes per staged row
+  constexpr int WAIT = 2 * DW + KS * NG;  // loads issued after a chunk's W_g (see the loop)
+  static_assert(WAIT <= 63, "vmcnt range");
+  constexpr int ldl = 128;              // logits row stride (N <= 128)
+  static_assert(ROWS * ldl * 4 <= CB, "the logits fit the first chunk buffer");
+  __shared__ __attribute__((aligned(1024))) unsigned char xb0[CB];
+  __shared__ __attribute__((aligned(1024))) unsigned char xb1[CB];
+  __shared__ __attribute__((aligned(1024))) unsigned char xb2[CB];
+  __shared__ __attribute__((aligned(1024))) unsigned char xb3[CB];
+  auto xbuf = [&](int i) -> unsigned char* { return i == 0 ? xb0 : i == 1 ? xb1 : i == 2 ? xb2 : xb3; };
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, kg = lane >> 4;
+  const int64_t t0 = (int64_t)blockIdx.x * ROWS;
+  const int64_t rows_here = (T - t0) < ROWS ? (T - t0) : ROWS;
+  const int nch = d / KC;
+  const __amdgpu_buffer_rsrc_t xres =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x + t0 * d), (short)0, (int)(rows_here * d * 2), 0x00020000);
+  // W_g in fragment order (route_wg_frag): 8 tiles x d / 32 k-steps x 1 KB
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(const_cast<u32x4*>(wgf), (short)0,
+                                                                        (int)((int64_t)8 * (d / 32) * 1024), 0x00020000);
+  // x: load i of this wave fills staged piece p = (w DW + i) 64 + lane, i.e.
+  // row p / CPR, stored piece p % CPR, which holds global piece (p % CPR) ^ (row & 15)
+  int x_voff[DW];
+#pragma unroll
+  for (int i = 0; i < DW; ++i) {
+    const int p = (w * DW + i) * 64 + lane, r = p / CPR, q = (p % CPR) ^ (r & 15);
+    x_voff[i] = r < rows_here ? (r * d + q * 8) * 2 : 0x7ffffff0;
+  }
+  int b_voff[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) b_voff[g] = ((w * NG + g) * 64 + lane) * 16;
+  auto issue_x = [&](int buf, int ch) {  // past the last chunk: re-read it (cache hits)
+    const int so = (ch < nch ? ch : nch - 1) * RB;
+    unsigned char* xb = xbuf(buf);
+#pragma unroll
+    for (int i = 0; i < DW; ++i) rt_dma16_so(xres, xb + (w * DW + i) * 1024, x_voff[i], so);
+  };
+  u32x4 wr0[KS][NG], wr1[KS][NG];
+  auto issue_w = [&](u32x4 (&wr)[KS][NG], int ch) {
+    const int so = (ch < nch ? ch : nch - 1) * KS * 8 * 1024;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int g = 0; g < NG; ++g)
+        wr[ks][g] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, b_voff[g], so + ks * 8 * 1024, 0));
+  };
+  f32x4 acc[TM][NG];
+#pragma unroll
+  for (int mt = 0; mt < TM; ++mt)
+#pragma unroll
+    for (int g = 0; g < NG; ++g) acc[mt][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const u32x4 (&wr)[KS][NG], int buf) {
+    const unsigned char* xb = xbuf(buf);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int mt = 0; mt < TM; ++mt) {
+        const int r = mt * 16 + c;
+        const u32x4 a = *reinterpret_cast<const u32x4*>(xb + r * RB + (((ks * 4 + kg) ^ (r & 15)) << 4));
+#pragma unroll
+        for (int g = 0; g < NG; ++g) acc[mt][g] = mfma_bf16_16x16x32(a, wr[ks][g], acc[mt][g]);
+      }
+  };
+  // chunk ch = ch0 + u (buffer u): every wave is done with chunk ch - 1, whose
+  // buffer takes chunk ch + 3; issue W_g of ch + 1 and x of ch + 3, wait for
+  // W_g and x of ch (WAIT loads were issued after W_g of ch), publish x of ch,
+  // multiply
+  auto body = [&](u32x4 (&cur)[KS][NG], u32x4 (&nxt)[KS][NG], int u, int ch) {
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue_w(nxt, ch + 1);
+    issue_x((u + 3) & 3, ch + 3);
+    SWM_RT_WAIT_VMCNT_LGKM0(WAIT);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    compute(cur, u);
+  };
+  issue_w(wr0, 0);
+  issue_x(0, 0);
+  issue_x(1, 1);
+  issue_x(2, 2);
+  // nch is a multiple of 4 (d % 1024 == 0): buffer and register-set indices
+  // stay compile-time constants and the loop has no inner branch (a branch
+  // would let the compiler sink the next chunk's W_g loads down to their use)
+  for (int ch = 0; ch < nch; ch += 4) {
+    body(wr0, wr1, 0, ch);
+    body(wr1, wr0, 1, ch + 1);
+    body(wr0, wr1, 2, ch + 2);
+    body(wr1, wr0, 3, ch + 3);
+  }
+  SWM_RT_WAIT_VMCNT_LGKM0(0);  // no load may still be writing LDS
+  __syncthreads();
+  float* lg = reinterpret_cast<float*>(xb0);  // the staged chunks are dead now
+#pragma unroll
+  for (int mt = 0; mt < TM; ++mt)
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lg[(mt * 16 + kg * 4 + i) * ldl + (w * NG + g) * 16 + c] = acc[mt][g][i];
+  __syncthreads();
+  route_epilogue<J>(lg, ldl, ROWS, t0, T, N, bias, expert_id, gate, part_p, part_cnt, blockIdx.x, ex);
 }
 
 // ----------------------------------------------------------------------------
@@ -764,6 +916,9 @@ __global__ __launch_bounds__(1024) void assign_token_finalize(const int32_t* __r
 // ----------------------------------------------------------------------------
 // host side
 // ----------------------------------------------------------------------------
+// the streaming kernel (rows staged in LDS chunks) takes the K-sliced plans with d % 1024 == 0
+static bool route_streams(const RoutePlan& pl, int d) { return pl.split == 0 && pl.kslice && d % 1024 == 0; }
+
 RoutePlan route_plan(int64_t T, int d, int N, int dtype) {
   RoutePlan pl{};
   const int64_t tiles16 = (T + 15) / 16;
@@ -800,6 +955,8 @@ RoutePlan route_plan(int64_t T, int d, int N, int dtype) {
   off = align_up(off + (size_t)pl.nblk * N * 4);
   pl.off_logits = off;
   if (pl.split > 0) off = align_up(off + (size_t)pl.split * T * N * 4);
+  pl.off_wgf = off;
+  if (route_streams(pl, d)) off = align_up(off + (size_t)8 * (d / 32) * 1024);  // 8 expert tiles x k-steps x 1 KB
   pl.tile_rows = pl.split == 0 ? pl.tm * 16 : (dtype == 1 ? 1 : 16);
   pl.bytes = off;
   return pl;
@@ -820,6 +977,20 @@ static hipError_t launch_route_j(const RoutePlan& pl, const void* x, const void*
     dim3 grid((unsigned)pl.nblk);
     auto* xb = static_cast<const uint16_t*>(x);
     auto* wb = static_cast<const uint16_t*>(wg);
+    if (J != 2 && pl.kslice) return hipErrorInvalidValue;  // the plan takes these kernels for N <= 128 only
+    if constexpr (J == 2) {
+    if (route_streams(pl, d)) {  // static LDS: four staged chunks
+      u32x4* wgf = reinterpret_cast<u32x4*>(ws + pl.off_wgf);
+      const int64_t frag = (int64_t)8 * (d / 32) * 64;
+      hipLaunchKernelGGL(route_wg_frag, dim3((unsigned)((frag + 255) / 256)), dim3(256), 0, st, wb, d, N, wgf);
+      if (pl.tm == 4)
+        hipLaunchKernelGGL((route_stream_bf16<4, J>), grid, dim3(kRouteThreads), 0, st, xb, wb, bias, T, d, N,
+                           expert_id, gate, part_p, part_cnt, ex, wgf);
+      else
+        hipLaunchKernelGGL((route_stream_bf16<2, J>), grid, dim3(kRouteThreads), 0, st, xb, wb, bias, T, d, N,
+                           expert_id, gate, part_p, part_cnt, ex, wgf);
+      return hipGetLastError();
+    }
     if (pl.kslice) {
       const size_t klds = (size_t)4 * pl.tm * 16 * 128 * 4;  // four quarters' partial logits
       if (pl.tm == 4)
@@ -828,7 +999,10 @@ static hipError_t launch_route_j(const RoutePlan& pl, const void* x, const void*
       else
         hipLaunchKernelGGL((route_kslice_bf16<2, J>), grid, dim3(kRouteThreads), klds, st, xb, wb, bias, T, d, N,
                            expert_id, gate, part_p, part_cnt, ex);
-    } else if (pl.tm == 4)
+      return hipGetLastError();
+    }
+    }
+    if (pl.tm == 4)
       hipLaunchKernelGGL((route_fused_bf16<4, 2, J, false>), grid, dim3(kRouteThreads), lds, st, xb, wb, bias, T, d, N,
                          expert_id, gate, part_p, part_cnt, ex);
     else if (pl.tm == 2)

@@ -21,7 +21,7 @@ HEADER = os.path.join(os.path.dirname(_PKG), "include", "switch_moe.h")
 
 F32, BF16 = 0, 1
 TOKEN_ORDER, GATE_DESC = 0, 1
-GATE_SCALE, RESIDUAL_ALL, RENORM = 1, 2, 4
+GATE_SCALE, RESIDUAL_ALL, RENORM, ACCUM_EXPERT_GRADS = 1, 2, 4, 8
 TOKEN_CHOICE, EXPERT_CHOICE = 0, 1
 _ROUTING = {"token": TOKEN_CHOICE, "expert": EXPERT_CHOICE, TOKEN_CHOICE: TOKEN_CHOICE, EXPERT_CHOICE: EXPERT_CHOICE}
 _DT = {torch.float32: F32, torch.bfloat16: BF16}
@@ -305,14 +305,16 @@ class SwitchMoE:
 
     def __init__(self, T, d_model, d_ff, N, *, dtype=torch.bfloat16, capacity_factor=1.0, C=0, priority="token",
                  gate_scale=True, residual_all=False, d_ff_shared=0, device="cuda", train=False, top_k=1,
-                 routing="token", renorm=False, weight_format="native", expand=1):
+                 routing="token", renorm=False, weight_format="native", expand=1, accumulate_expert_grads=False):
         """top_k > 1: top-K token choice; routing="expert": expert choice; expand = M >= 2: Expanded
         Drop over each token's M highest-logit experts (see include/switch_moe.h).
-        With top-K, out["expert_id"], out["gate"] and out["slot"] are [T, K]."""
+        With top-K, out["expert_id"], out["gate"] and out["slot"] are [T, K].
+        accumulate_expert_grads: the backward adds the routed experts' weight gradients to
+        self.grads["dw1"] / ["dw2"] (SWITCH_ACCUM_EXPERT_GRADS); idle experts are left as they are."""
         self.desc = SwitchMoeDesc(T=T, d_model=d_model, d_ff=d_ff, N=N, C=C, capacity_factor=capacity_factor,
                                   dtype=_DT[dtype], priority=_PRIO[priority],
                                   flags=(GATE_SCALE if gate_scale else 0) | (RESIDUAL_ALL if residual_all else 0)
-                                  | (RENORM if renorm else 0),
+                                  | (RENORM if renorm else 0) | (ACCUM_EXPERT_GRADS if accumulate_expert_grads else 0),
                                   d_ff_shared=d_ff_shared, top_k=top_k, routing=_ROUTING[routing],
                                   weight_format={"native": 0, "mxfp4": 1}[weight_format],
                                   expand_choices=expand)

@@ -129,7 +129,7 @@ def test_forward_validation(L):
     assert fwd(None, ctypes.byref(ins), ctypes.byref(outs), FAKE, 1 << 30, None) == E_NULL
     assert fwd(ctypes.byref(d), None, ctypes.byref(outs), FAKE, 1 << 30, None) == E_NULL
     assert fwd(ctypes.byref(d), ctypes.byref(ins), ctypes.byref(outs), FAKE, 16, None) == E_WS
-    d.flags = 8
+    d.flags = 16  # an unknown flag bit
     assert fwd(ctypes.byref(d), ctypes.byref(ins), ctypes.byref(outs), FAKE, 1 << 30, None) == E_UNSUP
     d.flags = 1
     d.d_ff_shared = 128
@@ -137,6 +137,13 @@ def test_forward_validation(L):
     d.d_ff_shared = 0
     d.capacity_factor = 0.0
     assert fwd(ctypes.byref(d), ctypes.byref(ins), ctypes.byref(outs), FAKE, 1 << 30, None) == E_SHAPE
+    # bf16 rows must be multiples of 128 elements (the kernels' granule); refused before any launch
+    d.capacity_factor = 1.0
+    for dm, dff in ((776, 3072), (768, 3080), (776, 3080)):
+        d.d_model, d.d_ff = dm, dff
+        assert fwd(ctypes.byref(d), ctypes.byref(ins), ctypes.byref(outs), FAKE, 1 << 30, None) == E_SHAPE
+        assert b"multiple of 128" in L.switch_last_error()
+        assert L.switch_moe_workspace_bytes(ctypes.byref(d)) == 0
 
 
 def test_timed_forward_validation(L):

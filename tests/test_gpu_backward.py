@@ -235,3 +235,65 @@ def test_backward_decode():
     inactive = torch.ones(wl.N, dtype=torch.bool, device="cuda")
     inactive[torch.from_numpy(ref["active"].astype(np.int64)).cuda()] = False
     assert not torch.any(g["dw1"][inactive]) and not torch.any(g["dw2"][inactive])
+
+
+@pytest.mark.parametrize("name", ["switch-decode-384", "switch-base-uniform"])
+def test_backward_accumulate_expert_grads(name):
+    """SWITCH_ACCUM_EXPERT_GRADS: dw1 / dw2 start from seeded prior gradients R;
+    after the backward, every expert that kept a token holds R + its gradient
+    (same bar, envelope shifted by R) and every other expert still holds R bit
+    for bit; dx, dW_g and db are the plain backward's."""
+    wl = workloads.WORKLOADS[name]
+    _say(f"{wl.name} accumulate")
+    dt, tol = wl.dtype, TOL_OUT[wl.dtype]
+    inp, d, dy = _prepare(wl)
+    ref = oracle.moe_forward_stored(inp)
+    x = oracle.widen(inp.x, dt)
+    d_out, _, _ = ob.combine_backward(oracle.widen(dy, dt), ref["out"], ref["expert_id"], ref["slot"], ref["gate"],
+                                      wl.gate_scale, wl.residual_all)
+    grads = {}
+    for e in ref["active"]:
+        k = int(ref["kept_count"][e])
+        _, dw1, dw2, _, env = ob.ffn_backward(x[ref["token_of_slot"][e, :k]], d_out[e, :k],
+                                              oracle.widen(inp.w1[e], dt), oracle.widen(inp.w2[e], dt), U32)
+        grads[int(e)] = (dw1, dw2, env["dw1"])
+    # prior gradients: N(0, 1) scaled to the largest gradient magnitude (so both terms count), bf16
+    scale = max(max(np.abs(a).max(), np.abs(b).max()) for a, b, _ in grads.values())
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4242)
+    layer = native.SwitchMoE(wl.T, wl.d_model, wl.d_ff, wl.N, dtype=_tdt(wl), capacity_factor=wl.capacity_factor,
+                             priority=wl.priority, gate_scale=wl.gate_scale, residual_all=wl.residual_all,
+                             train=True, accumulate_expert_grads=True)
+    R1 = (torch.randn(layer.grads["dw1"].shape, generator=gen, device="cuda") * scale).to(_tdt(wl))
+    R2 = (torch.randn(layer.grads["dw2"].shape, generator=gen, device="cuda") * scale).to(_tdt(wl))
+    layer.grads["dw1"].copy_(R1)
+    layer.grads["dw2"].copy_(R2)
+    kw = dict(bias=d["bias"])
+    layer.forward_train(d["x"], d["w_gate"], d["w1"], d["w2"], **kw)
+    dla = torch.tensor([workloads.DL_AUX], dtype=torch.float32, device="cuda")
+    g = layer.backward(d["x"], d["w_gate"], d["w1"], d["w2"], dev(dy, dt), dl_aux=dla, **kw)
+    torch.cuda.synchronize()
+    idle = torch.ones(wl.N, dtype=torch.bool, device="cuda")
+    idle[torch.from_numpy(ref["active"].astype(np.int64)).cuda()] = False
+    assert torch.equal(g["dw1"][idle].view(torch.int16), R1[idle].view(torch.int16))
+    assert torch.equal(g["dw2"][idle].view(torch.int16), R2[idle].view(torch.int16))
+    worst = 0.0
+    for e, (dw1, dw2, env1) in grads.items():
+        r1, r2 = host(R1[e]), host(R2[e])
+        worst = max(worst, check_rows(f"dw1[{e}]", host(g["dw1"][e]), r1 + dw1, tol, (r1 + env1[0], r1 + env1[1])))
+        worst = max(worst, check_rows(f"dw2[{e}]", host(g["dw2"][e]), r2 + dw2, tol))
+    _say(f"{wl.name} accumulate: {len(grads)} active experts, max row rel err {worst:.2e}")
+    # the other gradients are the plain backward's
+    check_streaming(wl, inp, dy, workloads.DL_AUX, g, experts=set())
+
+
+def test_backward_accumulate_refused_on_generic_path():
+    """The flag needs the fused bf16 expert backward; the fp32 layer is refused before any launch."""
+    wl = workloads.WORKLOADS["switch-tiny-fp32"]
+    inp, d, dy = _prepare(wl)
+    layer = native.SwitchMoE(wl.T, wl.d_model, wl.d_ff, wl.N, dtype=torch.float32, capacity_factor=wl.capacity_factor,
+                             train=True, accumulate_expert_grads=True)
+    layer.forward_train(d["x"], d["w_gate"], d["w1"], d["w2"])
+    with pytest.raises(native.SwitchError) as ei:
+        layer.backward(d["x"], d["w_gate"], d["w1"], d["w2"], dev(dy, wl.dtype))
+    assert ei.value.status == 3

@@ -29,6 +29,7 @@ def _host_bf16(t):
     return oracle.widen(t.detach().cpu().view(torch.int16).numpy().view(np.uint16), "bf16")
 
 
+@pytest.mark.timeout(600)
 def test_large_shared_layer():
     import switch_top_routed_amd as sw
     from switch_top_routed_amd import native

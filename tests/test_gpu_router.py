@@ -6,9 +6,10 @@ mechanism and Load balancing).
   would stage a workgroup's rows in LDS (T = 4096): the staging's swizzle
   needs d % 128 == 0, so these shapes must take the streaming path and still
   match;
-* the K-sliced kernel (many tokens, rows of >= 2048 elements, N <= 128) at
-  both tile heights (32 and 64 tokens per workgroup), with a ragged last
-  tile and N not a multiple of 16.
+* the two kernels for many tokens with long rows (>= 2048 elements, N <=
+  128): the streaming one (rows staged in LDS chunk by chunk, d % 1024 == 0)
+  and the K-sliced one (otherwise), at both tile heights (32 and 64 tokens
+  per workgroup), with a ragged last tile and N not a multiple of 16.
 Expert ids and counts bit-exact, gate / P / L_aux at the router tolerances.
 """
 import math
@@ -28,9 +29,12 @@ CASES = [
     # (T, d_model, N, bias_scale)
     (4096, 96, 64, 0.0),      # one 16-token tile per workgroup, 3 k-steps
     (4096, 160, 40, 1.0),     # 5 k-steps, N ragged, Zipf-like bias
-    (8200, 2048, 100, 0.0),   # K-sliced, 32 tokens per workgroup, last tile 8 tokens
-    (16400, 2048, 128, 1.0),  # K-sliced, 64 tokens per workgroup, last tile 16 tokens
-    (8192, 4096, 128, 0.0),   # K-sliced, 32 tokens per workgroup, 128 k-steps
+    (8200, 2048, 100, 0.0),   # streaming (rows staged in LDS chunks), 32 tokens per workgroup, last tile 8
+    (16400, 2048, 128, 1.0),  # streaming, 64 tokens per workgroup, last tile 16 tokens, 8 chunks
+    (8192, 4096, 128, 0.0),   # streaming, 32 tokens per workgroup, 16 chunks
+    (16400, 5120, 128, 0.0),  # streaming, 64 tokens per workgroup, last tile 16 tokens, 20 chunks
+    (8192, 2560, 96, 1.0),    # K-sliced waves (d % 1024 != 0), 32 tokens per workgroup
+    (16400, 2560, 120, 0.0),  # K-sliced waves, 64 tokens per workgroup, last tile 16 tokens
 ]
 
 
