@@ -82,13 +82,13 @@ TRAFFIC = {
 BWD_SOURCES = ("switch_top_routed_amd/csrc/backward_fused.hip", "switch_top_routed_amd/csrc/common.hpp")
 BWD_TRAFFIC = {
     "switch-base-uniform": {
-        "sources_sha256": "409d356bb35470314da9ef7f5376d0dd79ac1a74923680b28b0e5940205c76b4",
-        "fetch_kib": [322784.0, 313059.0], "write_kib": [614909.0, 601879.0],
+        "sources_sha256": "f019f7dee3cd11f15edc95fad08c0221bb3c792f675aaf811058b458a711525d",
+        "fetch_kib": [322801.2, 313118.8], "write_kib": [614901.1, 601878.9],
         "fetch_scale": 2.0, "write_scale": 1.0,
     },
     "switch-large-shared": {
-        "sources_sha256": "409d356bb35470314da9ef7f5376d0dd79ac1a74923680b28b0e5940205c76b4",
-        "fetch_kib": [5879322.0, 5801339.0], "write_kib": [10761420.0, 10813443.0],
+        "sources_sha256": "f019f7dee3cd11f15edc95fad08c0221bb3c792f675aaf811058b458a711525d",
+        "fetch_kib": [5871750.4, 5811617.3], "write_kib": [10761241.9, 10813443.0],
         "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
@@ -660,15 +660,28 @@ def cpu_baseline(inp, seconds, top_k=1, routing="token", renorm=False, weights="
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
-    passes = 0
-    t0 = time.perf_counter()
-    while True:
-        one_pass()
-        passes += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or passes >= 30:
-            break
+    def timed(budget):
+        passes = 0
+        t0 = time.perf_counter()
+        while True:
+            one_pass()
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= budget or passes >= 30:
+                return passes, el
+
+    passes, el = timed(seconds)
+    one = None
+    if inp.wl.T * inp.wl.d_model <= 4096 * 768:  # small layers: also on one thread (BLAS limited to 1)
+        try:
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(limits=1):
+                p1, e1 = timed(seconds / 2)
+            one = {"value": inp.wl.T * p1 / e1, "unit": "tokens/s", "cores": 1, "seconds": e1, "passes": p1}
+        except Exception:  # pragma: no cover -- informative only
+            one = None
     return {"value": inp.wl.T * passes / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "one_thread": one,
             "seconds": el, "sample": f"{passes} full fp64 layer passes over the {inp.wl.name} batch "
                                      f"(T={inp.wl.T} tokens each, "
                                      f"{'expert choice' if routing == 'expert' else f'top-{max(1, top_k)}'}"
@@ -746,8 +759,9 @@ def cpu_baseline_sampled(inp, W, C, seconds):
             "seconds": total, "step_seconds": tm,
             "sample": f"fp64 oracle over the {wl.name} batch (T={wl.T}): router, statistics, slots, dispatch and "
                       f"combine in full; expert FFN on {done} of {active.size} active experts, scaled by "
-                      f"{active.size}/{done}; shared FFN on {ns} of {wl.T} tokens, scaled by {wl.T}/{ns} "
-                      f"(weights widened once, in full)"}
+                      f"{active.size}/{done}"
+                      + (f"; shared FFN on {ns} of {wl.T} tokens, scaled by {wl.T}/{ns} (weights widened once, in full)"
+                         if ns else "")}
 
 
 if __name__ == "__main__":
