@@ -5,8 +5,8 @@
 // filled slots of the active experts; "Top-1 Routing" page, Key parameters and
 // compute), for experts with more than 64 rows and for the always-on shared
 // dense expert, where the work per weight byte is high enough that MFMA
-// throughput and panel reuse matter.  A workgroup (4 waves, 2 x 2) owns a
-// BM x TN output tile and walks K in 32-deep steps:
+// throughput and panel reuse matter.  A workgroup (2 x 2 waves, or 2 x 4 for
+// the widest tiles) owns a BM x TN output tile and walks K in 32-deep steps:
 //  * every global load is a buffer load that writes LDS directly (16 bytes per
 //    lane, 1 KB per wave instruction), so the operands never pass through
 //    registers on their way in and S LDS stages (separate LDS arrays) keep
@@ -25,8 +25,9 @@
 // of bank conflicts for 8- and 16-lane LDS service; weight chunks are XORed
 // with 2 (k mod 4) + 8 (k / 8 mod 2), which puts the 8 k-rows that one
 // transposing read touches (4 per 16-lane group) on distinct banks.  Two
-// workgroups share a CU (two waves per SIMD), so one wave's MFMAs overlap the
-// other's LDS reads and barrier; tiles are dealt to the 8 XCDs in contiguous
+// waves share each SIMD (two 4-wave workgroups per CU, or one of 8 waves), so
+// one wave's MFMAs overlap the other's LDS reads and barrier; tiles are dealt
+// to the 8 XCDs in contiguous
 // ranges, up to 8 m-chunks of an expert walking the column blocks together
 // (shared A and W panels in L2).
 #include "common.hpp"
@@ -72,20 +73,21 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const unsigned char* lds) {
 
 }  // namespace
 
-// MTW m-tiles x NJ n-tiles of 16 x 16 per wave (2 x 2 waves): a BM = 32 MTW
-// by TN = 32 NJ tile; S LDS stages.  WNT: the weights are read once per launch
-// (one m-chunk per expert), so their loads carry the non-temporal policy and
-// leave the caches to the token rows, which every column block re-reads.
-template <int MTW, int NJ, int S, bool WNT>
-__global__ __launch_bounds__(256, MTW * NJ >= 48 ? 1 : 2) void ffn_tile_dma(
+// MTW m-tiles x NJ n-tiles of 16 x 16 per wave (2 x WN waves): a BM = 32 MTW
+// by TN = 16 NJ WN tile; S LDS stages.  WNT: the weights are read once per
+// launch (one m-chunk per expert), so their loads carry the non-temporal policy
+// and leave the caches to the token rows, which every column block re-reads.
+template <int MTW, int NJ, int S, bool WNT, int WN>
+__global__ __launch_bounds__(128 * WN, WN > 2 || MTW * NJ >= 48 ? 1 : 2) void ffn_tile_dma(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, uint16_t* __restrict__ out,
     const int32_t* __restrict__ kept_count, const int32_t* __restrict__ active, const int32_t* __restrict__ n_active,
     int N, int C, int K, int Ncols, int relu, int mch, const int32_t* __restrict__ gather, int64_t a_rows) {
-  constexpr int BM = 32 * MTW, TN = 32 * NJ;
+  constexpr int NWV = 2 * WN;          // waves
+  constexpr int BM = 32 * MTW, TN = 16 * NJ * WN;
   constexpr int AB = BM / 16;          // 1 KB blocks of A per stage (16 rows each)
   constexpr int WB = TN / 16;          // 1 KB blocks of W per stage (32 k-rows x TN columns)
   constexpr int NB = AB + WB;
-  constexpr int LW = (NB + 3) / 4;     // loads per wave per step
+  constexpr int LW = (NB + NWV - 1) / NWV;  // loads per wave per step
   constexpr int RB = TN * 2;           // bytes per W k-row
   constexpr int SB = NB * 1024;        // bytes per stage
   static_assert(S >= 2 && S <= 4, "2 to 4 LDS stages");
@@ -97,7 +99,7 @@ __global__ __launch_bounds__(256, MTW * NJ >= 48 ? 1 : 2) void ffn_tile_dma(
 
   const int tid = threadIdx.x, lane = tid & 63, c = lane & 15, kg = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w / WN, wn = w % WN;
   const int NT = Ncols / TN;
   int n_act = n_active[0];
   if (n_act > N) n_act = N;
@@ -135,14 +137,14 @@ __global__ __launch_bounds__(256, MTW * NJ >= 48 ? 1 : 2) void ffn_tile_dma(
                                                         : dma_rsrc(A + ((int64_t)e * C + m0) * K, (int64_t)rows * K * 2);
   const __amdgpu_buffer_rsrc_t wres = dma_rsrc(W + (int64_t)e * K * Ncols, (int64_t)K * Ncols * 2);
 
-  // the LW blocks this wave loads every step (block w + 4 i; past NB it repeats
-  // block w + 4 (i - 1): same bytes to the same place), as lane offsets
+  // the LW blocks this wave loads every step (block w + NWV i; past NB it
+  // repeats block w + NWV (i - 1): same bytes to the same place), as lane offsets
   int voff[LW], lds_blk[LW];
   bool is_a[LW];
 #pragma unroll
   for (int i = 0; i < LW; ++i) {
-    int j = w + 4 * i;
-    if (j >= NB) j -= 4;
+    int j = w + NWV * i;
+    if (j >= NB) j -= NWV;
     lds_blk[i] = j * 1024;
     is_a[i] = j < AB;
     if (j < AB) {
@@ -258,7 +260,7 @@ __global__ __launch_bounds__(256, MTW * NJ >= 48 ? 1 : 2) void ffn_tile_dma(
   // land on different banks) and leaves as 16-byte non-temporal stores that
   // cover whole 128-byte lines (4 rows x 32 NJ bytes per instruction).
   constexpr int ROWB = 32 * NJ + 16;
-  static_assert(4 * 16 * ROWB <= SB, "the output staging fits one LDS stage");
+  static_assert(NWV * 16 * ROWB <= SB, "the output staging fits one LDS stage");
   unsigned char* ost = st0 + w * 16 * ROWB;
   constexpr int CH = 2 * NJ;  // 16-byte chunks per staged row
 #pragma unroll
@@ -289,21 +291,21 @@ __global__ __launch_bounds__(256, MTW * NJ >= 48 ? 1 : 2) void ffn_tile_dma(
   }
 }
 
-template <int MTW, int NJ, int S>
+template <int MTW, int NJ, int S, int WN = 2>
 static hipError_t launch_dma(const void* A, const void* W, void* out, const int32_t* kept, const int32_t* active,
                              const int32_t* n_active, int N, int C, int K, int Ncols, int relu, hipStream_t st,
                              const int32_t* gather, int64_t a_rows) {
-  constexpr int BM = 32 * MTW, TN = 32 * NJ;
+  constexpr int BM = 32 * MTW, TN = 16 * NJ * WN;
   const int mch = (C + BM - 1) / BM;
   int64_t grid = (int64_t)N * mch * (Ncols / TN);
   grid = (grid + kDmaXcds - 1) / kDmaXcds * kDmaXcds;
   // one m-chunk per expert: each weight panel is streamed by exactly one tile
   if (mch == 1)
-    hipLaunchKernelGGL((ffn_tile_dma<MTW, NJ, S, true>), dim3((unsigned)grid), dim3(256), 0, st,
+    hipLaunchKernelGGL((ffn_tile_dma<MTW, NJ, S, true, WN>), dim3((unsigned)grid), dim3(128 * WN), 0, st,
                        static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(W), static_cast<uint16_t*>(out),
                        kept, active, n_active, N, C, K, Ncols, relu, mch, gather, a_rows);
   else
-    hipLaunchKernelGGL((ffn_tile_dma<MTW, NJ, S, false>), dim3((unsigned)grid), dim3(256), 0, st,
+    hipLaunchKernelGGL((ffn_tile_dma<MTW, NJ, S, false, WN>), dim3((unsigned)grid), dim3(128 * WN), 0, st,
                        static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(W), static_cast<uint16_t*>(out),
                        kept, active, n_active, N, C, K, Ncols, relu, mch, gather, a_rows);
   return hipGetLastError();
@@ -313,19 +315,27 @@ static hipError_t launch_dma(const void* A, const void* W, void* out, const int3
 // groups of 8, whole 128- or 256-column blocks).
 bool tiled_ffn_applies(int C, int d, int dff) { return C > 64 && d % 256 == 0 && dff % 256 == 0; }
 
-// 160 x 256 tiles with 2 stages for 128 < C <= 160 (one m-chunk per expert:
-// each weight panel is streamed once; measured on the 128-expert large layer,
-// GEMM 1 1.97 ms against 2.09 ms with 3 stages and 2.83 ms with 160 x 128
-// tiles); 96 x 256 tiles with 2 stages for 64 < C <= 96 (top-2 on the base
+// 128 < C <= 160: one m-chunk per expert (each weight panel is streamed
+// once).  With Ncols a multiple of 512, 160 x 512 tiles on 8 waves (2 x 4,
+// 80 x 128 each) and 3 stages: every token-row block staged in LDS feeds twice
+// as many weight columns, so the CU moves fewer bytes per weight byte (the
+// 128-expert large layer, back-to-back launches: GEMM 1 1.72 ms against 1.80,
+// GEMM 2 1.91 ms against 2.15-2.20 for 160 x 256 on 4 waves, which in turn took
+// GEMM 1 from 2.83 ms with 160 x 128).  Otherwise 160 x 256 on 4 waves with 2
+// stages.  64 < C <= 96: 96 x 256 tiles with 2 stages (top-2 on the base
 // layer, C = 80: 132 us per launch against 138 us with 128 x 256 x 3 and
-// 135-145 us for the other shapes tried); 128 x 256 tiles with 3 stages
-// otherwise, including the shared dense expert (1.21 ms per GEMM, against
-// 1.27-1.45 ms for 160 x 256 or 2 stages).
+// 135-145 us for the other shapes tried).  128 x 256 tiles with 3 stages
+// otherwise, including the shared dense expert (1.14-1.18 ms per GEMM on the
+// large layer; 128 x 512 on 8 waves and 160 x 256 on 8 waves were within
+// +-5% of it, one GEMM faster and the other slower).
 hipError_t launch_tiled_dma(const void* A, const void* W, void* out, const int32_t* kept, const int32_t* active,
                             const int32_t* n_active, int N, int C, int K, int Ncols, int relu, hipStream_t st,
                             const int32_t* gather, int64_t a_rows) {
-  if (C > 128 && C <= 160)
+  if (C > 128 && C <= 160) {
+    if (Ncols % 512 == 0)
+      return launch_dma<5, 8, 3, 4>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st, gather, a_rows);
     return launch_dma<5, 8, 2>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st, gather, a_rows);
+  }
   if (C > 64 && C <= 96)
     return launch_dma<3, 8, 2>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st, gather, a_rows);
   return launch_dma<4, 8, 3>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st, gather, a_rows);

@@ -230,7 +230,7 @@ def test_base_layer_matches_staged_path(base):
         np.testing.assert_array_equal(host_bits(o[k]), host_bits(st[k]), err_msg=k)
 
 
-@pytest.mark.parametrize("name", ["ragged", "f32-odd", "n1000", "tiled-c150", "f32-many-tiles"])
+@pytest.mark.parametrize("name", ["ragged", "f32-odd", "n1000", "tiled-c150", "tiled-c150-wide", "f32-many-tiles"])
 def test_edge_layer_matches_staged_path(name):
     wl = next(w for w in EDGE if w.name == name)
     _say(f"edge layer vs staged path {name}")
@@ -305,7 +305,8 @@ EDGE = [
     _custom("residual", 700, 128, 256, 8, 1.0, seed=8, residual_all=True),
     _custom("tiled-c90", 720, 256, 512, 8, 1.0, seed=15, bias_scale=0.4),      # C = 90: 96 x 256 tiles
     _custom("tiled-c128", 2048, 256, 512, 16, 1.0, seed=11, bias_scale=0.3),   # C > 64: LDS-tiled GEMM, 128 x 256 tiles
-    _custom("tiled-c150", 1200, 256, 512, 8, 1.0, seed=13, bias_scale=0.5),     # C = 150: 160 x 256 tiles
+    _custom("tiled-c150", 1200, 256, 512, 8, 1.0, seed=13, bias_scale=0.5),     # C = 150: 160 x 512 (GEMM 1), 160 x 256 tiles
+    _custom("tiled-c150-wide", 1200, 512, 1536, 8, 1.0, seed=16, bias_scale=0.5),  # C = 150: 160 x 512 tiles on 8 waves, both GEMMs
     _custom("tiled-c180", 1440, 512, 256, 8, 1.0, seed=14, priority="gate"),    # C = 180: two 128-row m-chunks
     _custom("tiled-c200", 1600, 512, 256, 8, 1.0, seed=12, priority="gate"),    # C = 200: two 128-row m-chunks
     # token-order assignment: 1250 router tiles (two LDS chunks of partials), one tile
