@@ -182,6 +182,168 @@ __device__ void route_epilogue(float* lg, int ldl, int rows, int64_t t0, int64_t
   }
 }
 
+// The plain top-1 case of the same epilogue (no probabilities out, no further
+// choices) for 16, 32 or 64 tokens and N <= 128 (logits rows of ldl <= 128
+// floats, ldl a multiple of 16).  The general one walks the tokens one per wave
+// and step, and each token costs a whole-wave arg-max and sum (12 dependent
+// lane exchanges); at 16 tokens per wave that took about 12 us of a 60 us
+// route call on 16384 x 5120 tokens.  Here TPT = 256 / ROWS consecutive lanes
+// share a token, so a token needs log2(TPT) exchanges and all of a wave's
+// tokens run at once.  The results are bit-identical to route_epilogue's, so
+// the two can serve the same layer in different calls:
+//  * lane-slot l (0..63) holds experts l and l + 64, as a lane does there; the
+//    lane of a token with index q takes the slots q L .. q L + L - 1 (L = 64 /
+//    TPT) and the exp-sum is the same balanced tree over the slots in order
+//    (slot sums, then pairs of adjacent blocks), its upper levels across the
+//    TPT lanes;
+//  * the block's sum of p per expert is the same ((S0 + S1) + S2) + S3 with
+//    S_w summed over tokens w, w + 4, ... in order.
+// The probabilities overwrite the logits for the column sums.  tok: ROWS ints
+// (16-byte aligned) and red: 512 floats of LDS scratch outside the logits.
+template <int ROWS>
+__device__ void route_epilogue_top1(float* lg, int ldl, int* tok, float* red, int rows, int64_t t0, int N,
+                                    const float* __restrict__ bias, int32_t* __restrict__ expert_id,
+                                    float* __restrict__ gate, float* __restrict__ part_p,
+                                    int32_t* __restrict__ part_cnt, int64_t blk, int32_t* __restrict__ ev_cm,
+                                    float* __restrict__ gv_cm) {
+  constexpr int TPT = kRouteThreads / ROWS;  // lanes per token
+  constexpr int L = 64 / TPT;                // lane-slots per lane
+  constexpr int CH = L / 4;                  // 16-byte chunks per half (experts < 64, >= 64)
+  static_assert(TPT == 4 || TPT == 8 || TPT == 16, "16, 32 or 64 tokens per workgroup");
+  const int m = threadIdx.x / TPT, q = threadIdx.x % TPT;
+  // chunk i of a half is read at position (i + rot) % CH, which puts the lanes
+  // of an LDS request on distinct 16-byte bank groups (16 lanes over 256 bytes,
+  // and any 8 over 128)
+  int rot = 0;
+  if constexpr (TPT == 4) rot = ((m & 3) + 2 * (q >> 1)) & 3;
+  if constexpr (TPT == 8) rot = ((m & 1) + (q >> 2)) & 1;
+  const float* row = lg + m * ldl + q * L;
+  float lo[L], hi[L];  // experts q L + i and 64 + q L + i
+  int nb[2][CH];
+  float best = -INFINITY;
+  int bi = 0x7fffffff;
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int cc = CH > 1 ? (i + rot) % CH : 0;
+      const int n0 = hh * 64 + q * L + cc * 4;
+      nb[hh][i] = n0;
+      // chunks at or past N (then also past the row's ldl floats) are not read
+      const f32x4 x4 = n0 < N ? *reinterpret_cast<const f32x4*>(row + hh * 64 + cc * 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int n = n0 + u;
+        const float val = n < N ? x4[u] + (bias != nullptr ? bias[n] : 0.f) : -INFINITY;
+        if (hh == 0) lo[i * 4 + u] = val;  // register slot i: chunk cc (see the sums)
+        else hi[i * 4 + u] = val;
+        if (n < N && (val > best || (val == best && n < bi))) {
+          best = val;
+          bi = n;
+        }
+      }
+    }
+  argmax_step<kDppQuadXor1, 0xf>(best, bi);
+  argmax_step<kDppQuadXor2, 0xf>(best, bi);
+  if constexpr (TPT >= 8) argmax_step<kDppHalfMirror, 0xf>(best, bi);
+  if constexpr (TPT == 16) argmax_step<kDppMirror, 0xf>(best, bi);
+  // exp, then the slot sums in slot order (register chunk i holds slots of
+  // chunk (i + rot) % CH, so slot j of this lane is chunk j / 4 - rot)
+  float e[2][L];
+  float sl[L];
+#pragma unroll
+  for (int i = 0; i < CH; ++i)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      e[0][i * 4 + u] = __expf(lo[i * 4 + u] - best);  // -inf (n >= N) -> 0
+      e[1][i * 4 + u] = __expf(hi[i * 4 + u] - best);
+    }
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    const int i = CH > 1 ? (j - rot + CH) % CH : 0;  // register chunk holding slot chunk j
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+      for (int r = 0; r < CH; ++r)
+        if (r == i) {
+          a0 = e[0][r * 4 + u];
+          a1 = e[1][r * 4 + u];
+        }
+      sl[j * 4 + u] = a0 + a1;
+    }
+  }
+#pragma unroll
+  for (int w2 = 1; w2 < L; w2 *= 2)
+#pragma unroll
+    for (int i = 0; i < L; i += 2 * w2) sl[i] = sl[i] + sl[i + w2];
+  float sum = sl[0];
+  sum += __int_as_float(dpp_move<kDppQuadXor1>(0, __float_as_int(sum)));
+  sum += __int_as_float(dpp_move<kDppQuadXor2>(0, __float_as_int(sum)));
+  if constexpr (TPT >= 8) sum += __int_as_float(dpp_move<kDppHalfMirror>(0, __float_as_int(sum)));
+  if constexpr (TPT == 16) sum += __int_as_float(dpp_move<kDppMirror>(0, __float_as_int(sum)));
+  const float inv = 1.0f / sum;
+  const bool valid = m < rows;
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      f32x4 p4;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) p4[u] = e[hh][i * 4 + u] * inv;
+      if (nb[hh][i] < N) *reinterpret_cast<f32x4*>(lg + m * ldl + nb[hh][i]) = p4;
+    }
+  if (q == 0) {
+    tok[m] = valid ? bi : -1;
+    if (valid) {
+      expert_id[t0 + m] = bi;
+      gate[t0 + m] = inv;
+      if (ev_cm != nullptr) {
+        ev_cm[t0 + m] = bi;
+        gv_cm[t0 + m] = inv;
+      }
+    }
+  }
+  __syncthreads();
+  {
+    // fixed trip counts, so that all reads of a loop are in flight together
+    // (a loop bounded by rows waited for each read in turn)
+    const int n = threadIdx.x & 127, h = threadIdx.x >> 7;
+    float s0 = 0.f, s1 = 0.f;  // S_{2h}, S_{2h+1}
+    int cn = 0;
+    if (n < N) {
+#pragma unroll
+      for (int k = 0; k < ROWS / 4; ++k) {
+        const int m0 = 4 * k + 2 * h;
+        const float a = lg[m0 * ldl + n], b = lg[(m0 + 1) * ldl + n];
+        if (m0 < rows) s0 += a;
+        if (m0 + 1 < rows) s1 += b;
+      }
+      if (h == 0) {
+#pragma unroll
+        for (int k = 0; k < ROWS / 4; ++k) {  // token ids past rows are -1
+          const u32x4 t4 = *reinterpret_cast<const u32x4*>(tok + 4 * k);
+          cn += ((int)t4[0] == n ? 1 : 0) + ((int)t4[1] == n ? 1 : 0) + ((int)t4[2] == n ? 1 : 0) +
+                ((int)t4[3] == n ? 1 : 0);
+        }
+      }
+    }
+    red[(2 * h) * 128 + n] = s0;
+    red[(2 * h + 1) * 128 + n] = s1;
+    if (h == 0 && n < N) part_cnt[blk * N + n] = cn;
+  }
+  __syncthreads();
+  if (threadIdx.x < N) {
+    const int n = threadIdx.x;
+    part_p[blk * N + n] = ((red[n] + red[128 + n]) + red[256 + n]) + red[384 + n];
+  }
+}
+
+// plain top-1: no per-token probabilities, further choices or candidates
+__device__ __forceinline__ bool route_plain_top1(const RouteExtra& ex) {
+  return ex.K <= 1 && !ex.expand && ex.probs == nullptr && ex.probs_t == nullptr;
+}
+
 // ----------------------------------------------------------------------------
 // fused bf16 router.  lane l: c = l & 15 selects the A row / B column, kg = l >> 4
 // selects 8 consecutive k.  A = x rows (k contiguous), B = W_g^T, whose
@@ -291,7 +453,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_fused_bf16(
       }
   }
   __syncthreads();
-  route_epilogue<J>(lg, ldl, TM * 16, t0, T, N, bias, expert_id, gate, part_p, part_cnt, blockIdx.x, ex);
+  if (N <= 128 && route_plain_top1(ex)) {  // scratch after the logits (the staged rows, if any, are dead)
+    float* scr = smem + TM * 16 * ldl;
+    route_epilogue_top1<TM * 16>(lg, ldl, reinterpret_cast<int*>(scr), scr + 64, (int)rows_here, t0, N, bias,
+                                 expert_id, gate, part_p, part_cnt, blockIdx.x, ex.ev_cm, ex.gv_cm);
+  } else {
+    route_epilogue<J>(lg, ldl, TM * 16, t0, T, N, bias, expert_id, gate, part_p, part_cnt, blockIdx.x, ex);
+  }
 }
 
 // ----------------------------------------------------------------------------
@@ -385,7 +553,13 @@ __global__ __launch_bounds__(kRouteThreads, 1) void route_kslice_bf16(
   for (int q = threadIdx.x; q < REG; q += kRouteThreads)
     smem[q] = ((smem[q] + smem[REG + q]) + smem[2 * REG + q]) + smem[3 * REG + q];
   __syncthreads();
-  route_epilogue<J>(smem, ldl, TM * 16, t0, T, N, bias, expert_id, gate, part_p, part_cnt, blockIdx.x, ex);
+  if (route_plain_top1(ex)) {  // the other quarters' regions are free for its scratch
+    const int64_t rows_here = (T - t0) < TM * 16 ? (T - t0) : TM * 16;
+    route_epilogue_top1<TM * 16>(smem, ldl, reinterpret_cast<int*>(smem + REG), smem + 2 * REG, (int)rows_here, t0, N,
+                                 bias, expert_id, gate, part_p, part_cnt, blockIdx.x, ex.ev_cm, ex.gv_cm);
+  } else {
+    route_epilogue<J>(smem, ldl, TM * 16, t0, T, N, bias, expert_id, gate, part_p, part_cnt, blockIdx.x, ex);
+  }
 }
 
 // ----------------------------------------------------------------------------
@@ -551,7 +725,11 @@ __global__ __launch_bounds__(kRouteThreads, 1) void route_stream_bf16(
 #pragma unroll
       for (int i = 0; i < 4; ++i) lg[(mt * 16 + kg * 4 + i) * ldl + (w * NG + g) * 16 + c] = acc[mt][g][i];
   __syncthreads();
-  route_epilogue<J>(lg, ldl, ROWS, t0, T, N, bias, expert_id, gate, part_p, part_cnt, blockIdx.x, ex);
+  if (route_plain_top1(ex))  // the other chunk buffers are free for its scratch
+    route_epilogue_top1<ROWS>(lg, ldl, reinterpret_cast<int*>(xb1), reinterpret_cast<float*>(xb2), (int)rows_here, t0, N,
+                              bias, expert_id, gate, part_p, part_cnt, blockIdx.x, ex.ev_cm, ex.gv_cm);
+  else
+    route_epilogue<J>(lg, ldl, ROWS, t0, T, N, bias, expert_id, gate, part_p, part_cnt, blockIdx.x, ex);
 }
 
 // ----------------------------------------------------------------------------
@@ -986,7 +1164,8 @@ static hipError_t launch_route_j(const RoutePlan& pl, const void* x, const void*
                                  const RouteExtra& ex) {
   if (dtype == 1 && pl.split == 0) {
     const int NT = (N + 15) / 16;
-    const size_t lds = (size_t)pl.tm * 16 * NT * 16 * 4;
+    // the logits, then the top-1 epilogue's scratch (64 token ids, 512 sums)
+    const size_t lds = (size_t)pl.tm * 16 * NT * 16 * 4 + 4096;
     const size_t xl_bytes = (size_t)pl.tm * 16 * d * 2;  // the token rows of a workgroup
     // the XOR swizzle of the staged rows (row & 15 over 16-byte chunks) is a
     // bijection only when a row holds a multiple of 16 chunks: d % 128 == 0
