@@ -65,13 +65,13 @@ FFN_SOURCES = ("switch_top_routed_amd/csrc/expert_ffn.hip", "switch_top_routed_a
 # profiles/*_hbm_traffic.md.
 TRAFFIC = {
     "switch-base-uniform": {
-        "sources_sha256": "0d519c177a34f984ce871c158551c41b333b8582de73f98cd133de1c504359df",
-        "fetch_kib": [305815.0, 315422.0], "write_kib": [24109.0, 6027.0],
+        "sources_sha256": "405b37e1e4e7b66a64e30dd92e13275bf3d4daaf687b4087b55735cef8c60b29",
+        "fetch_kib": [305819.4, 315686.1], "write_kib": [24108.6, 6027.0],
         "fetch_scale": 2.0, "write_scale": 1.0,
     },
     "switch-large-shared": {
-        "sources_sha256": "0d519c177a34f984ce871c158551c41b333b8582de73f98cd133de1c504359df",
-        "fetch_kib": [5345023.0, 5420117.0], "write_kib": [262145.0, 163840.0],
+        "sources_sha256": "405b37e1e4e7b66a64e30dd92e13275bf3d4daaf687b4087b55735cef8c60b29",
+        "fetch_kib": [5366621.4, 5439252.8], "write_kib": [262148.0, 163840.0],
         "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
