@@ -82,13 +82,13 @@ TRAFFIC = {
 BWD_SOURCES = ("switch_top_routed_amd/csrc/backward_fused.hip", "switch_top_routed_amd/csrc/common.hpp")
 BWD_TRAFFIC = {
     "switch-base-uniform": {
-        "sources_sha256": "f019f7dee3cd11f15edc95fad08c0221bb3c792f675aaf811058b458a711525d",
-        "fetch_kib": [322801.2, 313118.8], "write_kib": [614901.1, 601878.9],
+        "sources_sha256": "5a1e0367bc876009e75bc64ae5e90adffbeb7467d853bb1863d91e8be95643ae",
+        "fetch_kib": [322815.7, 314168.8], "write_kib": [614961.2, 601878.8],
         "fetch_scale": 2.0, "write_scale": 1.0,
     },
     "switch-large-shared": {
-        "sources_sha256": "f019f7dee3cd11f15edc95fad08c0221bb3c792f675aaf811058b458a711525d",
-        "fetch_kib": [5871750.4, 5811617.3], "write_kib": [10761241.9, 10813443.0],
+        "sources_sha256": "5a1e0367bc876009e75bc64ae5e90adffbeb7467d853bb1863d91e8be95643ae",
+        "fetch_kib": [6111479.6, 5790485.9], "write_kib": [10778442.9, 10813451.3],
         "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
