@@ -11,6 +11,8 @@ mechanism and Load balancing).
   and the K-sliced one (otherwise), at both tile heights (32 and 64 tokens
   per workgroup), with a ragged last tile and N not a multiple of 16.
 Expert ids and counts bit-exact, gate / P / L_aux at the router tolerances.
+Plus: the plain forward's top-1 epilogue and the training forward's general
+epilogue give bit-identical routing, statistics and outputs on every kernel.
 """
 import math
 
@@ -53,3 +55,35 @@ def test_route_shapes(T, d, N, bias_scale):
     o = sw.switch_route(dev(inp.x, "bf16"), dev(inp.w_gate, "bf16"), bias)
     torch.cuda.synchronize()
     check_routing(o, ref, N)
+
+
+# (T, d_model, N): the fused kernel with staged rows (16 tokens per workgroup), the
+# streaming kernel at 32 and 64 tokens per workgroup, and the K-sliced kernel
+EPILOGUE_CASES = [(4096, 768, 128), (4096, 256, 40), (8200, 2048, 100), (16400, 2048, 128), (16400, 2560, 120)]
+
+
+@pytest.mark.parametrize("T,d,N", EPILOGUE_CASES)
+def test_top1_epilogues_agree(T, d, N):
+    """The plain forward ends the router with the several-lanes-per-token top-1
+    epilogue; the training forward (probabilities saved) with the general one.
+    Both must give the same expert ids, gates and statistics bit for bit."""
+    import switch_top_routed_amd as sw
+    from tests.gpu_util import host_bits
+
+    F = 128
+    wl = workloads.Workload(f"epi-{T}x{d}x{N}", T, d, F, N, 1.0, "bf16", 1.0 / math.sqrt(d), bias_scale=0.5,
+                            seed=30_000 + T + d + N)
+    print(f"[case] epilogues T={T} d={d} N={N}", flush=True)
+    inp = inputs_util.conditioned_inputs(wl, weights=False)
+    rng = np.random.default_rng(wl.seed + 1)
+    w1 = torch.from_numpy((rng.standard_normal((N, d, F)) / math.sqrt(d)).astype(np.float32)).cuda().to(torch.bfloat16)
+    w2 = torch.from_numpy((rng.standard_normal((N, F, d)) / math.sqrt(F)).astype(np.float32)).cuda().to(torch.bfloat16)
+    x, wg = dev(inp.x, "bf16"), dev(inp.w_gate, "bf16")
+    bias = None if inp.bias is None else torch.from_numpy(inp.bias).cuda()
+    plain = sw.SwitchMoE(T, d, F, N, dtype=torch.bfloat16, capacity_factor=1.0)
+    a = {k: v.clone() for k, v in plain(x, wg, w1, w2, bias=bias).items()}
+    train = sw.SwitchMoE(T, d, F, N, dtype=torch.bfloat16, capacity_factor=1.0, train=True)
+    b = train.forward_train(x, wg, w1, w2, bias=bias)
+    torch.cuda.synchronize()
+    for k in ("expert_id", "gate", "routed_count", "f", "P", "l_aux", "y"):
+        np.testing.assert_array_equal(host_bits(a[k]), host_bits(b[k]), err_msg=k)
