@@ -693,17 +693,37 @@ static switch_status moe_forward(const switch_moe_desc* desc, const switch_moe_i
   if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/expert_ffn");
   if ((e = mark(4)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
   void* sout = nullptr;
+  // top-1 token choice with a shared expert on the tiled GEMM: its second GEMM
+  // does the combine as it writes S, so S never goes to memory and no combine
+  // kernel runs (the events 5 and 6 then bracket nothing)
+  const bool fused_combine = d.d_ff_shared > 0 && !L.ec && L.K == 1 && d.dtype == SWITCH_BF16 &&
+                             tiled_ffn_applies((int)d.T, d.d_model, d.d_ff_shared);
   if (d.d_ff_shared > 0) {
     int32_t* dk = reinterpret_cast<int32_t*>(w + L.off_dense);
     e = launch_dense_plan(dk, dk + 1, dk + 2, (int32_t)d.T, st);
     if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/shared_plan");
     sout = w + L.off_sout;
+    CombineArgs cmb;
+    if (fused_combine) {
+      cmb.eo = static_cast<const uint16_t*>(xout);
+      cmb.x = static_cast<const uint16_t*>(in->x);
+      cmb.expert_id = out->expert_id;
+      cmb.slot = out->slot;
+      cmb.gate = out->gate;
+      cmb.N = d.N;
+      cmb.C = C;
+      cmb.flags = d.flags;
+      cmb.y = static_cast<uint16_t*>(out->y);
+    }
     e = launch_ffn(L.sffn, in->x, in->ws1, in->ws2, d.dtype, 1, (int)d.T, d.d_model, d.d_ff_shared, dk, dk + 1,
-                   dk + 2, sout, w + L.off_sffn, st, nullptr, 0, sv != nullptr ? sv->h_shared : nullptr);
+                   dk + 2, sout, w + L.off_sffn, st, nullptr, 0, sv != nullptr ? sv->h_shared : nullptr, nullptr,
+                   nullptr, fused_combine ? &cmb : nullptr);
     if (e != hipSuccess) return hip_fail(e, "switch_moe_forward/shared_ffn");
   }
   if ((e = mark(5)) != hipSuccess) return hip_fail(e, "switch_moe_forward/event");
-  if (L.ec)
+  if (fused_combine)
+    e = hipSuccess;
+  else if (L.ec)
     e = launch_combine_picks(1, xout, in->x, sout, d.dtype, d.T, d.d_model, 1, nullptr, nullptr, nullptr,
                              reinterpret_cast<const int32_t*>(w + L.off_pick), rex.probs_t, d.N, C, d.flags,
                              out->slot, out->n_dropped, out->y, st);

@@ -534,9 +534,12 @@ static hipError_t gemm_bf16(const FfnPlan& pl, const void* A, const void* W, voi
 hipError_t launch_ffn(const FfnPlan& pl, const void* xin, const void* w1, const void* w2, int dtype, int N, int C, int d,
                       int dff, const int32_t* kept_count, const int32_t* active, const int32_t* n_active, void* xout,
                       char* ws, hipStream_t st, const int32_t* gather, int64_t a_rows, void* h_out,
-                      const MxWeights* mx, const ActiveFromKept* afk) {
+                      const MxWeights* mx, const ActiveFromKept* afk, const CombineArgs* cmb) {
   void* h = h_out != nullptr ? h_out : static_cast<void*>(ws + pl.off_h);
   if (afk != nullptr && !ffn_stream_applies(dtype, C, d, dff, mx != nullptr)) return hipErrorInvalidValue;
+  // the fused combine exists on the tiled path only (the caller checks tiled_ffn_applies)
+  if (cmb != nullptr && cmb->y != nullptr && (dtype != 1 || mx != nullptr || !tiled_ffn_applies(C, d, dff)))
+    return hipErrorInvalidValue;
   if (mx != nullptr)  // MXFP4 weights (bf16 activations; the caller checked mx_ffn_applies)
     return launch_ffn_mx(xin, *mx, N, C, d, dff, kept_count, active, n_active, xout, h, st, gather, a_rows,
                          afk != nullptr ? *afk : ActiveFromKept{});
@@ -554,7 +557,7 @@ hipError_t launch_ffn(const FfnPlan& pl, const void* xin, const void* w1, const 
   if (tiled_ffn_applies(C, d, dff)) {
     hipError_t e = launch_tiled_dma(xin, w1, h, kept_count, active, n_active, N, C, d, dff, 1, st, gather, a_rows);
     if (e != hipSuccess) return e;
-    return launch_tiled_dma(h, w2, xout, kept_count, active, n_active, N, C, dff, d, 0, st);
+    return launch_tiled_dma(h, w2, xout, kept_count, active, n_active, N, C, dff, d, 0, st, nullptr, 0, cmb);
   }
   // The hidden matrix stays in the library's workspace unless the caller keeps
   // it (training); then it is row-major [N, C, d_ff] as documented.  In the

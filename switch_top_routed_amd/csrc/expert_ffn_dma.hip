@@ -71,17 +71,60 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const unsigned char* lds) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)lds));
 }
 
+// y piece (8 bf16) of token t at column col from the S piece sv: the same
+// arithmetic, in the same order, as combine_rows (dispatch_combine.hip), so the
+// fused layer is bit-identical to the separate combine
+__device__ __forceinline__ void combine_piece(const CombineArgs& cb, const u32x4& sv, int64_t t, int col, int d) {
+  const int s = cb.slot[t];
+  const int e = s >= 0 ? cb.expert_id[t] : 0;
+  const bool kept = s >= 0 && s < cb.C && e >= 0 && e < cb.N;
+  const float scale = (cb.flags & SWITCH_GATE_SCALE) ? cb.gate[t] : 1.0f;
+  const bool res = (cb.flags & SWITCH_RESIDUAL_ALL) != 0;
+  const bool need_x = !kept || res;
+  const u32x4 xv = need_x ? *reinterpret_cast<const u32x4*>(cb.x + t * d + col) : u32x4{0u, 0u, 0u, 0u};
+  const u32x4 ov = kept ? *reinterpret_cast<const u32x4*>(cb.eo + ((int64_t)e * cb.C + s) * d + col)
+                        : u32x4{0u, 0u, 0u, 0u};
+  float v[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    v[2 * q] = bf2f(xv[q] & 0xffffu);
+    v[2 * q + 1] = bf2f(xv[q] >> 16);
+  }
+  if (kept) {
+    float o[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      o[2 * q] = bf2f(ov[q] & 0xffffu);
+      o[2 * q + 1] = bf2f(ov[q] >> 16);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = res ? v[q] + scale * o[q] : scale * o[q];
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    v[2 * q] += bf2f(sv[q] & 0xffffu);
+    v[2 * q + 1] += bf2f(sv[q] >> 16);
+  }
+  u32x4 out;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) out[q] = pack_bf2(v[2 * q], v[2 * q + 1]);
+  __builtin_nontemporal_store(out, reinterpret_cast<u32x4*>(cb.y + t * d + col));
+}
+
 }  // namespace
 
 // MTW m-tiles x NJ n-tiles of 16 x 16 per wave (2 x WN waves): a BM = 32 MTW
 // by TN = 16 NJ WN tile; S LDS stages.  WNT: the weights are read once per
 // launch (one m-chunk per expert), so their loads carry the non-temporal policy
 // and leave the caches to the token rows, which every column block re-reads.
-template <int MTW, int NJ, int S, bool WNT, int WN>
+// CMB: the dense (shared-expert) second GEMM also does the top-1 combine
+// (CombineArgs): each 16-byte piece of S becomes the piece of y.
+template <int MTW, int NJ, int S, bool WNT, int WN, bool CMB>
 __global__ __launch_bounds__(128 * WN, WN > 2 || MTW * NJ >= 48 ? 1 : 2) void ffn_tile_dma(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, uint16_t* __restrict__ out,
     const int32_t* __restrict__ kept_count, const int32_t* __restrict__ active, const int32_t* __restrict__ n_active,
-    int N, int C, int K, int Ncols, int relu, int mch, const int32_t* __restrict__ gather, int64_t a_rows) {
+    int N, int C, int K, int Ncols, int relu, int mch, const int32_t* __restrict__ gather, int64_t a_rows,
+    CombineArgs cmb) {
   constexpr int NWV = 2 * WN;          // waves
   constexpr int BM = 32 * MTW, TN = 16 * NJ * WN;
   constexpr int AB = BM / 16;          // 1 KB blocks of A per stage (16 rows each)
@@ -281,9 +324,12 @@ __global__ __launch_bounds__(128 * WN, WN > 2 || MTW * NJ >= 48 ? 1 : 2) void ff
       const int q = q0 + lane, r = q / CH, ch = q - r * CH;
       const int rl = wm * (BM / 2) + mt * 16 + r;
       const u32x4 v = *reinterpret_cast<const u32x4*>(ost + r * ROWB + ch * 16);
-      if (rl < rows)
+      if constexpr (CMB) {
+        if (rl < rows) combine_piece(cmb, v, (int64_t)m0 + rl, n0 + wn * 16 * NJ + ch * 8, Ncols);
+      } else if (rl < rows) {
         __builtin_nontemporal_store(
             v, reinterpret_cast<u32x4*>(out + ((int64_t)e * C + m0 + rl) * Ncols + n0 + wn * 16 * NJ + ch * 8));
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();  // the next slice overwrites the region
@@ -294,20 +340,24 @@ __global__ __launch_bounds__(128 * WN, WN > 2 || MTW * NJ >= 48 ? 1 : 2) void ff
 template <int MTW, int NJ, int S, int WN = 2>
 static hipError_t launch_dma(const void* A, const void* W, void* out, const int32_t* kept, const int32_t* active,
                              const int32_t* n_active, int N, int C, int K, int Ncols, int relu, hipStream_t st,
-                             const int32_t* gather, int64_t a_rows) {
+                             const int32_t* gather, int64_t a_rows, const CombineArgs* cmb = nullptr) {
   constexpr int BM = 32 * MTW, TN = 16 * NJ * WN;
   const int mch = (C + BM - 1) / BM;
   int64_t grid = (int64_t)N * mch * (Ncols / TN);
   grid = (grid + kDmaXcds - 1) / kDmaXcds * kDmaXcds;
+  const auto* a = static_cast<const uint16_t*>(A);
+  const auto* w = static_cast<const uint16_t*>(W);
+  auto* o = static_cast<uint16_t*>(out);
   // one m-chunk per expert: each weight panel is streamed by exactly one tile
-  if (mch == 1)
-    hipLaunchKernelGGL((ffn_tile_dma<MTW, NJ, S, true, WN>), dim3((unsigned)grid), dim3(128 * WN), 0, st,
-                       static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(W), static_cast<uint16_t*>(out),
-                       kept, active, n_active, N, C, K, Ncols, relu, mch, gather, a_rows);
+  if (cmb != nullptr && cmb->y != nullptr)
+    hipLaunchKernelGGL((ffn_tile_dma<MTW, NJ, S, false, WN, true>), dim3((unsigned)grid), dim3(128 * WN), 0, st, a, w,
+                       o, kept, active, n_active, N, C, K, Ncols, relu, mch, gather, a_rows, *cmb);
+  else if (mch == 1)
+    hipLaunchKernelGGL((ffn_tile_dma<MTW, NJ, S, true, WN, false>), dim3((unsigned)grid), dim3(128 * WN), 0, st, a,
+                       w, o, kept, active, n_active, N, C, K, Ncols, relu, mch, gather, a_rows, CombineArgs{});
   else
-    hipLaunchKernelGGL((ffn_tile_dma<MTW, NJ, S, false, WN>), dim3((unsigned)grid), dim3(128 * WN), 0, st,
-                       static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(W), static_cast<uint16_t*>(out),
-                       kept, active, n_active, N, C, K, Ncols, relu, mch, gather, a_rows);
+    hipLaunchKernelGGL((ffn_tile_dma<MTW, NJ, S, false, WN, false>), dim3((unsigned)grid), dim3(128 * WN), 0, st, a,
+                       w, o, kept, active, n_active, N, C, K, Ncols, relu, mch, gather, a_rows, CombineArgs{});
   return hipGetLastError();
 }
 
@@ -330,7 +380,11 @@ bool tiled_ffn_applies(int C, int d, int dff) { return C > 64 && d % 256 == 0 &&
 // +-5% of it, one GEMM faster and the other slower).
 hipError_t launch_tiled_dma(const void* A, const void* W, void* out, const int32_t* kept, const int32_t* active,
                             const int32_t* n_active, int N, int C, int K, int Ncols, int relu, hipStream_t st,
-                            const int32_t* gather, int64_t a_rows) {
+                            const int32_t* gather, int64_t a_rows, const CombineArgs* cmb) {
+  if (cmb != nullptr && cmb->y != nullptr) {  // the dense second GEMM with the combine: the default tile
+    if (N != 1) return hipErrorInvalidValue;
+    return launch_dma<4, 8, 3>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st, gather, a_rows, cmb);
+  }
   if (C > 128 && C <= 160) {
     if (Ncols % 512 == 0)
       return launch_dma<5, 8, 3, 4>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st, gather, a_rows);

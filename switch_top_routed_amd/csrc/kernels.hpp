@@ -103,11 +103,26 @@ struct ActiveFromKept {
   float* l_aux = nullptr;
   int64_t TV = 0;  // choices in the assignment list (T K)
 };
+// The top-1 combine (combine_rows' arithmetic) done by the shared expert's
+// second GEMM as it writes each row of its output S: y[t] = (x[t] if the token
+// was dropped or RESIDUAL_ALL) + (s_t o_t if kept) + S[t], with o_t the routed
+// expert's output row.  y == NULL: off (the GEMM writes S).
+struct CombineArgs {
+  const uint16_t* eo = nullptr;  // routed expert outputs [N][C][d]
+  const uint16_t* x = nullptr;   // token rows [T][d]
+  const int32_t* expert_id = nullptr;
+  const int32_t* slot = nullptr;
+  const float* gate = nullptr;
+  int N = 0, C = 0;
+  uint32_t flags = 0;
+  uint16_t* y = nullptr;  // [T][d]
+};
 bool ffn_stream_applies(int dtype, int C, int d, int dff, bool mx);
 hipError_t launch_ffn(const FfnPlan& pl, const void* xin, const void* w1, const void* w2, int dtype, int N, int C, int d,
                       int dff, const int32_t* kept_count, const int32_t* active, const int32_t* n_active, void* xout,
                       char* ws, hipStream_t st, const int32_t* gather = nullptr, int64_t a_rows = 0,
-                      void* h_out = nullptr, const MxWeights* mx = nullptr, const ActiveFromKept* afk = nullptr);
+                      void* h_out = nullptr, const MxWeights* mx = nullptr, const ActiveFromKept* afk = nullptr,
+                      const CombineArgs* cmb = nullptr);
 bool mx_ffn_applies(int C, int d, int dff);
 hipError_t launch_ffn_mx(const void* xin, const MxWeights& mw, int N, int C, int d, int dff,
                          const int32_t* kept_count, const int32_t* active, const int32_t* n_active, void* xout,
@@ -121,7 +136,7 @@ hipError_t launch_mx_quantize(const void* w, int dtype, int64_t batches, int K, 
 bool tiled_ffn_applies(int C, int d, int dff);
 hipError_t launch_tiled_dma(const void* A, const void* W, void* out, const int32_t* kept, const int32_t* active,
                             const int32_t* n_active, int N, int C, int K, int Ncols, int relu, hipStream_t st,
-                            const int32_t* gather = nullptr, int64_t a_rows = 0);
+                            const int32_t* gather = nullptr, int64_t a_rows = 0, const CombineArgs* cmb = nullptr);
 hipError_t launch_dense_plan(int32_t* kept, int32_t* active, int32_t* n_active, int32_t M, hipStream_t st);
 
 // ---------------- backward ----------------

@@ -208,12 +208,20 @@ def test_base_layer_deterministic_and_poison_proof(base):
 
 def _staged_layer(wl, d, C, priority="token", gate_scale=True):
     """The layer composed from the per-stage entry points (router, assignment,
-    dispatch, expert FFN, combine), for comparison with switch_moe_forward."""
+    dispatch, expert FFN, the shared expert as a one-expert FFN over all tokens,
+    combine), for comparison with switch_moe_forward."""
     r = sw.switch_route(d["x"], d["w_gate"], d["bias"])
     a = sw.switch_assign_capacity(r["expert_id"], r["gate"], wl.N, C, priority)
     xin = sw.switch_dispatch(d["x"], a["token_of_slot"], a["kept_count"], wl.N, C)
     xout = sw.switch_expert_ffn(xin, d["w1"], d["w2"], a["kept_count"], a["active"], a["n_active"])
-    y = sw.switch_combine(xout, d["x"], r["expert_id"], a["slot"], r["gate"], native.GATE_SCALE if gate_scale else 0)
+    shared = None
+    if wl.d_ff_shared:
+        T, dm, fs = wl.T, wl.d_model, wl.d_ff_shared
+        one = lambda v: torch.tensor([v], dtype=torch.int32, device="cuda")
+        shared = sw.switch_expert_ffn(d["x"].view(1, T, dm), d["ws1"].view(1, dm, fs), d["ws2"].view(1, fs, dm),
+                                      one(T), one(0), one(1)).view(T, dm)
+    flags = (native.GATE_SCALE if gate_scale else 0) | (native.RESIDUAL_ALL if wl.residual_all else 0)
+    y = sw.switch_combine(xout, d["x"], r["expert_id"], a["slot"], r["gate"], flags, shared_out=shared)
     torch.cuda.synchronize()
     return dict(r, **a, y=y)
 
@@ -230,7 +238,8 @@ def test_base_layer_matches_staged_path(base):
         np.testing.assert_array_equal(host_bits(o[k]), host_bits(st[k]), err_msg=k)
 
 
-@pytest.mark.parametrize("name", ["ragged", "f32-odd", "n1000", "tiled-c150", "tiled-c150-wide", "f32-many-tiles"])
+@pytest.mark.parametrize("name", ["ragged", "f32-odd", "n1000", "tiled-c150", "tiled-c150-wide", "f32-many-tiles",
+                                  "shared-drops", "shared-residual", "shared-gate-noscale"])
 def test_edge_layer_matches_staged_path(name):
     wl = next(w for w in EDGE if w.name == name)
     _say(f"edge layer vs staged path {name}")
@@ -309,6 +318,12 @@ EDGE = [
     _custom("tiled-c150-wide", 1200, 512, 1536, 8, 1.0, seed=16, bias_scale=0.5),  # C = 150: 160 x 512 tiles on 8 waves, both GEMMs
     _custom("tiled-c180", 1440, 512, 256, 8, 1.0, seed=14, priority="gate"),    # C = 180: two 128-row m-chunks
     _custom("tiled-c200", 1600, 512, 256, 8, 1.0, seed=12, priority="gate"),    # C = 200: two 128-row m-chunks
+    # a shared expert on the tiled GEMM: its second GEMM also does the combine (dropped
+    # tokens, the residual flag, gate order without gate scaling)
+    _custom("shared-drops", 1000, 256, 384, 16, 0.5, seed=21, d_ff_shared=256),
+    _custom("shared-residual", 700, 256, 256, 8, 0.5, seed=22, residual_all=True, d_ff_shared=512),
+    _custom("shared-gate-noscale", 900, 256, 256, 8, 0.8, seed=23, priority="gate", gate_scale=False,
+            d_ff_shared=256),
     # token-order assignment: 1250 router tiles (two LDS chunks of partials), one tile
     # group per expert (N = 1024), tokens in two 16K chunks
     _custom("f32-many-tiles", 20000, 32, 64, 1024, 1.0, dtype="f32", seed=16),
