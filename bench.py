@@ -65,13 +65,13 @@ FFN_SOURCES = ("switch_top_routed_amd/csrc/expert_ffn.hip", "switch_top_routed_a
 # profiles/*_hbm_traffic.md.
 TRAFFIC = {
     "switch-base-uniform": {
-        "sources_sha256": "405b37e1e4e7b66a64e30dd92e13275bf3d4daaf687b4087b55735cef8c60b29",
-        "fetch_kib": [305819.4, 315686.1], "write_kib": [24108.6, 6027.0],
+        "sources_sha256": "7c940d215314e6406a76b0ba9066c6b37fbc0e53ceb00e9fb84b79b51e180400",
+        "fetch_kib": [305806.9, 315437.6], "write_kib": [24108.6, 6027.0],
         "fetch_scale": 2.0, "write_scale": 1.0,
     },
     "switch-large-shared": {
-        "sources_sha256": "405b37e1e4e7b66a64e30dd92e13275bf3d4daaf687b4087b55735cef8c60b29",
-        "fetch_kib": [5366621.4, 5439252.8], "write_kib": [262148.0, 163840.0],
+        "sources_sha256": "7c940d215314e6406a76b0ba9066c6b37fbc0e53ceb00e9fb84b79b51e180400",
+        "fetch_kib": [5365989.3, 5437079.2], "write_kib": [262160.3, 163840.0],
         "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
