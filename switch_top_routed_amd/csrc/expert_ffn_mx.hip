@@ -59,6 +59,8 @@ __device__ __forceinline__ u32x4 fp4x8_to_bf16(uint32_t codes, float scale) {
 // E8M0 byte -> 2^(b - 127) as fp32 (b = 0: 2^-127, a subnormal)
 __device__ __forceinline__ float e8m0_to_f32(uint32_t b) { return __uint_as_float(b ? (b << 23) : 0x00400000u); }
 
+// waves that split one item's K: the fewest that fill the device's wave slots,
+// up to `waves`
 __device__ __forceinline__ int mx_waves_per_item(int64_t base, int64_t wave_slots, int waves, int nk) {
   int best = 1;
   for (int kw = 1; kw <= waves; kw *= 2) {
@@ -98,7 +100,12 @@ __global__ __launch_bounds__(WAVES * 64, 2) void ffn_mx_stream(
   const int nk = K >> 7;  // 128-deep steps
   const int64_t base = (int64_t)n_act * NCB * mch;
   if (base <= 0) return;
-  const int KW = mx_waves_per_item(base, (int64_t)gridDim.x * WAVES, WAVES, nk);
+  // one 16-row tile (decode-sized experts): at most 2 waves per item (the
+  // 384-expert decode batch, 14 experts, C = 1: 94 -> 82 us per layer step
+  // against 4; the LDS meeting of more partials costs more than the extra waves
+  // give).  Larger tiles keep up to all 4 (the skewed 17-expert layer at C = 32
+  // was 15% slower with 2)
+  const int KW = mx_waves_per_item(base, (int64_t)gridDim.x * WAVES, MT == 1 && WAVES > 2 ? 2 : WAVES, nk);
   const int groups = WAVES / KW;
   const int g = w / KW, kw = w - g * KW;
   const int nx = (gridDim.x % kMxXcds == 0) ? kMxXcds : 1;
@@ -155,9 +162,13 @@ __global__ __launch_bounds__(WAVES * 64, 2) void ffn_mx_stream(
         a_voff[mt] = rr < rows ? (int)((src * K + kw * 128 + 32 * kg) * 2) : kMxOOR;
       }
       const int q_step = KW * 64, s_step = KW * 4, a_step = KW * 256;
+      // one step's operands: the weight codes and scales and the token-row
+      // fragments, loaded STAGES - 1 steps ahead together (the row fragments one
+      // step ahead left each step waiting on its own row loads)
       struct WStage {
         u32x4 q[4];
         uint32_t s[4];
+        u32x4 a[MT][4];
       };
       auto load_w = [&](WStage& d, int step) {
         const int st = step < myk ? step : myk - 1;  // past the end: re-read the last step (cache hit)
@@ -177,19 +188,19 @@ __global__ __launch_bounds__(WAVES * 64, 2) void ffn_mx_stream(
 #pragma unroll
           for (int q = 0; q < 4; ++q) d[mt][q] = mx_load16(ares, a_voff[mt], st * a_step + q * 16);
       };
-      u32x4 acur[MT][4];
-      load_a(acur, 0);
       WStage ring[STAGES];
 #pragma unroll
-      for (int s = 0; s < STAGES - 1; ++s) load_w(ring[s], s);
+      for (int s = 0; s < STAGES - 1; ++s) {
+        load_w(ring[s], s);
+        load_a(ring[s].a, s);
+      }
       const int nk_pad = (myk + STAGES - 1) / STAGES * STAGES;
       for (int it = 0; it < nk_pad; it += STAGES) {
 #pragma unroll
         for (int u = 0; u < STAGES; ++u) {
           const int cur = it + u;
-          u32x4 anext[MT][4];
-          load_a(anext, cur + 1);
           load_w(ring[(u + STAGES - 1) % STAGES], cur + STAGES - 1);
+          load_a(ring[(u + STAGES - 1) % STAGES].a, cur + STAGES - 1);
           __builtin_amdgcn_sched_barrier(0);
           const bool live = cur < myk;
 #pragma unroll
@@ -201,13 +212,9 @@ __global__ __launch_bounds__(WAVES * 64, 2) void ffn_mx_stream(
               const u32x4 bf = fp4x8_to_bf16(ring[u].q[j][q], sc);
 #pragma unroll
               for (int mt = 0; mt < MT; ++mt)
-                acc[mt][j] = mfma_bf16_16x16x32(live ? acur[mt][q] : zero, bf, acc[mt][j]);
+                acc[mt][j] = mfma_bf16_16x16x32(live ? ring[u].a[mt][q] : zero, bf, acc[mt][j]);
             }
           }
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) acur[mt][q] = anext[mt][q];
         }
       }
     }
@@ -328,7 +335,7 @@ static hipError_t launch_mx_mt(const void* A, const uint8_t* q, const uint8_t* s
                                int relu, hipStream_t st, const int32_t* gather, int64_t a_rows,
                                const ActiveFromKept& afk) {
   constexpr int kWaves = 4;
-  constexpr int kStages = MT <= 2 ? 3 : 2;
+  constexpr int kStages = MT == 1 ? 4 : MT <= 2 ? 3 : 2;  // ring depth within the register budget
   auto kern = ffn_mx_stream<MT, kWaves, kStages>;
   const int mch = (C + MT * 16 - 1) / (MT * 16);
   const int grid = mx_grid(reinterpret_cast<const void*>(kern), kWaves * 64);
