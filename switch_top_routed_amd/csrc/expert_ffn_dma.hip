@@ -375,15 +375,17 @@ bool tiled_ffn_applies(int C, int d, int dff) { return C > 64 && d % 256 == 0 &&
 // stages.  64 < C <= 96: 96 x 256 tiles with 2 stages (top-2 on the base
 // layer, C = 80: 132 us per launch against 138 us with 128 x 256 x 3 and
 // 135-145 us for the other shapes tried).  128 x 256 tiles with 3 stages
-// otherwise, including the shared dense expert (1.14-1.18 ms per GEMM on the
-// large layer; 128 x 512 on 8 waves and 160 x 256 on 8 waves were within
-// +-5% of it, one GEMM faster and the other slower).
+// otherwise.  The dense shared expert runs that tile on 8 waves (2 x 4, 64 x
+// 64 each; two workgroups per CU, four waves per SIMD): the large layer's step
+// went from 6.25 to 6.04 ms against 4 waves (A/B in one process; 6.13 with 2
+// stages, 6.06 with 160 x 256 on 8 waves for GEMM 1).  Timed alone, back to back,
+// 128 x 512 and 160 x 256 on 8 waves had been within +-5% of the 4-wave tile.
 hipError_t launch_tiled_dma(const void* A, const void* W, void* out, const int32_t* kept, const int32_t* active,
                             const int32_t* n_active, int N, int C, int K, int Ncols, int relu, hipStream_t st,
                             const int32_t* gather, int64_t a_rows, const CombineArgs* cmb) {
-  if (cmb != nullptr && cmb->y != nullptr) {  // the dense second GEMM with the combine: the default tile
+  if (cmb != nullptr && cmb->y != nullptr) {  // the dense second GEMM with the combine
     if (N != 1) return hipErrorInvalidValue;
-    return launch_dma<4, 8, 3>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st, gather, a_rows, cmb);
+    return launch_dma<4, 4, 3, 4>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st, gather, a_rows, cmb);
   }
   if (C > 128 && C <= 160) {
     if (Ncols % 512 == 0)
@@ -392,6 +394,8 @@ hipError_t launch_tiled_dma(const void* A, const void* W, void* out, const int32
   }
   if (C > 64 && C <= 96)
     return launch_dma<3, 8, 2>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st, gather, a_rows);
+  if (N == 1)  // the dense shared expert: 128 x 256 on 8 waves
+    return launch_dma<4, 4, 3, 4>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st, gather, a_rows);
   return launch_dma<4, 8, 3>(A, W, out, kept, active, n_active, N, C, K, Ncols, relu, st, gather, a_rows);
 }
 
