@@ -65,13 +65,13 @@ FFN_SOURCES = ("switch_top_routed_amd/csrc/expert_ffn.hip", "switch_top_routed_a
 # profiles/*_hbm_traffic.md.
 TRAFFIC = {
     "switch-base-uniform": {
-        "sources_sha256": "7c940d215314e6406a76b0ba9066c6b37fbc0e53ceb00e9fb84b79b51e180400",
-        "fetch_kib": [305806.9, 315437.6], "write_kib": [24108.6, 6027.0],
+        "sources_sha256": "007d29d65a7d5acacbdfd056b903734a3c5cd4b4a943ddde96d04425295288b1",
+        "fetch_kib": [305813.3, 315572.1], "write_kib": [24108.6, 6027.0],
         "fetch_scale": 2.0, "write_scale": 1.0,
     },
     "switch-large-shared": {
-        "sources_sha256": "7c940d215314e6406a76b0ba9066c6b37fbc0e53ceb00e9fb84b79b51e180400",
-        "fetch_kib": [5365989.3, 5437079.2], "write_kib": [262160.3, 163840.0],
+        "sources_sha256": "007d29d65a7d5acacbdfd056b903734a3c5cd4b4a943ddde96d04425295288b1",
+        "fetch_kib": [5365659.5, 5436823.2], "write_kib": [262159.4, 163840.0],
         "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }
