@@ -53,14 +53,15 @@ __device__ __forceinline__ u32x2 dn_tr16(const unsigned char* lds) {
 
 // out[M][Ncols] = A . B over K.  AT: A stored [K][M]; BNT: B stored [Ncols][K].
 // EPI 0: bf16 out; 1: fp32 out; 2: bf16 out times [H[m][n] > 0] (H bf16 [M][Ncols]).
-// A workgroup (4 waves, 2 x 2) owns a BM x TN tile, BM = 32 MTW, TN = 32 NJ.
-template <int MTW, int NJ, int S, bool AT, bool BNT, int EPI>
-__global__ __launch_bounds__(256, 2) void dense_tile_dma(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
+// A workgroup (2 WN waves, 2 x WN) owns a BM x TN tile, BM = 32 MTW, TN = 16 NJ WN.
+template <int MTW, int NJ, int S, bool AT, bool BNT, int EPI, int WN>
+__global__ __launch_bounds__(128 * WN, WN > 2 ? 1 : 2) void dense_tile_dma(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
                                                          void* __restrict__ out, const uint16_t* __restrict__ H, int M,
                                                          int K, int Ncols, int mch) {
-  constexpr int BM = 32 * MTW, TN = 32 * NJ;
+  constexpr int BM = 32 * MTW, TN = 16 * NJ * WN, NWV = 2 * WN;
   constexpr int AB = BM / 16, WB = TN / 16, NB = AB + WB;
-  constexpr int LW = (NB + 3) / 4;
+  constexpr int LW = (NB + NWV - 1) / NWV;
+  static_assert(NB >= NWV, "every wave loads at least one block");
   constexpr int ARB = BM * 2, BRB = TN * 2;  // bytes per K-row of a K-row tile
   constexpr int SB = NB * 1024;
   static_assert(S >= 2 && S <= 4, "2 to 4 LDS stages");
@@ -72,7 +73,7 @@ __global__ __launch_bounds__(256, 2) void dense_tile_dma(const uint16_t* __restr
 
   const int tid = threadIdx.x, lane = tid & 63, c = lane & 15, kg = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w / WN, wn = w % WN;
   const int NT = Ncols / TN;
   const int64_t tiles = (int64_t)mch * NT;
   const int nx = (gridDim.x % kDenseXcds == 0) ? kDenseXcds : 1;
@@ -103,8 +104,8 @@ __global__ __launch_bounds__(256, 2) void dense_tile_dma(const uint16_t* __restr
   bool is_a[LW];
 #pragma unroll
   for (int i = 0; i < LW; ++i) {
-    int j = w + 4 * i;
-    if (j >= NB) j -= 4;  // repeats block j - 4: same bytes to the same place
+    int j = w + NWV * i;
+    if (j >= NB) j -= NWV;  // repeats block j - NWV: same bytes to the same place
     lds_blk[i] = j * 1024;
     is_a[i] = j < AB;
     if (j < AB) {
@@ -237,8 +238,9 @@ __global__ __launch_bounds__(256, 2) void dense_tile_dma(const uint16_t* __restr
   constexpr int EB = EPI == 1 ? 4 : 2;        // output bytes per element
   constexpr int ROWB = 16 * NJ * EB + 16;     // staged row: the wave's 16 NJ columns
   constexpr int CH = 16 * NJ * EB / 16;       // 16-byte chunks per staged row
-  static_assert(2 * 16 * ROWB <= SB, "two waves' staging fits one LDS stage");
-  unsigned char* ost = (w < 2 ? st0 : st1) + (w & 1) * 16 * ROWB;
+  constexpr int WPS = SB / (16 * ROWB);        // waves staged per LDS stage
+  static_assert(WPS * S >= NWV, "every wave's staging fits the stages");
+  unsigned char* ost = stage(w / WPS) + (w % WPS) * 16 * ROWB;
   const int64_t col0 = (int64_t)n0 + wn * 16 * NJ;
 #pragma unroll
   for (int mt = 0; mt < MTW; ++mt) {
@@ -284,15 +286,15 @@ __global__ __launch_bounds__(256, 2) void dense_tile_dma(const uint16_t* __restr
 }
 
 // ----------------------------------------------------------------------------
-// 128 x 256 tiles, 3 stages (the forward's shared-FFN configuration)
+// 128 x 256 tiles on 8 waves (2 x 4, each 64 x 64), 3 stages: the forward's shared-FFN configuration
 template <bool AT, bool BNT, int EPI>
 static hipError_t launch_dense(const void* A, const void* B, void* out, const void* H, int M, int K, int Ncols,
                                hipStream_t st) {
-  constexpr int MTW = 4, NJ = 8, S = 3, BM = 32 * MTW, TN = 32 * NJ;
+  constexpr int MTW = 4, NJ = 4, S = 3, WN = 4, BM = 32 * MTW, TN = 16 * NJ * WN;
   const int mch = (M + BM - 1) / BM;
   int64_t grid = (int64_t)mch * (Ncols / TN);
   grid = (grid + kDenseXcds - 1) / kDenseXcds * kDenseXcds;
-  hipLaunchKernelGGL((dense_tile_dma<MTW, NJ, S, AT, BNT, EPI>), dim3((unsigned)grid), dim3(256), 0, st,
+  hipLaunchKernelGGL((dense_tile_dma<MTW, NJ, S, AT, BNT, EPI, WN>), dim3((unsigned)grid), dim3(128 * WN), 0, st,
                      static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), out,
                      static_cast<const uint16_t*>(H), M, K, Ncols, mch);
   return hipGetLastError();
