@@ -690,11 +690,14 @@ __global__ __launch_bounds__(kRouteThreads, 1) void route_stream_bf16(
   // chunk ch = ch0 + u (buffer u): every wave is done with chunk ch - 1, whose
   // buffer takes chunk ch + 3; issue W_g of ch + 1 and x of ch + 3, wait for
   // W_g and x of ch (WAIT loads were issued after W_g of ch), publish x of ch,
-  // multiply
+  // multiply.  The W_g loads go out before the x loads: loads retire in order,
+  // so an x load the compiler placed among them would be waited for one chunk
+  // later with the W_g (54.5 -> 53.4 us per route call on 16384 x 5120 tokens)
   auto body = [&](u32x4 (&cur)[KS][NG], u32x4 (&nxt)[KS][NG], int u, int ch) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     issue_w(nxt, ch + 1);
+    asm volatile("" ::: "memory");
     issue_x((u + 3) & 3, ch + 3);
     SWM_RT_WAIT_VMCNT_LGKM0(WAIT);
     asm volatile("" ::: "memory");

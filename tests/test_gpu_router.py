@@ -35,6 +35,8 @@ CASES = [
     (16400, 2048, 128, 1.0),  # streaming, 64 tokens per workgroup, last tile 16 tokens, 8 chunks
     (8192, 4096, 128, 0.0),   # streaming, 32 tokens per workgroup, 16 chunks
     (16400, 5120, 128, 0.0),  # streaming, 64 tokens per workgroup, last tile 16 tokens, 20 chunks
+    (16512, 3072, 100, 1.0),  # streaming, 64 tokens per workgroup, 12 chunks, N ragged
+    (16448, 2048, 72, 0.0),   # streaming, 64 tokens per workgroup, N ragged, 257 workgroups
     (8192, 2560, 96, 1.0),    # K-sliced waves (d % 1024 != 0), 32 tokens per workgroup
     (16400, 2560, 120, 0.0),  # K-sliced waves, 64 tokens per workgroup, last tile 16 tokens
 ]
@@ -59,7 +61,8 @@ def test_route_shapes(T, d, N, bias_scale):
 
 # (T, d_model, N): the fused kernel with staged rows (16 tokens per workgroup), the
 # streaming kernel at 32 and 64 tokens per workgroup, and the K-sliced kernel
-EPILOGUE_CASES = [(4096, 768, 128), (4096, 256, 40), (8200, 2048, 100), (16400, 2048, 128), (16400, 2560, 120)]
+EPILOGUE_CASES = [(4096, 768, 128), (4096, 256, 40), (8200, 2048, 100), (16400, 2048, 128), (16400, 2560, 120),
+                  (16512, 3072, 100)]
 
 
 @pytest.mark.parametrize("T,d,N", EPILOGUE_CASES)

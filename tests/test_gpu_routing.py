@@ -133,6 +133,9 @@ TOPK_EDGE = [
     # 18000 choices: the per-expert token-order assignment's 1024-thread top-K
     # instance over two 16K-choice chunks, with a ragged last chunk
     (_custom("k2-two-chunks", 9000, 128, 128, 16, 1.0, seed=8, bias_scale=0.5), 2),
+    # 16400 tokens with d = 2048: the streaming router (64 tokens per workgroup) under
+    # the top-K epilogue, with a ragged last tile of 16 tokens
+    (_custom("k2-streaming-router", 16400, 2048, 128, 64, 1.0, seed=9), 2),
 ]
 
 
@@ -197,6 +200,7 @@ EC_EDGE = [
     _custom("ec-residual-shared", 384, 256, 512, 8, 0.7, seed=12, residual_all=True, d_ff_shared=256),
     _custom("ec-f32-odd", 301, 20, 36, 7, 1.3, dtype="f32", seed=13),
     _custom("ec-c-exceeds-t", 40, 128, 128, 4, 8.0, seed=14),
+    _custom("ec-streaming-router", 16400, 2048, 128, 64, 1.0, seed=15),  # streaming router, ragged last tile
 ]
 
 
