@@ -237,13 +237,14 @@ def test_backward_decode():
     assert not torch.any(g["dw1"][inactive]) and not torch.any(g["dw2"][inactive])
 
 
-@pytest.mark.parametrize("name", ["switch-decode-384", "switch-base-uniform"])
+@pytest.mark.parametrize("name", ["switch-decode-384", "switch-base-uniform", "tiled-c150"])
 def test_backward_accumulate_expert_grads(name):
     """SWITCH_ACCUM_EXPERT_GRADS: dw1 / dw2 start from seeded prior gradients R;
     after the backward, every expert that kept a token holds R + its gradient
     (same bar, envelope shifted by R) and every other expert still holds R bit
-    for bit; dx, dW_g and db are the plain backward's."""
-    wl = workloads.WORKLOADS[name]
+    for bit; dx, dW_g and db are the plain backward's.  tiled-c150 (C = 150)
+    runs the fused passes at their largest row count (10 row tiles)."""
+    wl = workloads.WORKLOADS[name] if name in workloads.WORKLOADS else {w.name: w for w in EDGE}[name]
     _say(f"{wl.name} accumulate")
     dt, tol = wl.dtype, TOL_OUT[wl.dtype]
     inp, d, dy = _prepare(wl)
