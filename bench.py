@@ -83,12 +83,12 @@ BWD_SOURCES = ("switch_top_routed_amd/csrc/backward_fused.hip", "switch_top_rout
 BWD_TRAFFIC = {
     "switch-base-uniform": {
         "sources_sha256": "5a1e0367bc876009e75bc64ae5e90adffbeb7467d853bb1863d91e8be95643ae",
-        "fetch_kib": [322815.7, 314168.8], "write_kib": [614961.2, 601878.8],
+        "fetch_kib": [322809.5, 314250.8], "write_kib": [614951.2, 601878.7],
         "fetch_scale": 2.0, "write_scale": 1.0,
     },
     "switch-large-shared": {
         "sources_sha256": "5a1e0367bc876009e75bc64ae5e90adffbeb7467d853bb1863d91e8be95643ae",
-        "fetch_kib": [6111479.6, 5790485.9], "write_kib": [10778442.9, 10813451.3],
+        "fetch_kib": [6231961.5, 5842643.3], "write_kib": [10775498.7, 10813449.6],
         "fetch_scale": 2.0, "write_scale": 1.0,
     },
 }

@@ -185,6 +185,9 @@ EDGE = [
     _custom("shared-dense-tiles", 640, 512, 256, 8, 1.0, seed=14, d_ff_shared=768),
     _custom("shared-generic", 300, 256, 256, 8, 1.0, seed=15, d_ff_shared=256),
     _custom("tiled-c150", 1200, 256, 512, 8, 1.0, seed=13, bias_scale=0.5),
+    # C = 154 with skewed routing: the 10-tile fused passes with experts from 16 kept rows
+    # to full ones
+    _custom("c154-two-classes", 1400, 256, 512, 10, 1.1, seed=16, bias_scale=1.0),
 ]
 
 
