@@ -59,7 +59,10 @@ def widen(a: np.ndarray, dtype: str) -> np.ndarray:
     """Stored values -> float64, exactly.  bf16 arrives as uint16 bit patterns."""
     if dtype == "bf16":
         u = np.ascontiguousarray(a, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
-        return u.view(np.float32).astype(np.float64)
+        # buffers read back from the device may hold signalling-NaN patterns (poisoned empty slots);
+        # widening them is still exact, so numpy's invalid-value flag is not an error here
+        with np.errstate(invalid="ignore"):
+            return u.view(np.float32).astype(np.float64)
     return np.asarray(a, dtype=np.float32).astype(np.float64)
 
 
