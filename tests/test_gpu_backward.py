@@ -188,6 +188,10 @@ EDGE = [
     # C = 154 with skewed routing: the 10-tile fused passes with experts from 16 kept rows
     # to full ones
     _custom("c154-two-classes", 1400, 256, 512, 10, 1.1, seed=16, bias_scale=1.0),
+    # the 10-tile fused passes with d and d_ff multiples of 512 (uniform, and skewed with
+    # ragged kept counts and full experts)
+    _custom("split-c150", 1200, 512, 1024, 8, 1.0, seed=17, bias_scale=0.5),
+    _custom("split-c154-skewed", 1400, 512, 1024, 10, 1.1, seed=18, bias_scale=1.0),
 ]
 
 
